@@ -1,0 +1,210 @@
+/*
+ * sps.h -- exact all-pairs cosine similarity of sparse embeddings on MI355X
+ * (gfx950), C ABI.
+ *
+ * What it computes. The page "稀疏嵌入批量相似度计算的工程化实践"
+ * (Engineering practice of bulk similarity for sparse embeddings) defines
+ * the result: for CSR query rows q and CSR item rows i over the same
+ * dimension,
+ *
+ *     S[q, i] = (sum over d in supp q ∩ supp i of q_d * i_d) / (|q|_2 |i|_2)
+ *
+ * (§3.1, both equations), a full (n_query, n_item) float32 matrix with no
+ * top-K and no approximation (§2.3), produced item chunk by item chunk
+ * (8192 items per chunk in §2.2 and §4.4). A row whose norm is 0 scores 0
+ * against every row (the page is silent; this library's convention).
+ *
+ * How. Items are prepared once: their L2 norms (§5.2, from the stored
+ * nonzeros only) and, for every chunk, inverted lists (a CSC of the chunk,
+ * values pre-divided by the item norm). Queries are prepared once per batch.
+ * Each chunk is then scored by one kernel launch that accumulates query
+ * nonzero x posting-list products in on-chip (LDS) accumulators and writes
+ * full output rows.
+ *
+ * Conventions for every call:
+ *  - Pointers marked DEVICE are device (HBM) addresses; the caller owns
+ *    every device buffer (inputs, workspaces, outputs) and keeps it alive
+ *    until the stream work that uses it has completed.
+ *  - `stream` is a hipStream_t (NULL = the default stream). Calls that take
+ *    a stream only enqueue work and return; they never synchronise unless
+ *    documented. Enqueued work runs in stream order.
+ *  - Every call returns an sps_status; nothing aborts, throws or exits.
+ *    On an error no work has been enqueued, and sps_last_error_message()
+ *    (thread-local) holds a detail string.
+ *  - Sizes are 64-bit on the interface; row counts, nnz and dims must be
+ *    below 2^31 (SPS_ERR_OVERFLOW otherwise).
+ *  - Input CSR must be canonical: indptr[0] = 0, non-decreasing,
+ *    indptr[n_rows] = nnz, column indices strictly ascending within a row
+ *    and inside [0, n_cols), values finite (§3.1 note: the merge needs
+ *    strictly ordered indices). The prepare calls check the structure on
+ *    the device: on a structural fault (indptr out of order or range, an
+ *    index outside [0, n_cols)) they do no out-of-range access; the handle
+ *    then scores every affected row as empty. sps_validate_csr reports the
+ *    fault to the host.
+ */
+#ifndef SPS_H
+#define SPS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SPS_OK = 0,
+  SPS_ERR_INVALID_ARGUMENT = -1,   /* NULL pointer, negative size, bad chunk size, ... */
+  SPS_ERR_BAD_CSR = -2,            /* sps_validate_csr found a non-canonical CSR */
+  SPS_ERR_DIM_MISMATCH = -3,       /* queries and items have different n_cols */
+  SPS_ERR_WORKSPACE_TOO_SMALL = -4,/* a workspace is smaller than its sizing call said */
+  SPS_ERR_CHUNK_RANGE = -5,        /* chunk index outside [0, num_chunks) */
+  SPS_ERR_OVERFLOW = -6,           /* a size reaches 2^31 (or a byte count overflows) */
+  SPS_ERR_HIP = -7,                /* a HIP runtime call or launch failed */
+  SPS_ERR_UNSUPPORTED = -8         /* e.g. chunk too large for the device's LDS */
+} sps_status;
+
+/* A CSR matrix. n_rows, n_cols and nnz are host values; the three arrays
+ * are DEVICE arrays: indptr[n_rows+1] int32, indices[nnz] int32,
+ * values[nnz] float32 (§4.2 and §3.2 of the page use int32 indptr). */
+typedef struct {
+  int64_t n_rows;
+  int64_t n_cols;
+  int64_t nnz;
+  const int32_t *indptr;
+  const int32_t *indices;
+  const float *values;
+} sps_csr;
+
+/* Opaque host handles. Immutable once prepared; the device data they refer
+ * to lives in caller-owned workspaces. */
+typedef struct sps_items sps_items;
+typedef struct sps_queries sps_queries;
+
+/* ------------------------------------------------------------------ */
+/* Items: norms + per-chunk inverted lists                             */
+/* ------------------------------------------------------------------ */
+
+/* Byte sizes for sps_prepare. `persistent` holds the prepared corpus and
+ * must outlive the handle; `scratch` is only used by sps_prepare itself and
+ * may be reused once the prepare's stream work has completed.
+ * chunk_size: items per chunk, 1..32768 (the page uses 8192, §3.3).
+ * Pure host arithmetic; no device access. */
+sps_status sps_items_workspace_size(int64_t n_items, int64_t dim, int64_t nnz,
+                                    int32_t chunk_size, size_t *persistent_bytes,
+                                    size_t *scratch_bytes);
+
+/* Prepare an item corpus (asynchronous, stream-ordered):
+ *  1. inverse norms inv[i] = fl32(1 / sqrt(sum v^2)) with the sum in float64
+ *     over the stored nonzeros in index order (§5.2); 0 for a zero norm;
+ *  2. chunk c covers items [c*chunk_size, min((c+1)*chunk_size, n_items)),
+ *     the chunk's entries are indptr[first]..indptr[last+1] (§4.4 slicing);
+ *  3. per chunk, the inverted lists: col_ptr[dim+1] (chunk-relative offsets,
+ *     col_ptr[0] = 0, col_ptr[dim] = chunk nnz), and for every entry the
+ *     chunk-local item id (uint16) and value fl32(v / ||item||) rounded once
+ *     from float64 (0 if the item norm is 0). Item ids ascend within each dim.
+ * The item CSR may be released once this stream work has completed.
+ * On success *out receives a new handle (free with sps_items_destroy). */
+sps_status sps_prepare(const sps_csr *items, int32_t chunk_size, void *persistent,
+                       size_t persistent_bytes, void *scratch, size_t scratch_bytes,
+                       void *stream, sps_items **out);
+
+sps_status sps_items_info(const sps_items *h, int64_t *n_items, int64_t *dim, int64_t *nnz,
+                          int32_t *chunk_size, int32_t *num_chunks);
+
+/* Device views of one prepared chunk (for parity tests and tooling).
+ * SYNCHRONOUS: reads the chunk's entry range back from the device after
+ * synchronising `stream`. col_ptr: DEVICE int32[dim+1]; row: DEVICE
+ * uint16[chunk_nnz]; val: DEVICE float[chunk_nnz]; item_inv_norm: DEVICE
+ * float[chunk_len] (the chunk's first item onwards). */
+typedef struct {
+  int64_t item_begin;
+  int32_t chunk_len;
+  int32_t chunk_nnz;
+  const int32_t *col_ptr;
+  const uint16_t *row;
+  const float *val;
+  const float *item_inv_norm;
+} sps_chunk_view;
+
+sps_status sps_items_chunk_view(const sps_items *h, int32_t chunk, void *stream,
+                                sps_chunk_view *view);
+
+void sps_items_destroy(sps_items *h);
+
+/* ------------------------------------------------------------------ */
+/* Queries                                                             */
+/* ------------------------------------------------------------------ */
+
+/* Byte size of the query workspace for a query batch scored against the
+ * prepared items `items` (the row grouping depends on the item chunk size).
+ * Pure host arithmetic. */
+sps_status sps_queries_workspace_size(const sps_items *items, int64_t n_rows, int64_t dim,
+                                      int64_t nnz, size_t *bytes);
+
+/* Prepare a query batch (asynchronous): inverse norms as for items (§5.2)
+ * and, for every group of consecutive rows scored by one workgroup, the
+ * union of the rows' dims in ascending order with each row's value (0 where
+ * a row lacks the dim), so that a posting list shared by several rows of a
+ * group is read once. The query CSR may be released once this stream work
+ * has completed. Free the handle with sps_queries_destroy. */
+sps_status sps_prepare_queries(const sps_csr *queries, const sps_items *items,
+                               void *workspace, size_t workspace_bytes, void *stream,
+                               sps_queries **out);
+
+/* DEVICE float[n_rows] inverse norms of a prepared query batch. */
+sps_status sps_queries_inv_norms(const sps_queries *q, const float **inv_norm);
+
+void sps_queries_destroy(sps_queries *q);
+
+/* ------------------------------------------------------------------ */
+/* Scoring                                                             */
+/* ------------------------------------------------------------------ */
+
+/* Score chunk `chunk` (asynchronous): for every query row q and every item
+ * j < chunk_len of the chunk,
+ *     out[q * ld_out + j] = S[q, item_begin + j]          (float32)
+ * computed as (sum over the query's nonzeros d of q_d * itemval_d) * inv_q,
+ * with item values pre-divided by the item norm (division after the dot,
+ * §4.4, up to fp32 rounding). Columns chunk_len <= j < ld_out are not
+ * touched. out: DEVICE, n_rows * ld_out floats, ld_out >= chunk_len.
+ * row_sums (nullable): DEVICE double[n_rows]; row_sums[q] = the float64 sum
+ * of the float32 scores written for row q (a per-chunk checksum).
+ * No clamping to [-1, 1] is applied. Results may differ between runs in the
+ * last bits (order of float additions into on-chip accumulators). */
+sps_status sps_cosine_chunk(const sps_queries *q, const sps_items *items, int32_t chunk,
+                            float *out, int64_t ld_out, double *row_sums, void *stream);
+
+/* Score chunks [chunk_begin, chunk_end) one after another into the same
+ * rotating buffer `out` (the streaming loop of §2.2 and §4.4 with the chunk
+ * output kept on the device). row_sums (nullable): DEVICE
+ * double[(chunk_end-chunk_begin) * n_rows], chunk-major. */
+sps_status sps_cosine_stream(const sps_queries *q, const sps_items *items, int32_t chunk_begin,
+                             int32_t chunk_end, float *out, int64_t ld_out, double *row_sums,
+                             void *stream);
+
+/* ------------------------------------------------------------------ */
+/* Stand-alone pieces                                                  */
+/* ------------------------------------------------------------------ */
+
+/* Inverse row norms of any CSR (asynchronous): inv_norm DEVICE float[n_rows],
+ * fl32(1/sqrt(sum v^2)), float64 sum in index order, 0 for a zero norm
+ * (§5.2). */
+sps_status sps_row_inv_norms(const sps_csr *rows, float *inv_norm, void *stream);
+
+/* Full canonical-CSR check (SYNCHRONOUS). scratch: DEVICE, >= 64 bytes.
+ * Returns SPS_OK, or SPS_ERR_BAD_CSR with *first_bad_row (nullable) set to
+ * the lowest offending row (0 for a fault in indptr[0] or indptr[n_rows])
+ * and *reason (nullable): 1 indptr, 2 order/duplicate, 3 index range,
+ * 4 non-finite value. */
+sps_status sps_validate_csr(const sps_csr *m, void *scratch, void *stream,
+                            int64_t *first_bad_row, int32_t *reason);
+
+const char *sps_status_string(sps_status s);
+const char *sps_last_error_message(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPS_H */

@@ -1,0 +1,361 @@
+"""Exact all-pairs cosine similarity of sparse embeddings on MI355X (gfx950).
+
+Thin Python binding of the C ABI in ``include/sps.h`` (``libsps.so``).
+Arguments are marshalled here; every step of the computation runs in the
+library's HIP kernels. PyTorch only provides device memory and streams.
+
+Page followed: "稀疏嵌入批量相似度计算的工程化实践" (Engineering practice of
+bulk similarity for sparse embeddings): §3.1 defines the cosine over the
+shared support, §5.2 the norms, §2.2 and §4.4 the item-chunk streaming with
+8192-item chunks, §2.3 the full float32 output.
+
+Typical use::
+
+    items = sps.prepare(sps.CSR.from_host(item_csr, "cuda"), chunk_size=8192)
+    queries = sps.prepare_queries(sps.CSR.from_host(query_csr, "cuda"), items)
+    out = torch.empty(n_query, 8192, device="cuda")
+    for c in range(items.num_chunks):
+        sps.cosine_chunk(queries, items, c, out)   # out[:, :chunk_len] = S[:, chunk c]
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libsps.so")
+
+SPS_OK = 0
+_STATUS = {
+    0: "SPS_OK", -1: "SPS_ERR_INVALID_ARGUMENT", -2: "SPS_ERR_BAD_CSR",
+    -3: "SPS_ERR_DIM_MISMATCH", -4: "SPS_ERR_WORKSPACE_TOO_SMALL", -5: "SPS_ERR_CHUNK_RANGE",
+    -6: "SPS_ERR_OVERFLOW", -7: "SPS_ERR_HIP", -8: "SPS_ERR_UNSUPPORTED",
+}
+
+
+class SpsError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__("%s: %s" % (_STATUS.get(status, status), msg))
+        self.status = status
+
+
+class _Csr(ctypes.Structure):
+    _fields_ = [("n_rows", ctypes.c_int64), ("n_cols", ctypes.c_int64), ("nnz", ctypes.c_int64),
+                ("indptr", ctypes.c_void_p), ("indices", ctypes.c_void_p),
+                ("values", ctypes.c_void_p)]
+
+
+class _ChunkView(ctypes.Structure):
+    _fields_ = [("item_begin", ctypes.c_int64), ("chunk_len", ctypes.c_int32),
+                ("chunk_nnz", ctypes.c_int32), ("col_ptr", ctypes.c_void_p),
+                ("row", ctypes.c_void_p), ("val", ctypes.c_void_p),
+                ("item_inv_norm", ctypes.c_void_p)]
+
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I32 = ctypes.c_int32
+_SZ = ctypes.c_size_t
+
+# name -> (restype, argtypes); every symbol include/sps.h declares
+SIGNATURES = {
+    "sps_items_workspace_size": (_I32, [_I64, _I64, _I64, _I32, ctypes.POINTER(_SZ),
+                                        ctypes.POINTER(_SZ)]),
+    "sps_prepare": (_I32, [ctypes.POINTER(_Csr), _I32, _P, _SZ, _P, _SZ, _P,
+                           ctypes.POINTER(_P)]),
+    "sps_items_info": (_I32, [_P, ctypes.POINTER(_I64), ctypes.POINTER(_I64),
+                              ctypes.POINTER(_I64), ctypes.POINTER(_I32), ctypes.POINTER(_I32)]),
+    "sps_items_chunk_view": (_I32, [_P, _I32, _P, ctypes.POINTER(_ChunkView)]),
+    "sps_items_destroy": (None, [_P]),
+    "sps_queries_workspace_size": (_I32, [_P, _I64, _I64, _I64, ctypes.POINTER(_SZ)]),
+    "sps_prepare_queries": (_I32, [ctypes.POINTER(_Csr), _P, _P, _SZ, _P, ctypes.POINTER(_P)]),
+    "sps_queries_inv_norms": (_I32, [_P, ctypes.POINTER(_P)]),
+    "sps_queries_destroy": (None, [_P]),
+    "sps_cosine_chunk": (_I32, [_P, _P, _I32, _P, _I64, _P, _P]),
+    "sps_cosine_stream": (_I32, [_P, _P, _I32, _I32, _P, _I64, _P, _P]),
+    "sps_row_inv_norms": (_I32, [ctypes.POINTER(_Csr), _P, _P]),
+    "sps_validate_csr": (_I32, [ctypes.POINTER(_Csr), _P, _P, ctypes.POINTER(_I64),
+                                ctypes.POINTER(_I32)]),
+    "sps_status_string": (ctypes.c_char_p, [_I32]),
+    "sps_last_error_message": (ctypes.c_char_p, []),
+}
+
+_lib = None
+
+
+def load_library(path: str | None = None):
+    """Load libsps.so (building it with hipcc first if it is absent).
+
+    There is no fallback: without the HIP library nothing here runs.
+    """
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        from . import _build
+        _build.build()
+    lib = ctypes.CDLL(p)
+    for name, (res, args) in SIGNATURES.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _check(st: int):
+    if st != SPS_OK:
+        msg = _lib.sps_last_error_message().decode(errors="replace")
+        raise SpsError(st, msg)
+
+
+def _stream_ptr(stream=None) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return int(s.cuda_stream)
+
+
+def _workspace(nbytes: int, device) -> tuple[torch.Tensor, int]:
+    """uint8 device buffer of at least nbytes, 256-byte aligned."""
+    buf = torch.empty(max(int(nbytes), 1) + 256, dtype=torch.uint8, device=device)
+    p = buf.data_ptr()
+    return buf, (p + 255) & ~255
+
+
+# ---------------------------------------------------------------------------
+
+@dataclass
+class CSR:
+    """Device CSR (int32 indptr/indices, float32 values) in torch tensors."""
+    indptr: torch.Tensor
+    indices: torch.Tensor
+    values: torch.Tensor
+    n_rows: int
+    n_cols: int
+
+    @property
+    def nnz(self) -> int:
+        return int(self.indices.numel())
+
+    @classmethod
+    def from_host(cls, m, device="cuda") -> "CSR":
+        """From any object with numpy indptr/indices/values, n_rows, n_cols."""
+        ip = torch.as_tensor(m.indptr).to(device=device, dtype=torch.int32).contiguous()
+        ix = torch.as_tensor(m.indices).to(device=device, dtype=torch.int32).contiguous()
+        v = torch.as_tensor(m.values).to(device=device, dtype=torch.float32).contiguous()
+        return cls(ip, ix, v, int(m.n_rows), int(m.n_cols))
+
+    def _c(self) -> _Csr:
+        assert self.indptr.is_cuda and self.indices.is_cuda and self.values.is_cuda
+        assert self.indptr.dtype == torch.int32 and self.indices.dtype == torch.int32
+        assert self.values.dtype == torch.float32
+        assert self.indptr.is_contiguous() and self.indices.is_contiguous() \
+            and self.values.is_contiguous()
+        assert self.indptr.numel() == self.n_rows + 1
+        assert self.values.numel() == self.indices.numel()
+        return _Csr(self.n_rows, self.n_cols, self.nnz, self.indptr.data_ptr(),
+                    self.indices.data_ptr() if self.nnz else None,
+                    self.values.data_ptr() if self.nnz else None)
+
+
+class Items:
+    """Prepared item corpus (owns its workspaces)."""
+
+    def __init__(self, handle, persistent, scratch, src: CSR, chunk_size: int):
+        self._h = handle
+        self._persistent = persistent
+        self._scratch = scratch
+        self._src = src  # kept alive until release_inputs()
+        n, d, z = _I64(), _I64(), _I64()
+        cs, nc = _I32(), _I32()
+        _check(_lib.sps_items_info(handle, ctypes.byref(n), ctypes.byref(d), ctypes.byref(z),
+                                   ctypes.byref(cs), ctypes.byref(nc)))
+        self.n_items, self.dim, self.nnz = n.value, d.value, z.value
+        self.chunk_size, self.num_chunks = cs.value, nc.value
+
+    def chunk_len(self, c: int) -> int:
+        b = c * self.chunk_size
+        return min(b + self.chunk_size, self.n_items) - b
+
+    def release_inputs(self):
+        """Drop the item CSR and prepare scratch (after the prepare work completed)."""
+        torch.cuda.current_stream().synchronize()
+        self._src = None
+        self._scratch = None
+
+    def chunk_view(self, c: int, stream=None) -> dict:
+        """Device views of chunk c's inverted lists (synchronous)."""
+        v = _ChunkView()
+        _check(_lib.sps_items_chunk_view(self._h, c, _stream_ptr(stream), ctypes.byref(v)))
+        dev = self._persistent.device
+
+        def view(ptr, n, dtype, elem):
+            if n == 0:
+                return torch.empty(0, dtype=dtype, device=dev)
+            base = self._persistent.data_ptr()
+            off = ptr - base
+            assert 0 <= off and off + n * elem <= self._persistent.numel()
+            return self._persistent[off:off + n * elem].view(dtype)
+
+        return {
+            "item_begin": v.item_begin, "chunk_len": v.chunk_len, "chunk_nnz": v.chunk_nnz,
+            "col_ptr": view(v.col_ptr, self.dim + 1, torch.int32, 4),
+            "row": view(v.row, v.chunk_nnz, torch.int16, 2),
+            "val": view(v.val, v.chunk_nnz, torch.float32, 4),
+            "item_inv_norm": view(v.item_inv_norm, v.chunk_len, torch.float32, 4),
+        }
+
+    def __del__(self):
+        h, self._h = getattr(self, "_h", None), None
+        if h and _lib is not None:
+            _lib.sps_items_destroy(h)
+
+
+class Queries:
+    """Prepared query batch (owns its workspace)."""
+
+    def __init__(self, handle, ws, n_rows: int, items: Items):
+        self._h = handle
+        self._ws = ws
+        self.n_rows = n_rows
+        self.items = items
+        p = _P()
+        _check(_lib.sps_queries_inv_norms(handle, ctypes.byref(p)))
+        off = p.value - ws.data_ptr()
+        self.inv_norm = ws[off:off + 4 * n_rows].view(torch.float32) if n_rows else \
+            torch.empty(0, dtype=torch.float32, device=ws.device)
+
+    def __del__(self):
+        h, self._h = getattr(self, "_h", None), None
+        if h and _lib is not None:
+            _lib.sps_queries_destroy(h)
+
+
+def items_workspace_size(n_items: int, dim: int, nnz: int, chunk_size: int) -> tuple[int, int]:
+    load_library()
+    p, s = _SZ(), _SZ()
+    _check(_lib.sps_items_workspace_size(n_items, dim, nnz, chunk_size, ctypes.byref(p),
+                                         ctypes.byref(s)))
+    return p.value, s.value
+
+
+def prepare(items: CSR, chunk_size: int = 8192, stream=None) -> Items:
+    """Norms + per-chunk inverted lists of an item corpus (asynchronous)."""
+    load_library()
+    pb, sb = items_workspace_size(items.n_rows, items.n_cols, items.nnz, chunk_size)
+    dev = items.indptr.device
+    pbuf, pptr = _workspace(pb, dev)
+    sbuf, sptr = _workspace(sb, dev)
+    h = _P()
+    c = items._c()
+    _check(_lib.sps_prepare(ctypes.byref(c), chunk_size, pptr, pb, sptr, sb, _stream_ptr(stream),
+                            ctypes.byref(h)))
+    # the persistent view handed out by chunk_view is relative to the aligned base
+    pview = pbuf[pptr - pbuf.data_ptr():]
+    return Items(h.value, pview, sbuf, items, chunk_size)
+
+
+def prepare_queries(queries: CSR, items: Items, stream=None) -> Queries:
+    """Inverse norms and per-workgroup merged dim lists of a query batch (asynchronous)."""
+    load_library()
+    nb = _SZ()
+    _check(_lib.sps_queries_workspace_size(items._h, queries.n_rows, queries.n_cols,
+                                           queries.nnz, ctypes.byref(nb)))
+    buf, ptr = _workspace(nb.value, queries.indptr.device)
+    h = _P()
+    c = queries._c()
+    _check(_lib.sps_prepare_queries(ctypes.byref(c), items._h, ptr, nb.value, _stream_ptr(stream),
+                                    ctypes.byref(h)))
+    q = Queries(h.value, buf[ptr - buf.data_ptr():], queries.n_rows, items)
+    q._src = queries
+    return q
+
+
+def _out_args(q: Queries, out: torch.Tensor, row_sums):
+    assert out.is_cuda and out.dtype == torch.float32 and out.dim() == 2
+    assert out.stride(1) == 1 and out.shape[0] == q.n_rows
+    ld = out.stride(0) if q.n_rows > 1 else out.shape[1]
+    rs = None
+    if row_sums is not None:
+        assert row_sums.is_cuda and row_sums.dtype == torch.float64 and row_sums.is_contiguous()
+        rs = row_sums.data_ptr()
+    return ld, rs
+
+
+def cosine_chunk(q: Queries, items: Items, chunk: int, out: torch.Tensor,
+                 row_sums: torch.Tensor | None = None, stream=None) -> None:
+    """out[:, :chunk_len] = S[:, chunk]; out is (n_query, >= chunk_len) float32, row-major."""
+    ld, rs = _out_args(q, out, row_sums)
+    assert out.shape[1] >= items.chunk_len(chunk)
+    if row_sums is not None:
+        assert row_sums.numel() >= q.n_rows
+    _check(_lib.sps_cosine_chunk(q._h, items._h, chunk, out.data_ptr(), ld, rs,
+                                 _stream_ptr(stream)))
+
+
+def cosine_stream(q: Queries, items: Items, chunk_begin: int, chunk_end: int,
+                  out: torch.Tensor, row_sums: torch.Tensor | None = None, stream=None) -> None:
+    """Chunks [chunk_begin, chunk_end) in turn into the same rotating buffer `out`."""
+    ld, rs = _out_args(q, out, row_sums)
+    assert out.shape[1] >= min(items.chunk_size, items.n_items)
+    if row_sums is not None:
+        assert row_sums.numel() >= (chunk_end - chunk_begin) * q.n_rows
+    _check(_lib.sps_cosine_stream(q._h, items._h, chunk_begin, chunk_end, out.data_ptr(), ld, rs,
+                                  _stream_ptr(stream)))
+
+
+def row_inv_norms(m: CSR, stream=None) -> torch.Tensor:
+    load_library()
+    out = torch.empty(m.n_rows, dtype=torch.float32, device=m.indptr.device)
+    c = m._c()
+    _check(_lib.sps_row_inv_norms(ctypes.byref(c), out.data_ptr() if m.n_rows else None,
+                                  _stream_ptr(stream)))
+    return out
+
+
+def validate_csr(m: CSR, stream=None) -> tuple[bool, int, int]:
+    """(ok, first_bad_row, reason); reason 1 indptr, 2 order/dup, 3 range, 4 non-finite."""
+    load_library()
+    scratch = torch.empty(64, dtype=torch.uint8, device=m.indptr.device)
+    row, why = _I64(), _I32()
+    c = m._c()
+    st = _lib.sps_validate_csr(ctypes.byref(c), scratch.data_ptr(), _stream_ptr(stream),
+                               ctypes.byref(row), ctypes.byref(why))
+    if st == -2:
+        return False, row.value, why.value
+    _check(st)
+    return True, -1, 0
+
+
+def bulk_similarity(queries: CSR, items: CSR, chunk_size: int = 8192, out=None,
+                    on_chunk=None, row_sums: bool = False):
+    """Full (n_query, n_item) float32 cosine matrix, item chunk by item chunk.
+
+    Mirrors the streaming loop of §4.4 with every step on the GPU. With
+    ``out`` (a device or pinned host tensor of shape (n_query, n_item)) each
+    chunk is copied there; with ``on_chunk(c, buf, sums)`` each chunk's
+    device buffer is handed to the callback instead (and reused after it
+    returns). Returns ``out`` (allocated on the device if neither is given).
+    """
+    it = prepare(items, chunk_size)
+    q = prepare_queries(queries, it)
+    width = min(chunk_size, it.n_items)
+    buf = torch.empty(queries.n_rows, max(width, 1), dtype=torch.float32,
+                      device=queries.indptr.device)
+    sums = torch.empty(queries.n_rows, dtype=torch.float64, device=buf.device) \
+        if row_sums else None
+    if out is None and on_chunk is None:
+        out = torch.empty(queries.n_rows, it.n_items, dtype=torch.float32, device=buf.device)
+    for c in range(it.num_chunks):
+        cosine_chunk(q, it, c, buf, sums)
+        n = it.chunk_len(c)
+        b = c * chunk_size
+        if on_chunk is not None:
+            on_chunk(c, buf[:, :n], sums)
+        if out is not None:
+            out[:, b:b + n].copy_(buf[:, :n], non_blocking=False)
+    return out

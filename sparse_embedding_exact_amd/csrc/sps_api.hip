@@ -1,0 +1,489 @@
+// sps_api.hip -- the C ABI of include/sps.h: argument checks, workspace
+// layout, handles and stream-ordered launches. Host code only; the kernels
+// live in sps_kernels.hip.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+
+#include "sps.h"
+#include "sps_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+sps_status fail(sps_status s, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+sps_status hip_fail(hipError_t e, const char *where) {
+  return fail(SPS_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+constexpr int64_t kI32Max = 2147483647ll;
+constexpr size_t kAlign = 256;
+constexpr int32_t kMaxChunk = 32768;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+// Byte layout builder: adds 256-aligned regions, detects overflow.
+struct Layout {
+  size_t off = 0;
+  bool overflow = false;
+  size_t add(uint64_t count, uint64_t elem) {
+    const size_t at = off;
+    if (elem != 0 && count > (UINT64_MAX / 4) / elem) {
+      overflow = true;
+      return at;
+    }
+    const uint64_t bytes = count * elem;
+    const size_t next = align_up(off + (size_t)bytes);
+    if (next < off) overflow = true;
+    off = next;
+    return at;
+  }
+};
+
+sps_status check_csr_shape(const sps_csr *m, const char *what) {
+  if (!m) return fail(SPS_ERR_INVALID_ARGUMENT, "%s: NULL CSR", what);
+  if (m->n_rows < 0 || m->n_cols <= 0 || m->nnz < 0)
+    return fail(SPS_ERR_INVALID_ARGUMENT, "%s: negative size or n_cols <= 0", what);
+  if (m->n_rows >= kI32Max || m->n_cols >= kI32Max || m->nnz >= kI32Max)
+    return fail(SPS_ERR_OVERFLOW, "%s: sizes must be below 2^31", what);
+  if (!m->indptr) return fail(SPS_ERR_INVALID_ARGUMENT, "%s: NULL indptr", what);
+  if (m->nnz > 0 && (!m->indices || !m->values))
+    return fail(SPS_ERR_INVALID_ARGUMENT, "%s: NULL indices or values", what);
+  return SPS_OK;
+}
+
+// LDS per workgroup on gfx950 (CDNA4): 160 KiB.
+constexpr size_t kLdsLimit = 163840;
+
+// Rows per score workgroup. SPS_SCORE_ROWS (1, 2, 4 or 8) overrides the
+// default when the chunk fits.
+int pick_rows(int32_t chunk_len, size_t lds_limit) {
+  const int maxr = sps::score_max_rows(chunk_len, lds_limit);
+  if (maxr == 0) return 0;
+  int r = maxr < 4 ? maxr : 4;
+  if (const char *env = getenv("SPS_SCORE_ROWS")) {
+    const int v = atoi(env);
+    if ((v == 1 || v == 2 || v == 4 || v == 8) && v <= maxr) r = v;
+  }
+  return r;
+}
+
+}  // namespace
+
+struct sps_items {
+  int64_t n_items, dim, nnz;
+  int32_t chunk_size, num_chunks;
+  int device;
+  float *inv_norm;
+  int32_t *col_ptr;
+  uint16_t *row;
+  float *val;
+  int32_t *chunk_base;
+};
+
+struct sps_queries {
+  int64_t n_rows, dim, nnz;
+  int32_t R, n_groups, chunk_size;
+  int device;
+  float *inv_norm;
+  int32_t *grp_ptr, *grp_dim;
+  float *grp_val;
+};
+
+namespace {
+
+struct ItemsLayout {
+  size_t inv, colp, row, val, cbase, persistent;
+  size_t flags, norm64, ticket, trow, tval, mlist, mcount, scratch;
+  bool overflow;
+};
+
+ItemsLayout items_layout(int64_t n, int64_t dim, int64_t nnz, int32_t C) {
+  const int64_t nch = (n + C - 1) / C;
+  ItemsLayout L{};
+  Layout p;
+  L.inv = p.add(n, 4);
+  L.colp = p.add((uint64_t)nch * (uint64_t)(dim + 1), 4);
+  L.row = p.add(nnz, 2);
+  L.val = p.add(nnz, 4);
+  L.cbase = p.add(nch + 1, 4);
+  L.persistent = p.off;
+  Layout s;
+  L.flags = s.add(sps::kFlagsInts, 4);
+  L.norm64 = s.add(n, 8);
+  L.ticket = s.add(nnz, 4);
+  L.trow = s.add(nnz, 2);
+  L.tval = s.add(nnz, 4);
+  L.mlist = s.add(nnz / 2 + nch + 1, 4);
+  L.mcount = s.add(nch, 4);
+  L.scratch = s.off;
+  L.overflow = p.overflow || s.overflow;
+  return L;
+}
+
+struct QueriesLayout {
+  size_t flags, inv, gptr, gdim, gval, total;
+  bool overflow;
+};
+
+QueriesLayout queries_layout(int64_t n, int64_t nnz, int R) {
+  const int64_t ng = (n + R - 1) / R;
+  QueriesLayout L{};
+  Layout p;
+  L.flags = p.add(sps::kFlagsInts, 4);
+  L.inv = p.add(n, 4);
+  L.gptr = p.add(ng + 1, 4);
+  L.gdim = p.add(nnz, 4);
+  L.gval = p.add((uint64_t)nnz * (uint64_t)R, 4);
+  L.total = p.off;
+  L.overflow = p.overflow;
+  return L;
+}
+
+template <typename T>
+T *at(void *base, size_t off) {
+  return reinterpret_cast<T *>(reinterpret_cast<char *>(base) + off);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *sps_status_string(sps_status s) {
+  switch (s) {
+    case SPS_OK: return "ok";
+    case SPS_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case SPS_ERR_BAD_CSR: return "non-canonical CSR";
+    case SPS_ERR_DIM_MISMATCH: return "query and item dimensions differ";
+    case SPS_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case SPS_ERR_CHUNK_RANGE: return "chunk index out of range";
+    case SPS_ERR_OVERFLOW: return "size overflow";
+    case SPS_ERR_HIP: return "HIP runtime error";
+    case SPS_ERR_UNSUPPORTED: return "unsupported configuration";
+  }
+  return "unknown status";
+}
+
+const char *sps_last_error_message(void) { return g_err; }
+
+sps_status sps_items_workspace_size(int64_t n_items, int64_t dim, int64_t nnz,
+                                    int32_t chunk_size, size_t *persistent_bytes,
+                                    size_t *scratch_bytes) {
+  if (!persistent_bytes || !scratch_bytes)
+    return fail(SPS_ERR_INVALID_ARGUMENT, "NULL output pointer");
+  if (n_items < 0 || dim <= 0 || nnz < 0)
+    return fail(SPS_ERR_INVALID_ARGUMENT, "negative size or dim <= 0");
+  if (chunk_size < 1 || chunk_size > kMaxChunk)
+    return fail(SPS_ERR_INVALID_ARGUMENT, "chunk_size must be in [1, %d]", kMaxChunk);
+  if (n_items >= kI32Max || dim >= kI32Max || nnz >= kI32Max)
+    return fail(SPS_ERR_OVERFLOW, "sizes must be below 2^31");
+  const ItemsLayout L = items_layout(n_items, dim, nnz, chunk_size);
+  if (L.overflow) return fail(SPS_ERR_OVERFLOW, "workspace byte count overflows");
+  *persistent_bytes = L.persistent;
+  *scratch_bytes = L.scratch;
+  return SPS_OK;
+}
+
+sps_status sps_prepare(const sps_csr *items, int32_t chunk_size, void *persistent,
+                       size_t persistent_bytes, void *scratch, size_t scratch_bytes,
+                       void *stream, sps_items **out) {
+  if (!out) return fail(SPS_ERR_INVALID_ARGUMENT, "NULL output handle pointer");
+  *out = nullptr;
+  sps_status st = check_csr_shape(items, "items");
+  if (st != SPS_OK) return st;
+  size_t need_p = 0, need_s = 0;
+  st = sps_items_workspace_size(items->n_rows, items->n_cols, items->nnz, chunk_size, &need_p,
+                                &need_s);
+  if (st != SPS_OK) return st;
+  if (!persistent || !scratch) return fail(SPS_ERR_INVALID_ARGUMENT, "NULL workspace");
+  if (persistent_bytes < need_p || scratch_bytes < need_s)
+    return fail(SPS_ERR_WORKSPACE_TOO_SMALL,
+                "need %zu persistent and %zu scratch bytes, got %zu and %zu", need_p, need_s,
+                persistent_bytes, scratch_bytes);
+  if ((reinterpret_cast<uintptr_t>(persistent) | reinterpret_cast<uintptr_t>(scratch)) & 255)
+    return fail(SPS_ERR_INVALID_ARGUMENT, "workspaces must be 256-byte aligned");
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(SPS_ERR_HIP, "no HIP device");
+
+  const ItemsLayout L = items_layout(items->n_rows, items->n_cols, items->nnz, chunk_size);
+  sps::ItemsDev d{};
+  d.n_items = items->n_rows;
+  d.dim = items->n_cols;
+  d.nnz = items->nnz;
+  d.chunk_size = chunk_size;
+  d.num_chunks = (int32_t)((items->n_rows + chunk_size - 1) / chunk_size);
+  d.indptr = items->indptr;
+  d.indices = items->indices;
+  d.values = items->values;
+  d.inv_norm = at<float>(persistent, L.inv);
+  d.col_ptr = at<int32_t>(persistent, L.colp);
+  d.row = at<uint16_t>(persistent, L.row);
+  d.val = at<float>(persistent, L.val);
+  d.chunk_base = at<int32_t>(persistent, L.cbase);
+  d.flags = at<int32_t>(scratch, L.flags);
+  d.norm64 = at<double>(scratch, L.norm64);
+  d.ticket = at<int32_t>(scratch, L.ticket);
+  d.trow = at<uint16_t>(scratch, L.trow);
+  d.tval = at<float>(scratch, L.tval);
+  d.mlist = at<int32_t>(scratch, L.mlist);
+  d.mcount = at<int32_t>(scratch, L.mcount);
+
+  sps_items *h = new (std::nothrow) sps_items;
+  if (!h) return fail(SPS_ERR_INVALID_ARGUMENT, "out of host memory");
+  hipError_t e = sps::launch_prepare_items(d, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    delete h;
+    return hip_fail(e, "sps_prepare");
+  }
+  h->n_items = d.n_items;
+  h->dim = d.dim;
+  h->nnz = d.nnz;
+  h->chunk_size = chunk_size;
+  h->num_chunks = d.num_chunks;
+  h->device = dev;
+  h->inv_norm = d.inv_norm;
+  h->col_ptr = d.col_ptr;
+  h->row = d.row;
+  h->val = d.val;
+  h->chunk_base = d.chunk_base;
+  *out = h;
+  return SPS_OK;
+}
+
+sps_status sps_items_info(const sps_items *h, int64_t *n_items, int64_t *dim, int64_t *nnz,
+                          int32_t *chunk_size, int32_t *num_chunks) {
+  if (!h) return fail(SPS_ERR_INVALID_ARGUMENT, "NULL handle");
+  if (n_items) *n_items = h->n_items;
+  if (dim) *dim = h->dim;
+  if (nnz) *nnz = h->nnz;
+  if (chunk_size) *chunk_size = h->chunk_size;
+  if (num_chunks) *num_chunks = h->num_chunks;
+  return SPS_OK;
+}
+
+static int32_t chunk_len_of(const sps_items *h, int32_t c) {
+  const int64_t b = (int64_t)c * h->chunk_size;
+  const int64_t e = b + h->chunk_size < h->n_items ? b + h->chunk_size : h->n_items;
+  return (int32_t)(e - b);
+}
+
+sps_status sps_items_chunk_view(const sps_items *h, int32_t chunk, void *stream,
+                                sps_chunk_view *view) {
+  if (!h || !view) return fail(SPS_ERR_INVALID_ARGUMENT, "NULL handle or view");
+  if (chunk < 0 || chunk >= h->num_chunks)
+    return fail(SPS_ERR_CHUNK_RANGE, "chunk %d outside [0, %d)", chunk, h->num_chunks);
+  hipError_t e = hipStreamSynchronize(reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "sps_items_chunk_view");
+  int32_t be[2];
+  e = hipMemcpy(be, h->chunk_base + chunk, sizeof be, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "sps_items_chunk_view");
+  view->item_begin = (int64_t)chunk * h->chunk_size;
+  view->chunk_len = chunk_len_of(h, chunk);
+  view->chunk_nnz = be[1] - be[0];
+  view->col_ptr = h->col_ptr + (int64_t)chunk * (h->dim + 1);
+  view->row = h->row + be[0];
+  view->val = h->val + be[0];
+  view->item_inv_norm = h->inv_norm + view->item_begin;
+  return SPS_OK;
+}
+
+void sps_items_destroy(sps_items *h) { delete h; }
+
+sps_status sps_queries_workspace_size(const sps_items *items, int64_t n_rows, int64_t dim,
+                                      int64_t nnz, size_t *bytes) {
+  if (!items || !bytes) return fail(SPS_ERR_INVALID_ARGUMENT, "NULL argument");
+  if (n_rows < 0 || dim <= 0 || nnz < 0)
+    return fail(SPS_ERR_INVALID_ARGUMENT, "negative size or dim <= 0");
+  if (n_rows >= kI32Max || dim >= kI32Max || nnz >= kI32Max)
+    return fail(SPS_ERR_OVERFLOW, "sizes must be below 2^31");
+  if (dim != items->dim)
+    return fail(SPS_ERR_DIM_MISMATCH, "query dim %lld != item dim %lld", (long long)dim,
+                (long long)items->dim);
+  const int R = pick_rows(items->chunk_size, kLdsLimit);
+  if (R == 0) return fail(SPS_ERR_UNSUPPORTED, "chunk of %d items exceeds LDS", items->chunk_size);
+  const QueriesLayout L = queries_layout(n_rows, nnz, R);
+  if (L.overflow || (uint64_t)nnz * (uint64_t)R >= (uint64_t)kI32Max * 8)
+    return fail(SPS_ERR_OVERFLOW, "workspace byte count overflows");
+  *bytes = L.total;
+  return SPS_OK;
+}
+
+sps_status sps_prepare_queries(const sps_csr *queries, const sps_items *items, void *workspace,
+                               size_t workspace_bytes, void *stream, sps_queries **out) {
+  if (!out) return fail(SPS_ERR_INVALID_ARGUMENT, "NULL output handle pointer");
+  *out = nullptr;
+  sps_status st = check_csr_shape(queries, "queries");
+  if (st != SPS_OK) return st;
+  if (!items) return fail(SPS_ERR_INVALID_ARGUMENT, "NULL items handle");
+  size_t need = 0;
+  st = sps_queries_workspace_size(items, queries->n_rows, queries->n_cols, queries->nnz, &need);
+  if (st != SPS_OK) return st;
+  if (!workspace) return fail(SPS_ERR_INVALID_ARGUMENT, "NULL workspace");
+  if (workspace_bytes < need)
+    return fail(SPS_ERR_WORKSPACE_TOO_SMALL, "need %zu bytes, got %zu", need, workspace_bytes);
+  if (reinterpret_cast<uintptr_t>(workspace) & 255)
+    return fail(SPS_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(SPS_ERR_HIP, "no HIP device");
+  const int R = pick_rows(items->chunk_size, kLdsLimit);
+  const QueriesLayout L = queries_layout(queries->n_rows, queries->nnz, R);
+  sps::QueriesDev d{};
+  d.n_rows = queries->n_rows;
+  d.dim = queries->n_cols;
+  d.nnz = queries->nnz;
+  d.R = R;
+  d.n_groups = (int32_t)((queries->n_rows + R - 1) / R);
+  d.indptr = queries->indptr;
+  d.indices = queries->indices;
+  d.values = queries->values;
+  d.flags = at<int32_t>(workspace, L.flags);
+  d.inv_norm = at<float>(workspace, L.inv);
+  d.grp_ptr = at<int32_t>(workspace, L.gptr);
+  d.grp_dim = at<int32_t>(workspace, L.gdim);
+  d.grp_val = at<float>(workspace, L.gval);
+  sps_queries *h = new (std::nothrow) sps_queries;
+  if (!h) return fail(SPS_ERR_INVALID_ARGUMENT, "out of host memory");
+  hipError_t e = sps::launch_prepare_queries(d, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    delete h;
+    return hip_fail(e, "sps_prepare_queries");
+  }
+  h->n_rows = d.n_rows;
+  h->dim = d.dim;
+  h->nnz = d.nnz;
+  h->R = R;
+  h->n_groups = d.n_groups;
+  h->chunk_size = items->chunk_size;
+  h->device = dev;
+  h->inv_norm = d.inv_norm;
+  h->grp_ptr = d.grp_ptr;
+  h->grp_dim = d.grp_dim;
+  h->grp_val = d.grp_val;
+  *out = h;
+  return SPS_OK;
+}
+
+sps_status sps_queries_inv_norms(const sps_queries *q, const float **inv_norm) {
+  if (!q || !inv_norm) return fail(SPS_ERR_INVALID_ARGUMENT, "NULL argument");
+  *inv_norm = q->inv_norm;
+  return SPS_OK;
+}
+
+void sps_queries_destroy(sps_queries *q) { delete q; }
+
+static sps_status check_score_args(const sps_queries *q, const sps_items *items, float *out,
+                                   int64_t ld_out) {
+  if (!q || !items) return fail(SPS_ERR_INVALID_ARGUMENT, "NULL handle");
+  if (q->dim != items->dim) return fail(SPS_ERR_DIM_MISMATCH, "query/item dims differ");
+  if (q->chunk_size != items->chunk_size)
+    return fail(SPS_ERR_INVALID_ARGUMENT, "queries were prepared for another chunk size");
+  if (q->n_rows > 0 && !out) return fail(SPS_ERR_INVALID_ARGUMENT, "NULL output");
+  if (ld_out < items->chunk_size && ld_out < items->n_items)
+    return fail(SPS_ERR_INVALID_ARGUMENT, "ld_out %lld below the chunk length",
+                (long long)ld_out);
+  if (q->n_rows > 0 && (uint64_t)ld_out > (uint64_t)INT64_MAX / 4 / (uint64_t)q->n_rows)
+    return fail(SPS_ERR_OVERFLOW, "n_rows * ld_out overflows");
+  return SPS_OK;
+}
+
+static sps_status score_one(const sps_queries *q, const sps_items *items, int32_t chunk,
+                            float *out, int64_t ld_out, double *row_sums, hipStream_t s) {
+  const int32_t len = chunk_len_of(items, chunk);
+  if (ld_out < len) return fail(SPS_ERR_INVALID_ARGUMENT, "ld_out below the chunk length");
+  sps::ScoreArgs a{};
+  a.grp_ptr = q->grp_ptr;
+  a.grp_dim = q->grp_dim;
+  a.grp_val = q->grp_val;
+  a.q_inv = q->inv_norm;
+  a.n_q = q->n_rows;
+  a.dim = q->dim;
+  a.R = q->R;
+  a.n_groups = q->n_groups;
+  a.col_ptr = items->col_ptr + (int64_t)chunk * (items->dim + 1);
+  a.row = items->row;
+  a.val = items->val;
+  a.chunk_base = items->chunk_base;
+  a.chunk = chunk;
+  a.chunk_len = len;
+  a.out = out;
+  a.ld = ld_out;
+  a.row_sums = row_sums;
+  const hipError_t e = sps::launch_score(a, s);
+  if (e != hipSuccess) return hip_fail(e, "score kernel");
+  return SPS_OK;
+}
+
+sps_status sps_cosine_chunk(const sps_queries *q, const sps_items *items, int32_t chunk,
+                            float *out, int64_t ld_out, double *row_sums, void *stream) {
+  sps_status st = check_score_args(q, items, out, ld_out);
+  if (st != SPS_OK) return st;
+  if (chunk < 0 || chunk >= items->num_chunks)
+    return fail(SPS_ERR_CHUNK_RANGE, "chunk %d outside [0, %d)", chunk, items->num_chunks);
+  return score_one(q, items, chunk, out, ld_out, row_sums, reinterpret_cast<hipStream_t>(stream));
+}
+
+sps_status sps_cosine_stream(const sps_queries *q, const sps_items *items, int32_t chunk_begin,
+                             int32_t chunk_end, float *out, int64_t ld_out, double *row_sums,
+                             void *stream) {
+  sps_status st = check_score_args(q, items, out, ld_out);
+  if (st != SPS_OK) return st;
+  if (chunk_begin < 0 || chunk_end > items->num_chunks || chunk_begin > chunk_end)
+    return fail(SPS_ERR_CHUNK_RANGE, "chunk range [%d, %d) outside [0, %d)", chunk_begin,
+                chunk_end, items->num_chunks);
+  for (int32_t c = chunk_begin; c < chunk_end; ++c) {
+    double *rs = row_sums ? row_sums + (int64_t)(c - chunk_begin) * q->n_rows : nullptr;
+    st = score_one(q, items, c, out, ld_out, rs, reinterpret_cast<hipStream_t>(stream));
+    if (st != SPS_OK) return st;
+  }
+  return SPS_OK;
+}
+
+sps_status sps_row_inv_norms(const sps_csr *rows, float *inv_norm, void *stream) {
+  sps_status st = check_csr_shape(rows, "rows");
+  if (st != SPS_OK) return st;
+  if (rows->n_rows > 0 && !inv_norm) return fail(SPS_ERR_INVALID_ARGUMENT, "NULL inv_norm");
+  const hipError_t e = sps::launch_row_norms(rows->n_rows, rows->nnz, rows->indptr, rows->values,
+                                             nullptr, inv_norm, nullptr,
+                                             reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "sps_row_inv_norms");
+  return SPS_OK;
+}
+
+sps_status sps_validate_csr(const sps_csr *m, void *scratch, void *stream,
+                            int64_t *first_bad_row, int32_t *reason) {
+  if (first_bad_row) *first_bad_row = -1;
+  if (reason) *reason = 0;
+  sps_status st = check_csr_shape(m, "csr");
+  if (st != SPS_OK) return st;
+  if (!scratch) return fail(SPS_ERR_INVALID_ARGUMENT, "NULL scratch");
+  if (reinterpret_cast<uintptr_t>(scratch) & 7)
+    return fail(SPS_ERR_INVALID_ARGUMENT, "scratch must be 8-byte aligned");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = sps::launch_csr_check(m->n_rows, m->n_cols, m->nnz, m->indptr, m->indices,
+                                       m->values, 1, static_cast<int32_t *>(scratch), s);
+  if (e != hipSuccess) return hip_fail(e, "sps_validate_csr");
+  int32_t flags[4];
+  e = hipMemcpyAsync(flags, scratch, sizeof flags, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "sps_validate_csr");
+  if (flags[0] == 0 && flags[1] == 0) return SPS_OK;
+  uint64_t key;
+  memcpy(&key, flags + 2, sizeof key);
+  if (first_bad_row) *first_bad_row = (int64_t)(key >> 3);
+  if (reason) *reason = (int32_t)(key & 7);
+  return fail(SPS_ERR_BAD_CSR, "non-canonical CSR at row %lld", (long long)(key >> 3));
+}
+
+}  // extern "C"

@@ -1,0 +1,89 @@
+"""The C ABI without a GPU: the library loads, exports every declared symbol,
+and its host-side argument checks return the documented statuses."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_embedding_exact_amd as sps
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_symbols():
+    text = open(os.path.join(ROOT, "include", "sps.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sps_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return sps.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_symbols()
+    assert len(names) >= 15
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+    assert set(names) == set(sps.SIGNATURES), set(names) ^ set(sps.SIGNATURES)
+
+
+def test_status_strings(lib):
+    for code in range(0, -9, -1):
+        s = lib.sps_status_string(code)
+        assert s and s != b"unknown status"
+    assert lib.sps_status_string(-99) == b"unknown status"
+
+
+def test_items_sizing(lib):
+    p, s = ctypes.c_size_t(), ctypes.c_size_t()
+    assert lib.sps_items_workspace_size(2_000_000, 1_200_000, 86_000_000, 8192,
+                                        ctypes.byref(p), ctypes.byref(s)) == 0
+    # col_ptr alone: 245 chunks x (1.2M + 1) int32
+    assert p.value >= 245 * 1_200_001 * 4 + 86_000_000 * 6
+    assert s.value >= 86_000_000 * 10
+    assert p.value % 256 == 0 and s.value % 256 == 0
+    bad = [(-1, 10, 0, 8192), (10, 0, 0, 8192), (10, 10, 0, 0), (10, 10, 0, 32769),
+           (10, 10, -5, 8192)]
+    for a in bad:
+        assert lib.sps_items_workspace_size(*a, ctypes.byref(p), ctypes.byref(s)) == -1, a
+    assert lib.sps_items_workspace_size(2**31, 10, 0, 8192, ctypes.byref(p),
+                                        ctypes.byref(s)) == -6
+    assert lib.sps_items_workspace_size(10, 10, 0, 8192, None, ctypes.byref(s)) == -1
+    assert b"NULL" in lib.sps_last_error_message()
+
+
+def test_null_handles_rejected(lib):
+    out = ctypes.c_void_p()
+    assert lib.sps_prepare(None, 8192, None, 0, None, 0, None, ctypes.byref(out)) == -1
+    assert lib.sps_prepare_queries(None, None, None, 0, None, ctypes.byref(out)) == -1
+    assert lib.sps_cosine_chunk(None, None, 0, None, 8192, None, None) == -1
+    assert lib.sps_cosine_stream(None, None, 0, 1, None, 8192, None, None) == -1
+    assert lib.sps_items_info(None, None, None, None, None, None) == -1
+    assert lib.sps_queries_inv_norms(None, None) == -1
+    size = ctypes.c_size_t()
+    assert lib.sps_queries_workspace_size(None, 10, 10, 10, ctypes.byref(size)) == -1
+    assert lib.sps_row_inv_norms(None, None, None) == -1
+    assert lib.sps_validate_csr(None, None, None, None, None) == -1
+    lib.sps_items_destroy(None)
+    lib.sps_queries_destroy(None)
+
+
+def test_csr_shape_checks(lib):
+    out = ctypes.c_void_p()
+    c = sps._Csr(10, 100, 5, 0x1000, 0x2000, 0x3000)
+    # workspace NULL after a valid shape -> invalid argument, before any device work
+    assert lib.sps_prepare(ctypes.byref(c), 8192, None, 0, None, 0, None, ctypes.byref(out)) == -1
+    c = sps._Csr(10, 0, 5, 0x1000, 0x2000, 0x3000)
+    assert lib.sps_prepare(ctypes.byref(c), 8192, None, 0, None, 0, None, ctypes.byref(out)) == -1
+    c = sps._Csr(10, 100, 5, 0x1000, None, 0x3000)
+    assert lib.sps_prepare(ctypes.byref(c), 8192, None, 0, None, 0, None, ctypes.byref(out)) == -1
+    c = sps._Csr(2**31, 100, 5, 0x1000, 0x2000, 0x3000)
+    assert lib.sps_prepare(ctypes.byref(c), 8192, None, 0, None, 0, None, ctypes.byref(out)) == -6
+    # too-small workspace is reported before any device work
+    c = sps._Csr(10, 100, 5, 0x1000, 0x2000, 0x3000)
+    assert lib.sps_prepare(ctypes.byref(c), 8192, 0x10000, 16, 0x20000, 16, None,
+                           ctypes.byref(out)) == -4
+    assert out.value is None

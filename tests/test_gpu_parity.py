@@ -1,0 +1,345 @@
+"""GPU path vs the float64 oracle, through the C ABI.
+
+Bars: bit-exact for index structures (inverted lists) and for the fp32
+inverse norms (both sides round fl32(1/sqrt(float64 sum)) once); max
+|S_gpu - S_oracle| <= 1e-5 for scores (the achieved maximum is printed
+against the page's 1e-6 goal, §2.3 of "稀疏嵌入批量相似度计算的工程化实践").
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import synth
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-5
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import sparse_embedding_exact_amd as sps
+    sps.load_library()
+    return torch, sps, torch.device("cuda:0")
+
+
+def report(name, err, n):
+    print("\n[parity] %-40s n=%-11d max|err|=%.3g (bar 1e-5; page goal 1e-6)" % (name, n, err),
+          file=sys.stderr, flush=True)
+
+
+def gpu_chunks(env, q, items, chunk_size, rows=None, sums=False):
+    """Yield (c, begin, scores[rows or all, chunk_len] numpy, row_sums numpy|None)."""
+    torch, sps, dev = env
+    it = sps.prepare(sps.CSR.from_host(items, dev), chunk_size=chunk_size)
+    qq = sps.prepare_queries(sps.CSR.from_host(q, dev), it)
+    width = min(chunk_size, items.n_rows)
+    out = torch.empty(q.n_rows, width, dtype=torch.float32, device=dev)
+    rs = torch.empty(q.n_rows, dtype=torch.float64, device=dev) if sums else None
+    sel = None if rows is None else torch.as_tensor(np.asarray(rows), device=dev)
+    for c in range(it.num_chunks):
+        sps.cosine_chunk(qq, it, c, out, rs)
+        n = it.chunk_len(c)
+        o = out[:, :n] if sel is None else out[sel, :n]
+        yield c, c * chunk_size, o.cpu().numpy(), (rs.cpu().numpy() if sums else None)
+
+
+# ---------------------------------------------------------------------------
+# norms and inverted lists: bit-exact
+# ---------------------------------------------------------------------------
+
+def _check_structures(env, orc, items, chunk_size, name):
+    torch, sps, dev = env
+    n64, inv32 = orc.row_norms(items)
+    it = sps.prepare(sps.CSR.from_host(items, dev), chunk_size=chunk_size)
+    for c in range(it.num_chunks):
+        v = it.chunk_view(c)
+        b = c * chunk_size
+        e = min(b + chunk_size, items.n_rows)
+        col_ptr, row, val = orc.chunk_csc(items, n64, b, e)
+        assert v["chunk_len"] == e - b and v["chunk_nnz"] == len(row), (name, c)
+        assert np.array_equal(v["col_ptr"].cpu().numpy(), col_ptr), (name, c, "col_ptr")
+        g_row = v["row"].cpu().numpy().view(np.uint16).astype(np.int32)
+        assert np.array_equal(g_row, row), (name, c, "row ids")
+        g_val = v["val"].cpu().numpy()
+        assert np.array_equal(g_val.view(np.uint32), val.view(np.uint32)), (name, c, "values")
+        g_inv = v["item_inv_norm"].cpu().numpy()
+        assert np.array_equal(g_inv.view(np.uint32), inv32[b:e].view(np.uint32)), (name, c)
+    print("\n[parity] %s: %d chunks, inverted lists + norms bit-exact" % (name, it.num_chunks),
+          file=sys.stderr, flush=True)
+
+
+def test_structures_tiny(env, orc):
+    _, items, _ = synth.make_workload("tiny")
+    _check_structures(env, orc, items, 4096, "tiny")
+
+
+def test_structures_zipf_ragged(env, orc):
+    _, items, _ = synth.make_workload("mid", n_item=30001)
+    _check_structures(env, orc, items, 8192, "mid 30001 items (ragged tail)")
+
+
+def test_structures_dense_and_edge(env, orc):
+    _, items, _ = synth.make_workload("dense", n_item=20000)
+    _check_structures(env, orc, items, 8192, "dense 20000 items")
+    _, items, _ = synth.make_workload("edge", n_item=17000)
+    _check_structures(env, orc, items, 8192, "edge 17000 items (empty rows, signed)")
+
+
+def test_query_inverse_norms(env, orc):
+    torch, sps, dev = env
+    for name, kw in [("tiny", {}), ("edge", {"n_item": 5000, "n_query": 777})]:
+        q, items, _ = synth.make_workload(name, **kw)
+        _, inv32 = orc.row_norms(q)
+        got = sps.row_inv_norms(sps.CSR.from_host(q, dev)).cpu().numpy()
+        assert np.array_equal(got.view(np.uint32), inv32.view(np.uint32)), name
+        it = sps.prepare(sps.CSR.from_host(items, dev), chunk_size=4096)
+        qq = sps.prepare_queries(sps.CSR.from_host(q, dev), it)
+        assert np.array_equal(qq.inv_norm.cpu().numpy().view(np.uint32), inv32.view(np.uint32))
+
+
+# ---------------------------------------------------------------------------
+# scores: every score on the two small workloads
+# ---------------------------------------------------------------------------
+
+def test_scores_tiny_full(env, orc):
+    q, items, _ = synth.make_workload("tiny")
+    ref = orc.scores(q, items)
+    (c, b, got, _), = list(gpu_chunks(env, q, items, 4096))
+    err = float(np.abs(got - ref).max())
+    report("tiny 256x4096 all scores", err, got.size)
+    assert err <= TOL
+
+
+def test_scores_mid_full(env, orc):
+    q, items, _ = synth.make_workload("mid")
+    worst, n = 0.0, 0
+    qn, _ = orc.row_norms(q)
+    inn, _ = orc.row_norms(items)
+    for c, b, got, rs in gpu_chunks(env, q, items, 8192, sums=True):
+        ref = orc.scores(q, items, q_norm=qn, i_norm=inn, item_begin=b,
+                         item_end=b + got.shape[1])
+        worst = max(worst, float(np.abs(got - ref).max()))
+        n += got.size
+        assert np.abs(rs - got.astype(np.float64).sum(1)).max() <= 1e-9
+    report("mid 2000x100000 all scores (13 chunks)", worst, n)
+    assert n == 2000 * 100000
+    assert worst <= TOL
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads: sampled rows x all items + closed-form row sums of
+# every chunk (the sums of the exact scores, by linearity)
+# ---------------------------------------------------------------------------
+
+def _sampled(env, orc, name, n_rows_sampled, self_scores=False):
+    w = synth.WORKLOADS[name]
+    q, items, extra = synth.make_workload(name)
+    rng = np.random.default_rng(1234)
+    rows = np.sort(rng.choice(q.n_rows, n_rows_sampled, replace=False))
+    qn, _ = orc.row_norms(q)
+    inn, _ = orc.row_norms(items)
+    ref_sums = orc.chunk_row_sums(q, items, w.chunk_size, q_norm=qn, i_norm=inn)
+    worst, worst_sum, n = 0.0, 0.0, 0
+    self_err = 0.0
+    torch, sps, dev = env
+    it = sps.prepare(sps.CSR.from_host(items, dev), chunk_size=w.chunk_size)
+    qq = sps.prepare_queries(sps.CSR.from_host(q, dev), it)
+    out = torch.empty(q.n_rows, w.chunk_size, dtype=torch.float32, device=dev)
+    rs = torch.empty(it.num_chunks, q.n_rows, dtype=torch.float64, device=dev)
+    sel = torch.as_tensor(rows, device=dev)
+    got_rows = np.empty((len(rows), items.n_rows), dtype=np.float32)
+    self_cols = None
+    if self_scores:
+        perm = extra["query_item"]
+        self_vals = np.full(q.n_rows, np.nan, dtype=np.float64)
+    for c in range(it.num_chunks):
+        sps.cosine_chunk(qq, it, c, out, rs[c])
+        n_c = it.chunk_len(c)
+        b = c * w.chunk_size
+        got_rows[:, b:b + n_c] = out[sel, :n_c].cpu().numpy()
+        if self_scores:
+            inside = np.nonzero((perm >= b) & (perm < b + n_c))[0]
+            if len(inside):
+                qi = torch.as_tensor(inside, device=dev)
+                cj = torch.as_tensor(perm[inside] - b, device=dev)
+                self_vals[inside] = out[qi, cj].double().cpu().numpy()
+    torch.cuda.synchronize()
+    ref = orc.scores(q, items, q_norm=qn, i_norm=inn, q_rows=rows)
+    worst = float(np.abs(got_rows - ref).max())
+    n = got_rows.size
+    g_sums = rs.cpu().numpy()
+    worst_sum = float(np.abs(g_sums - ref_sums).max())
+    # each row sum adds at most chunk_len fp32 errors of the scores
+    report("%s %d sampled rows x all items" % (name, len(rows)), worst, n)
+    print("[parity] %s row sums of %d chunks x %d rows: max|err|=%.3g" %
+          (name, it.num_chunks, q.n_rows, worst_sum), file=sys.stderr, flush=True)
+    assert worst <= TOL
+    assert worst_sum <= TOL * w.chunk_size
+    if self_scores:
+        empty = np.diff(q.indptr) == 0
+        self_err = float(np.abs(self_vals[~empty] - 1.0).max())
+        print("[parity] %s self-scores of %d non-empty queries: max|S-1|=%.3g; %d empty -> 0" %
+              (name, int((~empty).sum()), self_err, int(empty.sum())), file=sys.stderr)
+        assert self_err <= TOL
+        assert np.all(self_vals[empty] == 0.0)
+
+
+def test_pages_shape_sampled(env, orc):
+    _sampled(env, orc, "pages", 64)
+
+
+def test_dense_overlap_sampled(env, orc):
+    _sampled(env, orc, "dense", 128)
+
+
+def test_edge_heavy_tail_sampled(env, orc):
+    _sampled(env, orc, "edge", 128, self_scores=True)
+
+
+# ---------------------------------------------------------------------------
+# edge cases
+# ---------------------------------------------------------------------------
+
+def _dense_ref(orc, q, items):
+    return orc.scores(q, items)
+
+
+@pytest.mark.parametrize("rows", ["1", "2", "4", "8"])
+def test_rows_per_workgroup_variants(env, orc, rows, monkeypatch):
+    """Odd query counts (not a multiple of the rows per workgroup), every R."""
+    monkeypatch.setenv("SPS_SCORE_ROWS", rows)
+    q, items, _ = synth.make_workload("mid", n_item=9001, n_query=37)
+    ref = orc.scores(q, items)
+    got = np.concatenate([g for _, _, g, _ in gpu_chunks(env, q, items, 4096)], axis=1)
+    err = float(np.abs(got - ref).max())
+    report("R=%s 37x9001 chunk 4096" % rows, err, got.size)
+    assert err <= TOL
+
+
+def test_edge_rows_and_ld(env, orc):
+    """Empty rows on both sides, explicit zeros, a dim no item has, a chunk
+    length that is not a multiple of 4, ld > chunk_len (the tail untouched)."""
+    import pins
+    torch, sps, dev = env
+    rng = np.random.default_rng(99)
+    items = pins.random_csr(rng, 1003, 5000, 0, 30, signed=True, empty_frac=0.1,
+                            explicit_zero_frac=0.05)
+    q = pins.random_csr(rng, 21, 5000, 0, 30, signed=True, empty_frac=0.2,
+                        explicit_zero_frac=0.05)
+    # a query on a dim beyond every item's support
+    q = pins.csr_from_rows([list(zip(*q.row(r))) for r in range(q.n_rows)] + [[(4999, 1.0)]],
+                           5000)
+    ref = orc.scores(q, items)
+    it = sps.prepare(sps.CSR.from_host(items, dev), chunk_size=333)
+    qq = sps.prepare_queries(sps.CSR.from_host(q, dev), it)
+    ld = 341  # not a multiple of 4: scalar stores
+    big = torch.full((q.n_rows, ld), float("nan"), dtype=torch.float32, device=dev)
+    worst = 0.0
+    for c in range(it.num_chunks):
+        big.fill_(float("nan"))
+        sps.cosine_chunk(qq, it, c, big)
+        n = it.chunk_len(c)
+        g = big.cpu().numpy()
+        assert np.isnan(g[:, n:]).all(), "columns beyond the chunk were written"
+        worst = max(worst, float(np.abs(g[:, :n] - ref[:, c * 333:c * 333 + n]).max()))
+    report("random signed 22x1003 chunk 333 ld 341", worst, ref.size)
+    assert worst <= TOL
+    # empty query rows and zero-norm items give exactly 0
+    got = np.concatenate([g for _, _, g, _ in gpu_chunks(env, q, items, 333)], axis=1)
+    qn, _ = orc.row_norms(q)
+    inn, _ = orc.row_norms(items)
+    assert np.all(got[qn == 0, :] == 0.0) and np.all(got[:, inn == 0] == 0.0)
+    assert np.all(got[-1] == 0.0)
+
+
+def test_chunk_size_extremes(env, orc):
+    q, items, _ = synth.make_workload("tiny", n_item=1500, n_query=50)
+    ref = orc.scores(q, items)
+    for cs in (1, 7, 1500, 32768):
+        got = np.concatenate([g for _, _, g, _ in gpu_chunks(env, q, items, cs)], axis=1)
+        err = float(np.abs(got - ref).max())
+        report("tiny 50x1500 chunk %d" % cs, err, got.size)
+        assert err <= TOL
+
+
+def test_chunk_size_invariance(env):
+    """Scores with 4096-item and 8192-item chunks agree (to fp32 accumulation order)."""
+    q, items, _ = synth.make_workload("mid", n_item=16384, n_query=200)
+    a = np.concatenate([g for _, _, g, _ in gpu_chunks(env, q, items, 4096)], axis=1)
+    b = np.concatenate([g for _, _, g, _ in gpu_chunks(env, q, items, 8192)], axis=1)
+    assert np.abs(a - b).max() <= 2e-6
+
+
+def test_stream_entry_and_bulk(env, orc):
+    torch, sps, dev = env
+    q, items, _ = synth.make_workload("mid", n_item=20000, n_query=64)
+    ref = orc.scores(q, items)
+    full = sps.bulk_similarity(sps.CSR.from_host(q, dev), sps.CSR.from_host(items, dev),
+                               chunk_size=8192)
+    assert float(np.abs(full.cpu().numpy() - ref).max()) <= TOL
+    it = sps.prepare(sps.CSR.from_host(items, dev), chunk_size=8192)
+    qq = sps.prepare_queries(sps.CSR.from_host(q, dev), it)
+    out = torch.empty(q.n_rows, 8192, dtype=torch.float32, device=dev)
+    sums = torch.empty(it.num_chunks, q.n_rows, dtype=torch.float64, device=dev)
+    sps.cosine_stream(qq, it, 0, it.num_chunks, out, sums)
+    last = it.chunk_len(it.num_chunks - 1)
+    b = (it.num_chunks - 1) * 8192
+    assert float(np.abs(out[:, :last].cpu().numpy() - ref[:, b:]).max()) <= TOL
+    s = sums.cpu().numpy()
+    for c in range(it.num_chunks):
+        n = it.chunk_len(c)
+        assert np.abs(s[c] - ref[:, c * 8192:c * 8192 + n].sum(1)).max() <= 1e-4
+
+
+def test_validate_and_bad_input(env):
+    """sps_validate_csr names each fault; a structurally bad CSR is scored as
+    empty by the prepare calls (no access outside the buffers)."""
+    import pins
+    from synth import HostCSR
+    torch, sps, dev = env
+    ok = pins.csr_from_rows([[(1, 1.0), (5, 2.0)], [], [(0, 3.0), (7, 1.0)]], 8)
+    assert sps.validate_csr(sps.CSR.from_host(ok, dev)) == (True, -1, 0)
+    cases = [
+        (HostCSR(ok.indptr, np.array([5, 1, 0, 7], np.int32), ok.values, 3, 8), 0, 2),
+        (HostCSR(ok.indptr, np.array([1, 5, 0, 9], np.int32), ok.values, 3, 8), 2, 3),
+        (HostCSR(ok.indptr, ok.indices, np.array([1, 2, np.inf, 1], np.float32), 3, 8), 2, 4),
+        (HostCSR(np.array([0, 3, 2, 4], np.int32), ok.indices, ok.values, 3, 8), 1, 1),
+    ]
+    for m, row, why in cases:
+        assert sps.validate_csr(sps.CSR.from_host(m, dev)) == (False, row, why)
+    # an index outside [0, n_cols) in the items: prepared as empty, scored 0
+    bad_items = HostCSR(ok.indptr, np.array([1, 5, 0, 99], np.int32), ok.values, 3, 8)
+    it = sps.prepare(sps.CSR.from_host(bad_items, dev), chunk_size=2)
+    qq = sps.prepare_queries(sps.CSR.from_host(ok, dev), it)
+    out = torch.full((3, 2), float("nan"), device=dev)
+    for c in range(it.num_chunks):
+        sps.cosine_chunk(qq, it, c, out)
+        assert torch.all(out[:, :it.chunk_len(c)] == 0).item()
+    # and in the queries
+    it = sps.prepare(sps.CSR.from_host(ok, dev), chunk_size=2)
+    qq = sps.prepare_queries(sps.CSR.from_host(bad_items, dev), it)
+    for c in range(it.num_chunks):
+        out.fill_(float("nan"))
+        sps.cosine_chunk(qq, it, c, out)
+        assert torch.all(out[:, :it.chunk_len(c)] == 0).item()
+
+
+def test_argument_errors(env):
+    torch, sps, dev = env
+    q, items, _ = synth.make_workload("tiny", n_item=100, n_query=4)
+    it = sps.prepare(sps.CSR.from_host(items, dev), chunk_size=64)
+    qq = sps.prepare_queries(sps.CSR.from_host(q, dev), it)
+    out = torch.empty(4, 64, device=dev)
+    with pytest.raises(sps.SpsError) as e:
+        sps.cosine_chunk(qq, it, 2, out)
+    assert e.value.status == -5
+    other = synth.make_corpus(10, 999, 1, 0, nnz=("uniform", 1, 3), idx=("uniform",), val=0)
+    with pytest.raises(sps.SpsError) as e:
+        sps.prepare_queries(sps.CSR.from_host(other, dev), it)
+    assert e.value.status == -3
