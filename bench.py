@@ -38,6 +38,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic", default=None,
                     help="JSON file with measured HBM bytes per score launch")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB (5 times) and "
+                         "exit: the reference for scaling FETCH_SIZE / WRITE_SIZE counters")
     return ap.parse_args()
 
 
@@ -55,6 +58,16 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.copy_probe:
+        n = args.copy_probe * (1 << 20) // 4
+        a = torch.ones(n, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": 4 * n, "launches": 5}))
+        return
 
     import sparse_embedding_exact_amd as sps
     import synth

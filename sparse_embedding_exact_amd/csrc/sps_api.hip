@@ -64,15 +64,29 @@ sps_status check_csr_shape(const sps_csr *m, const char *what) {
   return SPS_OK;
 }
 
-// LDS per workgroup on gfx950 (CDNA4): 160 KiB.
+// LDS per workgroup on gfx950 (CDNA4): 160 KiB. When a device is present
+// its opt-in limit is used if smaller.
 constexpr size_t kLdsLimit = 163840;
+
+size_t lds_limit() {
+  static size_t cached = 0;
+  if (cached) return cached;
+  size_t lim = kLdsLimit;
+  int dev = 0, v = 0;
+  if (hipGetDevice(&dev) == hipSuccess &&
+      hipDeviceGetAttribute(&v, hipDeviceAttributeSharedMemPerBlockOptin, dev) == hipSuccess &&
+      v > 0 && (size_t)v < lim)
+    lim = (size_t)v;
+  cached = lim;
+  return lim;
+}
 
 // Rows per score workgroup. SPS_SCORE_ROWS (1, 2, 4 or 8) overrides the
 // default when the chunk fits.
 int pick_rows(int32_t chunk_len, size_t lds_limit) {
   const int maxr = sps::score_max_rows(chunk_len, lds_limit);
   if (maxr == 0) return 0;
-  int r = maxr < 4 ? maxr : 4;
+  int r = 1;
   if (const char *env = getenv("SPS_SCORE_ROWS")) {
     const int v = atoi(env);
     if ((v == 1 || v == 2 || v == 4 || v == 8) && v <= maxr) r = v;
@@ -134,7 +148,7 @@ ItemsLayout items_layout(int64_t n, int64_t dim, int64_t nnz, int32_t C) {
 }
 
 struct QueriesLayout {
-  size_t flags, inv, gptr, gdim, gval, total;
+  size_t flags, inv, norm64, gptr, gdim, gval, total;
   bool overflow;
 };
 
@@ -144,6 +158,7 @@ QueriesLayout queries_layout(int64_t n, int64_t nnz, int R) {
   Layout p;
   L.flags = p.add(sps::kFlagsInts, 4);
   L.inv = p.add(n, 4);
+  L.norm64 = p.add(n, 8);
   L.gptr = p.add(ng + 1, 4);
   L.gdim = p.add(nnz, 4);
   L.gval = p.add((uint64_t)nnz * (uint64_t)R, 4);
@@ -311,7 +326,7 @@ sps_status sps_queries_workspace_size(const sps_items *items, int64_t n_rows, in
   if (dim != items->dim)
     return fail(SPS_ERR_DIM_MISMATCH, "query dim %lld != item dim %lld", (long long)dim,
                 (long long)items->dim);
-  const int R = pick_rows(items->chunk_size, kLdsLimit);
+  const int R = pick_rows(items->chunk_size, lds_limit());
   if (R == 0) return fail(SPS_ERR_UNSUPPORTED, "chunk of %d items exceeds LDS", items->chunk_size);
   const QueriesLayout L = queries_layout(n_rows, nnz, R);
   if (L.overflow || (uint64_t)nnz * (uint64_t)R >= (uint64_t)kI32Max * 8)
@@ -337,7 +352,7 @@ sps_status sps_prepare_queries(const sps_csr *queries, const sps_items *items, v
     return fail(SPS_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return fail(SPS_ERR_HIP, "no HIP device");
-  const int R = pick_rows(items->chunk_size, kLdsLimit);
+  const int R = pick_rows(items->chunk_size, lds_limit());
   const QueriesLayout L = queries_layout(queries->n_rows, queries->nnz, R);
   sps::QueriesDev d{};
   d.n_rows = queries->n_rows;
@@ -350,6 +365,7 @@ sps_status sps_prepare_queries(const sps_csr *queries, const sps_items *items, v
   d.values = queries->values;
   d.flags = at<int32_t>(workspace, L.flags);
   d.inv_norm = at<float>(workspace, L.inv);
+  d.norm64 = at<double>(workspace, L.norm64);
   d.grp_ptr = at<int32_t>(workspace, L.gptr);
   d.grp_dim = at<int32_t>(workspace, L.gdim);
   d.grp_val = at<float>(workspace, L.gval);

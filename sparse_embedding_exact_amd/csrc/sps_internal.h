@@ -49,9 +49,10 @@ struct QueriesDev {
   const float *values;
   int32_t *flags;
   float *inv_norm;
+  double *norm64;     // n_rows
   int32_t *grp_ptr;   // n_groups + 1
   int32_t *grp_dim;   // nnz
-  float *grp_val;     // nnz * R
+  float *grp_val;     // nnz * R: fl32(q / |q|) * 2^30 per row (0 where absent)
 };
 hipError_t launch_prepare_queries(const QueriesDev &d, hipStream_t s);
 

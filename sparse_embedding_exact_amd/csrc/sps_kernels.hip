@@ -14,6 +14,7 @@
 // buffers the host sized, whatever the CSR contents.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #include "sps_internal.h"
 
@@ -453,26 +454,35 @@ hipError_t launch_prepare_items(const ItemsDev &d, hipStream_t s) {
 // ---------------------------------------------------------------------------
 // Query row groups: rows [g*R, g*R+R) merged into one ascending dim list with
 // R values per dim (0 where a row lacks the dim). Computed once per batch.
+// The stored value is the row-normalised query value rounded once to fp32,
+// fl32(q_d / |q|) (|q| in float64, §5.2), times 2^30 (exact: a power of two),
+// the scale of the fixed-point accumulators of the score kernel.
 // ---------------------------------------------------------------------------
+
+constexpr float kFixScale = 1073741824.0f;        // 2^30
+constexpr float kFixInv = 9.313225746154785e-10f;  // 2^-30
 
 template <bool FILL>
 __global__ __launch_bounds__(256) void group_merge_kernel(
     int64_t n_rows, int64_t nnz, int32_t R, int32_t n_groups, const int32_t *__restrict__ indptr,
     const int32_t *__restrict__ indices, const float *__restrict__ values,
-    const int32_t *__restrict__ flags, int32_t *__restrict__ grp_ptr,
-    int32_t *__restrict__ grp_dim, float *__restrict__ grp_val) {
+    const double *__restrict__ norm64, const int32_t *__restrict__ flags,
+    int32_t *__restrict__ grp_ptr, int32_t *__restrict__ grp_dim, float *__restrict__ grp_val) {
   const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (g >= n_groups) return;
   int64_t p[8], e[8];
+  double nrm[8];
   const bool bad = flags[0] != 0;
   for (int r = 0; r < 8; ++r) {
     const int64_t q = g * R + r;
     if (r < R && q < n_rows && !bad) {
       p[r] = indptr[q];
       e[r] = indptr[q + 1];
+      nrm[r] = norm64[q];
     } else {
       p[r] = 0;
       e[r] = 0;
+      nrm[r] = 0.0;
     }
   }
   int64_t out = FILL ? grp_ptr[g] : 0;
@@ -486,7 +496,7 @@ __global__ __launch_bounds__(256) void group_merge_kernel(
     for (int r = 0; r < R; ++r) {
       float v = 0.0f;
       if (p[r] < e[r] && indices[p[r]] == dmin) {
-        v = values[p[r]];
+        if (nrm[r] > 0.0) v = (float)((double)values[p[r]] / nrm[r]) * kFixScale;
         ++p[r];
       }
       if (FILL) grp_val[out * R + r] = v;
@@ -516,72 +526,94 @@ hipError_t launch_prepare_queries(const QueriesDev &d, hipStream_t s) {
   hipError_t e;
   e = launch_csr_check(d.n_rows, d.dim, d.nnz, d.indptr, d.indices, d.values, 0, d.flags, s);
   if (e != hipSuccess) return e;
-  e = launch_row_norms(d.n_rows, d.nnz, d.indptr, d.values, d.flags, d.inv_norm, nullptr, s);
+  e = launch_row_norms(d.n_rows, d.nnz, d.indptr, d.values, d.flags, d.inv_norm, d.norm64, s);
   if (e != hipSuccess) return e;
   e = launch_fill_i32(d.grp_ptr, (int64_t)d.n_groups + 1, 0, s);
   if (e != hipSuccess) return e;
   if (d.n_groups == 0) return hipSuccess;
   const unsigned blocks = (unsigned)((d.n_groups + 255) / 256);
   hipLaunchKernelGGL(group_merge_kernel<false>, dim3(blocks), dim3(256), 0, s, d.n_rows, d.nnz,
-                     d.R, d.n_groups, d.indptr, d.indices, d.values, d.flags, d.grp_ptr,
-                     d.grp_dim, d.grp_val);
+                     d.R, d.n_groups, d.indptr, d.indices, d.values, d.norm64, d.flags,
+                     d.grp_ptr, d.grp_dim, d.grp_val);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(scan_inplace_kernel<1024>, dim3(1), dim3(1024), 0, s, d.grp_ptr,
                      (int64_t)d.n_groups + 1);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(group_merge_kernel<true>, dim3(blocks), dim3(256), 0, s, d.n_rows, d.nnz,
-                     d.R, d.n_groups, d.indptr, d.indices, d.values, d.flags, d.grp_ptr,
-                     d.grp_dim, d.grp_val);
+                     d.R, d.n_groups, d.indptr, d.indices, d.values, d.norm64, d.flags,
+                     d.grp_ptr, d.grp_dim, d.grp_val);
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
 // Score kernel: one workgroup per group of R query rows, one chunk.
 //
-// LDS holds acc[R][lenp] float32 (lenp = chunk_len rounded up to 4). For a
-// batch of up to NT dims of the group's merged list, thread t looks up dim
-// t's posting list [col_ptr[d], col_ptr[d+1]); a block scan lays all lists
-// of the batch end to end, and the threads stride through that flat range:
-// each loaded posting entry (item j, value w) is added, for every row r of
-// the group holding the dim, as acc[r][j] += q_r,d * w with an LDS float
-// atomic. Item ids are chunk-local, so j < chunk_len.
-// Epilogue: out[q, j] = acc[r][j] * inv_norm[q], full rows, 16-byte stores
-// when the row start is aligned; optional float64 row sum of what was
-// written.
+// LDS holds acc[R][lenp] as 32-bit fixed point with 30 fraction bits
+// (lenp = chunk_len rounded up to 4). The group's merged dim list is taken in
+// batches; thread t looks up dim t's posting list [col_ptr[d], col_ptr[d+1])
+// in the chunk. Each loaded posting entry (item j, value w = i_d / |i|) is
+// added, for every row r of the group holding the dim, as
+//     acc[r][j] += rn(fl32(qs_r,d * w)),   qs_r,d = fl32(q_d / |q|) * 2^30,
+// with an LDS integer atomic (ds_add_u32). Why integers: on gfx950 the LDS
+// float atomic (ds_add_f32) sustains about 0.3 updates per CU cycle while
+// ds_add_u32 sustains about 14. Why it cannot overflow: the partial sums of
+// normalised rows are bounded by sum |q^_d i^_d| <= 1 (Cauchy-Schwarz), so
+// |acc| <= 2^30 plus rounding, inside int32. Integer addition is exact and
+// order independent, so the result does not depend on how waves interleave
+// (bitwise reproducible). Error per term: fp32 product rounding (<= 2^-24 of
+// the term) plus fixed-point rounding (<= 2^-31 absolute).
+//
+//  - long lists (>= kLongList entries) are walked by the whole workgroup one
+//    list at a time: the query values are uniform (scalar registers), and U
+//    independent loads per thread are in flight before their atomics;
+//  - short lists are laid end to end (block scan of their lengths) and the
+//    threads stride through that flat range.
+//
+// Epilogue: out[q, j] = fl32(acc[r][j]) * 2^-30 over full rows, 16-byte
+// nontemporal stores when the row start is aligned (the scores are streamed
+// out and not re-read, so they should not displace posting lists from L2);
+// optional float64 row sum of the values written.
 // ---------------------------------------------------------------------------
 
-constexpr int kScoreNT = 256;
-constexpr int kUnroll = 4;
+constexpr int kLongList = 128;
+constexpr int kBatch = 256;
 
-template <int R, int NT>
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <int R, int NT, int U>
 __global__ __launch_bounds__(NT) void score_kernel(
     const int32_t *__restrict__ grp_ptr, const int32_t *__restrict__ grp_dim,
-    const float *__restrict__ grp_val, const float *__restrict__ q_inv, int64_t n_q,
-    int64_t dim, const int32_t *__restrict__ col_ptr, const uint16_t *__restrict__ prow_all,
+    const float *__restrict__ grp_val, int64_t n_q, int64_t dim,
+    const int32_t *__restrict__ col_ptr, const uint16_t *__restrict__ prow_all,
     const float *__restrict__ pval_all, const int32_t *__restrict__ chunk_base, int32_t chunk,
     int32_t chunk_len, int32_t lenp, float *__restrict__ out, int64_t ld,
     double *__restrict__ row_sums, int vec4) {
-  extern __shared__ float acc[];
-  __shared__ int32_t s_start[NT];
-  __shared__ int32_t s_pre[NT + 1];
-  __shared__ float s_qv[NT * R];
-  __shared__ int32_t ws[NT / 64];
+  constexpr int B = kBatch < NT ? kBatch : NT;  // merged-list entries per batch
+  extern __shared__ int acc[];
+  __shared__ int32_t s_start[B];   // posting start per batch entry
+  __shared__ int32_t s_len[B];     // posting length per batch entry
+  __shared__ float s_qv[B * R];    // query values per batch entry
+  __shared__ int32_t s_long[B];    // batch entries with long lists (compacted)
+  __shared__ int32_t s_sidx[B];    // batch entries with short lists (compacted)
+  __shared__ int32_t s_spre[B + 1];  // flat offsets of the short lists
+  __shared__ int64_t ws[NT / 64];
   __shared__ double ds[NT / 64];
 
   const int t = threadIdx.x;
   const int64_t g = blockIdx.x;
   const int64_t q0 = g * R;
   const int32_t cb0 = chunk_base[chunk];
-  const int32_t chunk_nnz = chunk_base[chunk + 1] - cb0 > 0 ? chunk_base[chunk + 1] - cb0 : 0;
+  const int32_t cb1 = chunk_base[chunk + 1];
+  const int32_t chunk_nnz = cb1 - cb0 > 0 ? cb1 - cb0 : 0;
   const uint16_t *__restrict__ prow = prow_all + cb0;
   const float *__restrict__ pval = pval_all + cb0;
 
-  float4 *acc4 = reinterpret_cast<float4 *>(acc);
-  for (int k = t; k < R * lenp / 4; k += NT) acc4[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+  int4 *acc4 = reinterpret_cast<int4 *>(acc);
+  for (int k = t; k < R * lenp / 4; k += NT) acc4[k] = make_int4(0, 0, 0, 0);
 
   const int32_t e0 = grp_ptr[g], e1 = grp_ptr[g + 1];
-  for (int32_t eb = e0; eb < e1; eb += NT) {
-    const int n = (e1 - eb) < NT ? (e1 - eb) : NT;
+  for (int32_t eb = e0; eb < e1; eb += B) {
+    const int n = (e1 - eb) < B ? (e1 - eb) : B;
     int32_t s = 0, L = 0;
     if (t < n) {
       const int32_t d = grp_dim[eb + t];
@@ -593,51 +625,103 @@ __global__ __launch_bounds__(NT) void score_kernel(
 #pragma unroll
       for (int r = 0; r < R; ++r) s_qv[t * R + r] = grp_val[(int64_t)(eb + t) * R + r];
     }
-    s_start[t] = s;
-    int32_t total;
-    const int32_t incl = block_incl_scan<NT>(L, ws, &total);
-    s_pre[t + 1] = incl;
-    if (t == 0) s_pre[0] = 0;
+    if (t < B) {
+      s_start[t] = s;
+      s_len[t] = L;
+    }
+    // compaction: (short-list lengths | short count << 32 | long count << 48)
+    const bool is_long = L >= kLongList;
+    const bool is_short = L > 0 && !is_long;
+    const int64_t key = (is_short ? (int64_t)L : 0) + ((int64_t)is_short << 32) +
+                        ((int64_t)is_long << 48);
+    int64_t tot;
+    const int64_t ex = block_incl_scan<NT>(key, ws, &tot) - key;
+    if (is_long) s_long[(ex >> 48) & 0xFFFF] = t;
+    if (is_short) {
+      const int si = (int)((ex >> 32) & 0xFFFF);
+      s_sidx[si] = t;
+      s_spre[si + 1] = (int32_t)(ex & 0xFFFFFFFFll) + L;
+    }
+    if (t == 0) s_spre[0] = 0;
+    const int n_long = (int)((tot >> 48) & 0xFFFF);
+    const int n_short = (int)((tot >> 32) & 0xFFFF);
+    const int32_t short_total = (int32_t)(tot & 0xFFFFFFFFll);
     __syncthreads();
 
-    int gi = 0;
-    for (int32_t f0 = t; f0 < total; f0 += NT * kUnroll) {
-      int32_t p[kUnroll];
-      int gs[kUnroll];
+    // ---- long lists: whole workgroup, one list at a time ----
+    int32_t rot = 0;  // rotates the thread <-> entry assignment between lists
+    for (int h = 0; h < n_long; ++h) {
+      const int k = __builtin_amdgcn_readfirstlane(s_long[h]);
+      const int32_t st = __builtin_amdgcn_readfirstlane(s_start[k]);
+      const int32_t len = __builtin_amdgcn_readfirstlane(s_len[k]);
+      float qv[R];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
+      for (int r = 0; r < R; ++r)
+        qv[r] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(s_qv[k * R + r])));
+      const int32_t first = (t - rot) & (NT - 1);
+      rot = (rot + len) & (NT - 1);
+      const uint32_t last = (uint32_t)(st + len - 1);
+      for (int32_t f0 = first; f0 < len; f0 += NT * U) {
+        uint32_t rw[U];
+        float w[U];
+        // indices past the list end are clamped to its last entry, so every
+        // load is in bounds and unconditional; those lanes skip the adds
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const uint32_t idx = min((uint32_t)(st + f0 + u * NT), last);
+          rw[u] = prow[idx];
+          w[u] = pval[idx];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          if (f0 + u * NT >= len || rw[u] >= (uint32_t)chunk_len) continue;
+#pragma unroll
+          for (int r = 0; r < R; ++r)
+            if (qv[r] != 0.0f) atomicAdd(&acc[r * lenp + (int)rw[u]], __float2int_rn(qv[r] * w[u]));
+        }
+      }
+    }
+
+    // ---- short lists: flat range over all of them ----
+    int gi = 0;
+    for (int32_t f0 = t; f0 < short_total; f0 += NT * U) {
+      int32_t p[U];
+      int gs[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
         const int32_t f = f0 + u * NT;
         p[u] = -1;
         gs[u] = 0;
-        if (f < total) {
-          while (s_pre[gi + 1] <= f) ++gi;
-          p[u] = s_start[gi] + (f - s_pre[gi]);
-          gs[u] = gi;
+        if (f < short_total) {
+          while (s_spre[gi + 1] <= f) ++gi;
+          const int k = s_sidx[gi];
+          p[u] = s_start[k] + (f - s_spre[gi]);
+          gs[u] = k;
         }
       }
-      uint32_t rw[kUnroll];
-      float w[kUnroll];
+      uint32_t rw[U];
+      float w[U];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
+      for (int u = 0; u < U; ++u) {
         if (p[u] >= 0) {
           rw[u] = prow[p[u]];
           w[u] = pval[p[u]];
         } else {
-          rw[u] = 0;
+          rw[u] = 0xFFFFFFFFu;
           w[u] = 0.f;
         }
       }
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        if (p[u] < 0) continue;
-        const int j = (int)rw[u] < chunk_len ? (int)rw[u] : 0;
+      for (int u = 0; u < U; ++u) {
+        if (rw[u] >= (uint32_t)chunk_len) continue;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
           const float qv = s_qv[gs[u] * R + r];
-          if (qv != 0.0f) atomicAdd(&acc[r * lenp + j], qv * w[u]);
+          if (qv != 0.0f) atomicAdd(&acc[r * lenp + (int)rw[u]], __float2int_rn(qv * w[u]));
         }
       }
     }
+    (void)n_short;
     __syncthreads();
   }
   __syncthreads();
@@ -646,31 +730,27 @@ __global__ __launch_bounds__(NT) void score_kernel(
   for (int r = 0; r < R; ++r) {
     const int64_t q = q0 + r;
     if (q >= n_q) break;
-    const float inv = q_inv[q];
     float *orow = out + q * ld;
-    const float *arow = acc + r * lenp;
+    const int *arow = acc + r * lenp;
     double rs = 0.0;
     int jstart = 0;
     if (vec4) {
       const int n4 = chunk_len >> 2;
-      const float4 *a4 = reinterpret_cast<const float4 *>(arow);
-      float4 *o4 = reinterpret_cast<float4 *>(orow);
+      const int4 *a4 = reinterpret_cast<const int4 *>(arow);
+      f32x4 *o4 = reinterpret_cast<f32x4 *>(orow);
       for (int k = t; k < n4; k += NT) {
-        float4 a = a4[k];
-        if (inv != 0.0f) {
-          a.x *= inv; a.y *= inv; a.z *= inv; a.w *= inv;
-        } else {
-          a = make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-        o4[k] = a;
-        rs += (double)a.x + (double)a.y + (double)a.z + (double)a.w;
+        const int4 a = a4[k];
+        const f32x4 v = {(float)a.x * kFixInv, (float)a.y * kFixInv, (float)a.z * kFixInv,
+                         (float)a.w * kFixInv};
+        __builtin_nontemporal_store(v, o4 + k);
+        rs += ((double)v.x + (double)v.y) + ((double)v.z + (double)v.w);
       }
       jstart = n4 << 2;
     }
     for (int j = jstart + t; j < chunk_len; j += NT) {
-      const float a = (inv != 0.0f) ? arow[j] * inv : 0.0f;
-      orow[j] = a;
-      rs += (double)a;
+      const float v = (float)arow[j] * kFixInv;
+      __builtin_nontemporal_store(v, &orow[j]);
+      rs += (double)v;
     }
     if (row_sums) {
       rs = wave_sum(rs);
@@ -686,11 +766,35 @@ __global__ __launch_bounds__(NT) void score_kernel(
   }
 }
 
+static int score_nt() {
+  static int v = -1;
+  if (v < 0) {
+    v = 256;
+    if (const char *e = getenv("SPS_SCORE_THREADS")) {
+      const int x = atoi(e);
+      if (x == 256 || x == 512 || x == 1024) v = x;
+    }
+  }
+  return v;
+}
+
+static int score_unroll() {
+  static int v = -1;
+  if (v < 0) {
+    v = 8;
+    if (const char *e = getenv("SPS_SCORE_UNROLL")) {
+      const int x = atoi(e);
+      if (x == 4 || x == 8) v = x;
+    }
+  }
+  return v;
+}
+
 size_t score_lds_bytes(int R, int32_t chunk_len) {
+  const size_t NT = 1024, B = kBatch;  // largest workgroup bounds the static part
   const size_t lenp = (size_t)((chunk_len + 3) & ~3);
   const size_t dyn = (size_t)R * lenp * sizeof(float);
-  const size_t stat = kScoreNT * 4 + (kScoreNT + 1) * 4 + (size_t)kScoreNT * R * 4 +
-                      (kScoreNT / 64) * (4 + 8) + 64;
+  const size_t stat = B * 4 * 4 + (B + 1) * 4 + B * (size_t)R * 4 + (NT / 64) * 16 + 64;
   return dyn + stat;
 }
 
@@ -700,23 +804,32 @@ int score_max_rows(int32_t chunk_len, size_t lds_limit) {
   return 0;
 }
 
-template <int R>
-static hipError_t launch_score_r(const ScoreArgs &a, hipStream_t s) {
+template <int R, int NT, int U>
+static hipError_t launch_score_t(const ScoreArgs &a, hipStream_t s) {
   const int32_t lenp = (a.chunk_len + 3) & ~3;
-  const size_t dyn = (size_t)R * lenp * sizeof(float);
-  auto kern = score_kernel<R, kScoreNT>;
-  static bool attr_done = false;
-  if (!attr_done && dyn > 65536) {
+  const size_t dyn = (size_t)R * lenp * sizeof(int);
+  auto kern = score_kernel<R, NT, U>;
+  // dynamic LDS above 64 KiB needs an explicit opt-in per kernel
+  static size_t opted = 65536;
+  if (dyn > opted) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 163840);
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
     if (e != hipSuccess) return e;
-    attr_done = true;
+    opted = dyn;
   }
   const int vec4 = (a.ld % 4 == 0) && ((reinterpret_cast<uintptr_t>(a.out) & 15) == 0);
-  hipLaunchKernelGGL(kern, dim3((unsigned)a.n_groups), dim3(kScoreNT), dyn, s, a.grp_ptr,
-                     a.grp_dim, a.grp_val, a.q_inv, a.n_q, a.dim, a.col_ptr, a.row, a.val,
-                     a.chunk_base, a.chunk, a.chunk_len, lenp, a.out, a.ld, a.row_sums, vec4);
+  hipLaunchKernelGGL(kern, dim3((unsigned)a.n_groups), dim3(NT), dyn, s, a.grp_ptr, a.grp_dim,
+                     a.grp_val, a.n_q, a.dim, a.col_ptr, a.row, a.val, a.chunk_base,
+                     a.chunk, a.chunk_len, lenp, a.out, a.ld, a.row_sums, vec4);
   return hipGetLastError();
+}
+
+template <int R>
+static hipError_t launch_score_r(const ScoreArgs &a, hipStream_t s) {
+  const int nt = score_nt(), u = score_unroll();
+  if (nt == 1024) return u == 8 ? launch_score_t<R, 1024, 8>(a, s) : launch_score_t<R, 1024, 4>(a, s);
+  if (nt == 512) return u == 8 ? launch_score_t<R, 512, 8>(a, s) : launch_score_t<R, 512, 4>(a, s);
+  return u == 8 ? launch_score_t<R, 256, 8>(a, s) : launch_score_t<R, 256, 4>(a, s);
 }
 
 hipError_t launch_score(const ScoreArgs &a, hipStream_t s) {

@@ -29,8 +29,12 @@ def env():
 
 
 def report(name, err, n):
-    print("\n[parity] %-40s n=%-11d max|err|=%.3g (bar 1e-5; page goal 1e-6)" % (name, n, err),
-          file=sys.stderr, flush=True)
+    line = "[parity] %-44s n=%-11d max|err|=%.3g (bar 1e-5; page goal 1e-6)" % (name, n, err)
+    print("\n" + line, file=sys.stderr, flush=True)
+    path = os.environ.get("SPS_PARITY_LOG")
+    if path:
+        with open(path, "a") as f:
+            f.write(line + "\n")
 
 
 def gpu_chunks(env, q, items, chunk_size, rows=None, sums=False):
@@ -177,15 +181,15 @@ def _sampled(env, orc, name, n_rows_sampled, self_scores=False):
     worst_sum = float(np.abs(g_sums - ref_sums).max())
     # each row sum adds at most chunk_len fp32 errors of the scores
     report("%s %d sampled rows x all items" % (name, len(rows)), worst, n)
-    print("[parity] %s row sums of %d chunks x %d rows: max|err|=%.3g" %
-          (name, it.num_chunks, q.n_rows, worst_sum), file=sys.stderr, flush=True)
+    report("%s row sums, %d chunks x %d rows" % (name, it.num_chunks, q.n_rows), worst_sum,
+           it.num_chunks * q.n_rows)
     assert worst <= TOL
     assert worst_sum <= TOL * w.chunk_size
     if self_scores:
         empty = np.diff(q.indptr) == 0
         self_err = float(np.abs(self_vals[~empty] - 1.0).max())
-        print("[parity] %s self-scores of %d non-empty queries: max|S-1|=%.3g; %d empty -> 0" %
-              (name, int((~empty).sum()), self_err, int(empty.sum())), file=sys.stderr)
+        report("%s self-scores (%d empty rows -> 0)" % (name, int(empty.sum())), self_err,
+               int((~empty).sum()))
         assert self_err <= TOL
         assert np.all(self_vals[empty] == 0.0)
 
@@ -228,13 +232,15 @@ def test_edge_rows_and_ld(env, orc):
     import pins
     torch, sps, dev = env
     rng = np.random.default_rng(99)
+    from synth import HostCSR
     items = pins.random_csr(rng, 1003, 5000, 0, 30, signed=True, empty_frac=0.1,
                             explicit_zero_frac=0.05)
+    items = HostCSR(items.indptr, items.indices, items.values, items.n_rows, 5001)
     q = pins.random_csr(rng, 21, 5000, 0, 30, signed=True, empty_frac=0.2,
                         explicit_zero_frac=0.05)
-    # a query on a dim beyond every item's support
-    q = pins.csr_from_rows([list(zip(*q.row(r))) for r in range(q.n_rows)] + [[(4999, 1.0)]],
-                           5000)
+    # a last query on dim 5000, which no item holds
+    q = pins.csr_from_rows([list(zip(*q.row(r))) for r in range(q.n_rows)] + [[(5000, 1.0)]],
+                           5001)
     ref = orc.scores(q, items)
     it = sps.prepare(sps.CSR.from_host(items, dev), chunk_size=333)
     qq = sps.prepare_queries(sps.CSR.from_host(q, dev), it)
@@ -309,7 +315,8 @@ def test_validate_and_bad_input(env):
         (HostCSR(ok.indptr, np.array([5, 1, 0, 7], np.int32), ok.values, 3, 8), 0, 2),
         (HostCSR(ok.indptr, np.array([1, 5, 0, 9], np.int32), ok.values, 3, 8), 2, 3),
         (HostCSR(ok.indptr, ok.indices, np.array([1, 2, np.inf, 1], np.float32), 3, 8), 2, 4),
-        (HostCSR(np.array([0, 3, 2, 4], np.int32), ok.indices, ok.values, 3, 8), 1, 1),
+        (HostCSR(np.array([0, 3, 2, 4], np.int32), np.array([0, 1, 5, 7], np.int32),
+                 ok.values, 3, 8), 1, 1),
     ]
     for m, row, why in cases:
         assert sps.validate_csr(sps.CSR.from_host(m, dev)) == (False, row, why)
