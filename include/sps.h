@@ -15,7 +15,7 @@
  * against every row (the page is silent; this library's convention).
  *
  * How. Items are prepared once: their L2 norms (§5.2, from the stored
- * nonzeros only) and, for every chunk, inverted lists (a CSC of the chunk,
+ * nonzeros only) and, for every slice of a chunk, inverted lists (a CSC,
  * values pre-divided by the item norm). Queries are prepared once per batch.
  * Each chunk is then scored by one kernel launch that accumulates query
  * nonzero x posting-list products in on-chip (LDS) accumulators and writes
@@ -88,7 +88,7 @@ typedef struct sps_queries sps_queries;
 /* Byte sizes for sps_prepare. `persistent` holds the prepared corpus and
  * must outlive the handle; `scratch` is only used by sps_prepare itself and
  * may be reused once the prepare's stream work has completed.
- * chunk_size: items per chunk, 1..32768 (the page uses 8192, §3.3).
+ * chunk_size: items per chunk, 1..1048576 (the page uses 8192, §3.3).
  * Pure host arithmetic; no device access. */
 sps_status sps_items_workspace_size(int64_t n_items, int64_t dim, int64_t nnz,
                                     int32_t chunk_size, size_t *persistent_bytes,
@@ -97,12 +97,19 @@ sps_status sps_items_workspace_size(int64_t n_items, int64_t dim, int64_t nnz,
 /* Prepare an item corpus (asynchronous, stream-ordered):
  *  1. inverse norms inv[i] = fl32(1 / sqrt(sum v^2)) with the sum in float64
  *     over the stored nonzeros in index order (§5.2); 0 for a zero norm;
- *  2. chunk c covers items [c*chunk_size, min((c+1)*chunk_size, n_items)),
- *     the chunk's entries are indptr[first]..indptr[last+1] (§4.4 slicing);
- *  3. per chunk, the inverted lists: col_ptr[dim+1] (chunk-relative offsets,
- *     col_ptr[0] = 0, col_ptr[dim] = chunk nnz), and for every entry the
- *     chunk-local item id (uint16) and value fl32(v / ||item||) rounded once
- *     from float64 (0 if the item norm is 0). Item ids ascend within each dim.
+ *  2. chunk c covers items [c*chunk_size, min((c+1)*chunk_size, n_items))
+ *     (§4.4 slicing). Each chunk is cut into slices_per_chunk =
+ *     ceil(chunk_size / 2048) slices of slice_size = ceil(chunk_size /
+ *     slices_per_chunk) items (the last slice of a chunk may be shorter): a
+ *     slice is what one workgroup accumulates on chip;
+ *  3. per slice, the inverted lists: col_ptr[dim+1] (slice-relative offsets,
+ *     col_ptr[0] = 0, col_ptr[dim] = slice nnz), and for every entry the
+ *     slice-local item id (uint16) and value fl32(v / ||item||) rounded once
+ *     from float64 (0 if the item norm is 0). Item ids ascend within each dim;
+ *  4. when slices hold at least 512 items: the "heavy" dims (at most 32, the
+ *     most frequent among those held by at least 1/16 of the items) and, per
+ *     slice, their values as dense rows (0 where an item lacks the dim). This
+ *     is a speed device; results do not depend on it (SPS_DENSE=0 turns it off).
  * The item CSR may be released once this stream work has completed.
  * On success *out receives a new handle (free with sps_items_destroy). */
 sps_status sps_prepare(const sps_csr *items, int32_t chunk_size, void *persistent,
@@ -112,23 +119,34 @@ sps_status sps_prepare(const sps_csr *items, int32_t chunk_size, void *persisten
 sps_status sps_items_info(const sps_items *h, int64_t *n_items, int64_t *dim, int64_t *nnz,
                           int32_t *chunk_size, int32_t *num_chunks);
 
-/* Device views of one prepared chunk (for parity tests and tooling).
- * SYNCHRONOUS: reads the chunk's entry range back from the device after
+/* Slice geometry (see sps_prepare step 2). Slice s of the corpus is slice
+ * s % slices_per_chunk of chunk s / slices_per_chunk. Pure host. */
+sps_status sps_items_slices(const sps_items *h, int32_t *slice_size, int32_t *slices_per_chunk,
+                            int64_t *num_slices);
+
+/* Device views of one prepared slice (for parity tests and tooling).
+ * SYNCHRONOUS: reads the slice's entry range back from the device after
  * synchronising `stream`. col_ptr: DEVICE int32[dim+1]; row: DEVICE
- * uint16[chunk_nnz]; val: DEVICE float[chunk_nnz]; item_inv_norm: DEVICE
- * float[chunk_len] (the chunk's first item onwards). */
+ * uint16[slice_nnz]; val: DEVICE float[slice_nnz]; item_inv_norm: DEVICE
+ * float[slice_len] (the slice's first item onwards). */
 typedef struct {
   int64_t item_begin;
-  int32_t chunk_len;
-  int32_t chunk_nnz;
+  int32_t slice_len;
+  int32_t slice_nnz;
   const int32_t *col_ptr;
   const uint16_t *row;
   const float *val;
   const float *item_inv_norm;
-} sps_chunk_view;
+} sps_slice_view;
 
-sps_status sps_items_chunk_view(const sps_items *h, int32_t chunk, void *stream,
-                                sps_chunk_view *view);
+sps_status sps_items_slice_view(const sps_items *h, int64_t slice, void *stream,
+                                sps_slice_view *view);
+
+/* The heavy dims chosen by sps_prepare, ascending (SYNCHRONOUS). Writes at
+ * most `capacity` dims to `dims` (nullable) and their number to *count
+ * (0 when the dense rows are off). */
+sps_status sps_items_heavy_dims(const sps_items *h, void *stream, int32_t *dims,
+                                int32_t capacity, int32_t *count);
 
 void sps_items_destroy(sps_items *h);
 
@@ -142,12 +160,13 @@ void sps_items_destroy(sps_items *h);
 sps_status sps_queries_workspace_size(const sps_items *items, int64_t n_rows, int64_t dim,
                                       int64_t nnz, size_t *bytes);
 
-/* Prepare a query batch (asynchronous): inverse norms as for items (§5.2)
- * and, for every group of consecutive rows scored by one workgroup, the
- * union of the rows' dims in ascending order with each row's value (0 where
- * a row lacks the dim), so that a posting list shared by several rows of a
- * group is read once. The query CSR may be released once this stream work
- * has completed. Free the handle with sps_queries_destroy. */
+/* Prepare a query batch for the prepared items `items` (asynchronous):
+ * inverse norms as for items (§5.2); every row normalised by its float64
+ * norm and rounded once to fp32, fl32(q_d / ||q||); values on the items'
+ * heavy dims gathered into dense blocks of 16 rows, the rest kept as a CSR of
+ * "light" entries. The query CSR may be released once this stream work has
+ * completed. The batch can only be scored against `items`. Free the handle
+ * with sps_queries_destroy. */
 sps_status sps_prepare_queries(const sps_csr *queries, const sps_items *items,
                                void *workspace, size_t workspace_bytes, void *stream,
                                sps_queries **out);
@@ -164,14 +183,15 @@ void sps_queries_destroy(sps_queries *q);
 /* Score chunk `chunk` (asynchronous): for every query row q and every item
  * j < chunk_len of the chunk,
  *     out[q * ld_out + j] = S[q, item_begin + j]          (float32)
- * computed as (sum over the query's nonzeros d of q_d * itemval_d) * inv_q,
- * with item values pre-divided by the item norm (division after the dot,
- * §4.4, up to fp32 rounding). Columns chunk_len <= j < ld_out are not
- * touched. out: DEVICE, n_rows * ld_out floats, ld_out >= chunk_len.
- * row_sums (nullable): DEVICE double[n_rows]; row_sums[q] = the float64 sum
- * of the float32 scores written for row q (a per-chunk checksum).
- * No clamping to [-1, 1] is applied. Results may differ between runs in the
- * last bits (order of float additions into on-chip accumulators). */
+ * computed as sum over the shared dims of fl32(q_d/|q|) * fl32(i_d/|i|)
+ * (both rows normalised before the dot; the page divides after it, §4.4 --
+ * equal up to rounding). The light dims are summed exactly in 32-bit fixed
+ * point (2^-30) after rounding each fp32 product; the heavy dims in fp32 on
+ * the matrix cores, then added. Columns chunk_len <= j < ld_out are not
+ * touched. out: DEVICE, n_rows * ld_out floats, ld_out >= min(chunk_size,
+ * n_items). row_sums (nullable): DEVICE double[n_rows]; row_sums[q] = the
+ * float64 sum of the float32 scores written for row q (a per-chunk checksum).
+ * No clamping to [-1, 1] is applied. Results are bitwise reproducible. */
 sps_status sps_cosine_chunk(const sps_queries *q, const sps_items *items, int32_t chunk,
                             float *out, int64_t ld_out, double *row_sums, void *stream);
 

@@ -48,9 +48,9 @@ class _Csr(ctypes.Structure):
                 ("values", ctypes.c_void_p)]
 
 
-class _ChunkView(ctypes.Structure):
-    _fields_ = [("item_begin", ctypes.c_int64), ("chunk_len", ctypes.c_int32),
-                ("chunk_nnz", ctypes.c_int32), ("col_ptr", ctypes.c_void_p),
+class _SliceView(ctypes.Structure):
+    _fields_ = [("item_begin", ctypes.c_int64), ("slice_len", ctypes.c_int32),
+                ("slice_nnz", ctypes.c_int32), ("col_ptr", ctypes.c_void_p),
                 ("row", ctypes.c_void_p), ("val", ctypes.c_void_p),
                 ("item_inv_norm", ctypes.c_void_p)]
 
@@ -68,7 +68,10 @@ SIGNATURES = {
                            ctypes.POINTER(_P)]),
     "sps_items_info": (_I32, [_P, ctypes.POINTER(_I64), ctypes.POINTER(_I64),
                               ctypes.POINTER(_I64), ctypes.POINTER(_I32), ctypes.POINTER(_I32)]),
-    "sps_items_chunk_view": (_I32, [_P, _I32, _P, ctypes.POINTER(_ChunkView)]),
+    "sps_items_slices": (_I32, [_P, ctypes.POINTER(_I32), ctypes.POINTER(_I32),
+                                ctypes.POINTER(_I64)]),
+    "sps_items_slice_view": (_I32, [_P, _I64, _P, ctypes.POINTER(_SliceView)]),
+    "sps_items_heavy_dims": (_I32, [_P, _P, _P, _I32, ctypes.POINTER(_I32)]),
     "sps_items_destroy": (None, [_P]),
     "sps_queries_workspace_size": (_I32, [_P, _I64, _I64, _I64, ctypes.POINTER(_SZ)]),
     "sps_prepare_queries": (_I32, [ctypes.POINTER(_Csr), _P, _P, _SZ, _P, ctypes.POINTER(_P)]),
@@ -176,6 +179,9 @@ class Items:
                                    ctypes.byref(cs), ctypes.byref(nc)))
         self.n_items, self.dim, self.nnz = n.value, d.value, z.value
         self.chunk_size, self.num_chunks = cs.value, nc.value
+        ss, spc, ns = _I32(), _I32(), _I64()
+        _check(_lib.sps_items_slices(handle, ctypes.byref(ss), ctypes.byref(spc), ctypes.byref(ns)))
+        self.slice_size, self.slices_per_chunk, self.num_slices = ss.value, spc.value, ns.value
 
     def chunk_len(self, c: int) -> int:
         b = c * self.chunk_size
@@ -187,10 +193,10 @@ class Items:
         self._src = None
         self._scratch = None
 
-    def chunk_view(self, c: int, stream=None) -> dict:
-        """Device views of chunk c's inverted lists (synchronous)."""
-        v = _ChunkView()
-        _check(_lib.sps_items_chunk_view(self._h, c, _stream_ptr(stream), ctypes.byref(v)))
+    def slice_view(self, s: int, stream=None) -> dict:
+        """Device views of slice s's inverted lists (synchronous)."""
+        v = _SliceView()
+        _check(_lib.sps_items_slice_view(self._h, s, _stream_ptr(stream), ctypes.byref(v)))
         dev = self._persistent.device
 
         def view(ptr, n, dtype, elem):
@@ -202,12 +208,19 @@ class Items:
             return self._persistent[off:off + n * elem].view(dtype)
 
         return {
-            "item_begin": v.item_begin, "chunk_len": v.chunk_len, "chunk_nnz": v.chunk_nnz,
+            "item_begin": v.item_begin, "slice_len": v.slice_len, "slice_nnz": v.slice_nnz,
             "col_ptr": view(v.col_ptr, self.dim + 1, torch.int32, 4),
-            "row": view(v.row, v.chunk_nnz, torch.int16, 2),
-            "val": view(v.val, v.chunk_nnz, torch.float32, 4),
-            "item_inv_norm": view(v.item_inv_norm, v.chunk_len, torch.float32, 4),
+            "row": view(v.row, v.slice_nnz, torch.int16, 2),
+            "val": view(v.val, v.slice_nnz, torch.float32, 4),
+            "item_inv_norm": view(v.item_inv_norm, v.slice_len, torch.float32, 4),
         }
+
+    def heavy_dims(self, stream=None) -> list:
+        """The dims kept as dense rows (ascending; synchronous)."""
+        buf = (_I32 * 64)()
+        n = _I32()
+        _check(_lib.sps_items_heavy_dims(self._h, _stream_ptr(stream), buf, 64, ctypes.byref(n)))
+        return [int(buf[i]) for i in range(n.value)]
 
     def __del__(self):
         h, self._h = getattr(self, "_h", None), None

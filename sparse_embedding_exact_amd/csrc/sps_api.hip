@@ -1,6 +1,6 @@
 // sps_api.hip -- the C ABI of include/sps.h: argument checks, workspace
 // layout, handles and stream-ordered launches. Host code only; the kernels
-// live in sps_kernels.hip.
+// live in sps_prepare.hip and sps_score.hip.
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
@@ -30,7 +30,7 @@ sps_status hip_fail(hipError_t e, const char *where) {
 
 constexpr int64_t kI32Max = 2147483647ll;
 constexpr size_t kAlign = 256;
-constexpr int32_t kMaxChunk = 32768;
+constexpr int32_t kMaxChunk = 1 << 20;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 
@@ -64,107 +64,11 @@ sps_status check_csr_shape(const sps_csr *m, const char *what) {
   return SPS_OK;
 }
 
-// LDS per workgroup on gfx950 (CDNA4): 160 KiB. When a device is present
-// its opt-in limit is used if smaller.
-constexpr size_t kLdsLimit = 163840;
-
-size_t lds_limit() {
-  static size_t cached = 0;
-  if (cached) return cached;
-  size_t lim = kLdsLimit;
-  int dev = 0, v = 0;
-  if (hipGetDevice(&dev) == hipSuccess &&
-      hipDeviceGetAttribute(&v, hipDeviceAttributeSharedMemPerBlockOptin, dev) == hipSuccess &&
-      v > 0 && (size_t)v < lim)
-    lim = (size_t)v;
-  cached = lim;
-  return lim;
-}
-
-// Rows per score workgroup. SPS_SCORE_ROWS (1, 2, 4 or 8) overrides the
-// default when the chunk fits.
-int pick_rows(int32_t chunk_len, size_t lds_limit) {
-  const int maxr = sps::score_max_rows(chunk_len, lds_limit);
-  if (maxr == 0) return 0;
-  int r = 1;
-  if (const char *env = getenv("SPS_SCORE_ROWS")) {
-    const int v = atoi(env);
-    if ((v == 1 || v == 2 || v == 4 || v == 8) && v <= maxr) r = v;
-  }
-  return r;
-}
-
-}  // namespace
-
-struct sps_items {
-  int64_t n_items, dim, nnz;
-  int32_t chunk_size, num_chunks;
-  int device;
-  float *inv_norm;
-  int32_t *col_ptr;
-  uint16_t *row;
-  float *val;
-  int32_t *chunk_base;
-};
-
-struct sps_queries {
-  int64_t n_rows, dim, nnz;
-  int32_t R, n_groups, chunk_size;
-  int device;
-  float *inv_norm;
-  int32_t *grp_ptr, *grp_dim;
-  float *grp_val;
-};
-
-namespace {
-
-struct ItemsLayout {
-  size_t inv, colp, row, val, cbase, persistent;
-  size_t flags, norm64, ticket, trow, tval, mlist, mcount, scratch;
-  bool overflow;
-};
-
-ItemsLayout items_layout(int64_t n, int64_t dim, int64_t nnz, int32_t C) {
-  const int64_t nch = (n + C - 1) / C;
-  ItemsLayout L{};
-  Layout p;
-  L.inv = p.add(n, 4);
-  L.colp = p.add((uint64_t)nch * (uint64_t)(dim + 1), 4);
-  L.row = p.add(nnz, 2);
-  L.val = p.add(nnz, 4);
-  L.cbase = p.add(nch + 1, 4);
-  L.persistent = p.off;
-  Layout s;
-  L.flags = s.add(sps::kFlagsInts, 4);
-  L.norm64 = s.add(n, 8);
-  L.ticket = s.add(nnz, 4);
-  L.trow = s.add(nnz, 2);
-  L.tval = s.add(nnz, 4);
-  L.mlist = s.add(nnz / 2 + nch + 1, 4);
-  L.mcount = s.add(nch, 4);
-  L.scratch = s.off;
-  L.overflow = p.overflow || s.overflow;
-  return L;
-}
-
-struct QueriesLayout {
-  size_t flags, inv, norm64, gptr, gdim, gval, total;
-  bool overflow;
-};
-
-QueriesLayout queries_layout(int64_t n, int64_t nnz, int R) {
-  const int64_t ng = (n + R - 1) / R;
-  QueriesLayout L{};
-  Layout p;
-  L.flags = p.add(sps::kFlagsInts, 4);
-  L.inv = p.add(n, 4);
-  L.norm64 = p.add(n, 8);
-  L.gptr = p.add(ng + 1, 4);
-  L.gdim = p.add(nnz, 4);
-  L.gval = p.add((uint64_t)nnz * (uint64_t)R, 4);
-  L.total = p.off;
-  L.overflow = p.overflow;
-  return L;
+// The heavy-dim dense path is on for slices it supports unless SPS_DENSE=0.
+bool dense_wanted(const sps::Geom &g) {
+  if (!sps::dense_slice_ok(g.S)) return false;
+  if (const char *env = getenv("SPS_DENSE")) return atoi(env) != 0;
+  return true;
 }
 
 template <typename T>
@@ -172,7 +76,91 @@ T *at(void *base, size_t off) {
   return reinterpret_cast<T *>(reinterpret_cast<char *>(base) + off);
 }
 
+struct ItemsLayout {
+  size_t inv, colp, row, val, sbase, heavy, slab, persistent;
+  size_t flags, norm64, ticket, trow, tval, mlist, mcount, gdf, scratch;
+  bool overflow;
+};
+
+ItemsLayout items_layout(const sps::Geom &g, int64_t dim, int64_t nnz, bool dense) {
+  const int64_t ns = g.num_slices();
+  ItemsLayout L{};
+  Layout p;
+  L.inv = p.add(g.n_items, 4);
+  L.colp = p.add((uint64_t)ns * (uint64_t)(dim + 1), 4);
+  L.row = p.add(nnz, 2);
+  L.val = p.add(nnz, 4);
+  L.sbase = p.add(ns + 1, 4);
+  L.heavy = p.add(sps::kHeavyMax + 1, 4);
+  L.slab = p.add(dense ? (uint64_t)ns * sps::kHeavyMax * (uint64_t)sps::slab_pitch(g.S) : 0, 4);
+  L.persistent = p.off;
+  Layout s;
+  L.flags = s.add(sps::kFlagsInts, 4);
+  L.norm64 = s.add(g.n_items, 8);
+  L.ticket = s.add(nnz, 4);
+  L.trow = s.add(nnz, 2);
+  L.tval = s.add(nnz, 4);
+  L.mlist = s.add(nnz / 2 + ns + 1, 4);
+  L.mcount = s.add(ns, 4);
+  L.gdf = s.add(dense ? (uint64_t)dim : 0, 4);
+  L.scratch = s.off;
+  L.overflow = p.overflow || s.overflow;
+  return L;
+}
+
+struct QueriesLayout {
+  size_t flags, inv, norm64, lptr, ldim, lval, lrow, qh, rspart, total;
+  bool overflow;
+};
+
+QueriesLayout queries_layout(int64_t n, int64_t nnz, int32_t n_sub, bool dense) {
+  const int64_t ng = (n + sps::kRows - 1) / sps::kRows;
+  QueriesLayout L{};
+  Layout p;
+  L.flags = p.add(sps::kFlagsInts, 4);
+  L.inv = p.add(n, 4);
+  L.norm64 = p.add(n, 8);
+  L.lptr = p.add(n + 1, 4);
+  L.ldim = p.add(nnz, 4);
+  L.lval = p.add(nnz, 4);
+  L.lrow = p.add(nnz, 1);
+  L.qh = p.add(dense ? (uint64_t)ng * sps::kHeavyMax * sps::kRows : 0, 4);
+  L.rspart = p.add(n_sub > 1 ? (uint64_t)n_sub * (uint64_t)n : 0, 8);
+  L.total = p.off;
+  L.overflow = p.overflow;
+  return L;
+}
+
 }  // namespace
+
+struct sps_items {
+  sps::Geom g;
+  int64_t dim, nnz;
+  int device;
+  bool dense;
+  int32_t pitch;  // slab row pitch (items), dense only
+  float *inv_norm;
+  int32_t *col_ptr;
+  uint16_t *row;
+  float *val;
+  int32_t *slice_base;
+  int32_t *heavy;
+  float *slab;
+};
+
+struct sps_queries {
+  int64_t n_rows, dim, nnz;
+  int32_t n_groups;
+  int device;
+  bool dense;
+  const sps_items *items;  // the corpus the queries were prepared for
+  float *inv_norm;
+  int32_t *lptr, *ldim;
+  float *lval;
+  uint8_t *lrow;
+  float *qh;
+  double *rs_part;
+};
 
 extern "C" {
 
@@ -204,7 +192,10 @@ sps_status sps_items_workspace_size(int64_t n_items, int64_t dim, int64_t nnz,
     return fail(SPS_ERR_INVALID_ARGUMENT, "chunk_size must be in [1, %d]", kMaxChunk);
   if (n_items >= kI32Max || dim >= kI32Max || nnz >= kI32Max)
     return fail(SPS_ERR_OVERFLOW, "sizes must be below 2^31");
-  const ItemsLayout L = items_layout(n_items, dim, nnz, chunk_size);
+  if (nnz >= (1ll << 30))
+    return fail(SPS_ERR_OVERFLOW, "item nnz must be below 2^30 (32-bit byte offsets)");
+  const sps::Geom g = sps::make_geom(n_items, chunk_size);
+  const ItemsLayout L = items_layout(g, dim, nnz, dense_wanted(g));
   if (L.overflow) return fail(SPS_ERR_OVERFLOW, "workspace byte count overflows");
   *persistent_bytes = L.persistent;
   *scratch_bytes = L.scratch;
@@ -232,13 +223,14 @@ sps_status sps_prepare(const sps_csr *items, int32_t chunk_size, void *persisten
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return fail(SPS_ERR_HIP, "no HIP device");
 
-  const ItemsLayout L = items_layout(items->n_rows, items->n_cols, items->nnz, chunk_size);
+  const sps::Geom g = sps::make_geom(items->n_rows, chunk_size);
+  const bool dense = dense_wanted(g);
+  const ItemsLayout L = items_layout(g, items->n_cols, items->nnz, dense);
   sps::ItemsDev d{};
-  d.n_items = items->n_rows;
+  d.g = g;
   d.dim = items->n_cols;
   d.nnz = items->nnz;
-  d.chunk_size = chunk_size;
-  d.num_chunks = (int32_t)((items->n_rows + chunk_size - 1) / chunk_size);
+  d.dense = dense;
   d.indptr = items->indptr;
   d.indices = items->indices;
   d.values = items->values;
@@ -246,7 +238,9 @@ sps_status sps_prepare(const sps_csr *items, int32_t chunk_size, void *persisten
   d.col_ptr = at<int32_t>(persistent, L.colp);
   d.row = at<uint16_t>(persistent, L.row);
   d.val = at<float>(persistent, L.val);
-  d.chunk_base = at<int32_t>(persistent, L.cbase);
+  d.slice_base = at<int32_t>(persistent, L.sbase);
+  d.heavy = at<int32_t>(persistent, L.heavy);
+  d.slab = dense ? at<float>(persistent, L.slab) : nullptr;
   d.flags = at<int32_t>(scratch, L.flags);
   d.norm64 = at<double>(scratch, L.norm64);
   d.ticket = at<int32_t>(scratch, L.ticket);
@@ -254,6 +248,7 @@ sps_status sps_prepare(const sps_csr *items, int32_t chunk_size, void *persisten
   d.tval = at<float>(scratch, L.tval);
   d.mlist = at<int32_t>(scratch, L.mlist);
   d.mcount = at<int32_t>(scratch, L.mcount);
+  d.gdf = dense ? at<int32_t>(scratch, L.gdf) : nullptr;
 
   sps_items *h = new (std::nothrow) sps_items;
   if (!h) return fail(SPS_ERR_INVALID_ARGUMENT, "out of host memory");
@@ -262,17 +257,19 @@ sps_status sps_prepare(const sps_csr *items, int32_t chunk_size, void *persisten
     delete h;
     return hip_fail(e, "sps_prepare");
   }
-  h->n_items = d.n_items;
+  h->g = g;
   h->dim = d.dim;
   h->nnz = d.nnz;
-  h->chunk_size = chunk_size;
-  h->num_chunks = d.num_chunks;
   h->device = dev;
+  h->dense = dense;
+  h->pitch = dense ? sps::slab_pitch(g.S) : 0;
   h->inv_norm = d.inv_norm;
   h->col_ptr = d.col_ptr;
   h->row = d.row;
   h->val = d.val;
-  h->chunk_base = d.chunk_base;
+  h->slice_base = d.slice_base;
+  h->heavy = d.heavy;
+  h->slab = d.slab;
   *out = h;
   return SPS_OK;
 }
@@ -280,37 +277,56 @@ sps_status sps_prepare(const sps_csr *items, int32_t chunk_size, void *persisten
 sps_status sps_items_info(const sps_items *h, int64_t *n_items, int64_t *dim, int64_t *nnz,
                           int32_t *chunk_size, int32_t *num_chunks) {
   if (!h) return fail(SPS_ERR_INVALID_ARGUMENT, "NULL handle");
-  if (n_items) *n_items = h->n_items;
+  if (n_items) *n_items = h->g.n_items;
   if (dim) *dim = h->dim;
   if (nnz) *nnz = h->nnz;
-  if (chunk_size) *chunk_size = h->chunk_size;
-  if (num_chunks) *num_chunks = h->num_chunks;
+  if (chunk_size) *chunk_size = h->g.C;
+  if (num_chunks) *num_chunks = h->g.num_chunks;
   return SPS_OK;
 }
 
-static int32_t chunk_len_of(const sps_items *h, int32_t c) {
-  const int64_t b = (int64_t)c * h->chunk_size;
-  const int64_t e = b + h->chunk_size < h->n_items ? b + h->chunk_size : h->n_items;
-  return (int32_t)(e - b);
+sps_status sps_items_slices(const sps_items *h, int32_t *slice_size, int32_t *slices_per_chunk,
+                            int64_t *num_slices) {
+  if (!h) return fail(SPS_ERR_INVALID_ARGUMENT, "NULL handle");
+  if (slice_size) *slice_size = h->g.S;
+  if (slices_per_chunk) *slices_per_chunk = h->g.n_sub;
+  if (num_slices) *num_slices = h->g.num_slices();
+  return SPS_OK;
 }
 
-sps_status sps_items_chunk_view(const sps_items *h, int32_t chunk, void *stream,
-                                sps_chunk_view *view) {
+sps_status sps_items_slice_view(const sps_items *h, int64_t slice, void *stream,
+                                sps_slice_view *view) {
   if (!h || !view) return fail(SPS_ERR_INVALID_ARGUMENT, "NULL handle or view");
-  if (chunk < 0 || chunk >= h->num_chunks)
-    return fail(SPS_ERR_CHUNK_RANGE, "chunk %d outside [0, %d)", chunk, h->num_chunks);
+  if (slice < 0 || slice >= h->g.num_slices())
+    return fail(SPS_ERR_CHUNK_RANGE, "slice %lld outside [0, %lld)", (long long)slice,
+                (long long)h->g.num_slices());
   hipError_t e = hipStreamSynchronize(reinterpret_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "sps_items_chunk_view");
+  if (e != hipSuccess) return hip_fail(e, "sps_items_slice_view");
   int32_t be[2];
-  e = hipMemcpy(be, h->chunk_base + chunk, sizeof be, hipMemcpyDeviceToHost);
-  if (e != hipSuccess) return hip_fail(e, "sps_items_chunk_view");
-  view->item_begin = (int64_t)chunk * h->chunk_size;
-  view->chunk_len = chunk_len_of(h, chunk);
-  view->chunk_nnz = be[1] - be[0];
-  view->col_ptr = h->col_ptr + (int64_t)chunk * (h->dim + 1);
+  e = hipMemcpy(be, h->slice_base + slice, sizeof be, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "sps_items_slice_view");
+  view->item_begin = h->g.slice_begin(slice);
+  view->slice_len = (int32_t)(h->g.slice_end(slice) - view->item_begin);
+  view->slice_nnz = be[1] - be[0];
+  view->col_ptr = h->col_ptr + slice * (h->dim + 1);
   view->row = h->row + be[0];
   view->val = h->val + be[0];
   view->item_inv_norm = h->inv_norm + view->item_begin;
+  return SPS_OK;
+}
+
+sps_status sps_items_heavy_dims(const sps_items *h, void *stream, int32_t *dims,
+                                int32_t capacity, int32_t *count) {
+  if (!h || !count) return fail(SPS_ERR_INVALID_ARGUMENT, "NULL argument");
+  hipError_t e = hipStreamSynchronize(reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "sps_items_heavy_dims");
+  int32_t buf[sps::kHeavyMax + 1];
+  e = hipMemcpy(buf, h->heavy, sizeof buf, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "sps_items_heavy_dims");
+  const int32_t m = h->dense ? buf[sps::kHeavyMax] : 0;
+  *count = m;
+  if (dims)
+    for (int32_t i = 0; i < m && i < capacity; ++i) dims[i] = buf[i];
   return SPS_OK;
 }
 
@@ -326,11 +342,8 @@ sps_status sps_queries_workspace_size(const sps_items *items, int64_t n_rows, in
   if (dim != items->dim)
     return fail(SPS_ERR_DIM_MISMATCH, "query dim %lld != item dim %lld", (long long)dim,
                 (long long)items->dim);
-  const int R = pick_rows(items->chunk_size, lds_limit());
-  if (R == 0) return fail(SPS_ERR_UNSUPPORTED, "chunk of %d items exceeds LDS", items->chunk_size);
-  const QueriesLayout L = queries_layout(n_rows, nnz, R);
-  if (L.overflow || (uint64_t)nnz * (uint64_t)R >= (uint64_t)kI32Max * 8)
-    return fail(SPS_ERR_OVERFLOW, "workspace byte count overflows");
+  const QueriesLayout L = queries_layout(n_rows, nnz, items->g.n_sub, items->dense);
+  if (L.overflow) return fail(SPS_ERR_OVERFLOW, "workspace byte count overflows");
   *bytes = L.total;
   return SPS_OK;
 }
@@ -352,23 +365,26 @@ sps_status sps_prepare_queries(const sps_csr *queries, const sps_items *items, v
     return fail(SPS_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return fail(SPS_ERR_HIP, "no HIP device");
-  const int R = pick_rows(items->chunk_size, lds_limit());
-  const QueriesLayout L = queries_layout(queries->n_rows, queries->nnz, R);
+  const bool dense = items->dense;
+  const QueriesLayout L = queries_layout(queries->n_rows, queries->nnz, items->g.n_sub, dense);
   sps::QueriesDev d{};
   d.n_rows = queries->n_rows;
   d.dim = queries->n_cols;
   d.nnz = queries->nnz;
-  d.R = R;
-  d.n_groups = (int32_t)((queries->n_rows + R - 1) / R);
+  d.n_groups = (int32_t)((queries->n_rows + sps::kRows - 1) / sps::kRows);
+  d.dense = dense;
   d.indptr = queries->indptr;
   d.indices = queries->indices;
   d.values = queries->values;
+  d.heavy = items->heavy;
   d.flags = at<int32_t>(workspace, L.flags);
   d.inv_norm = at<float>(workspace, L.inv);
   d.norm64 = at<double>(workspace, L.norm64);
-  d.grp_ptr = at<int32_t>(workspace, L.gptr);
-  d.grp_dim = at<int32_t>(workspace, L.gdim);
-  d.grp_val = at<float>(workspace, L.gval);
+  d.lptr = at<int32_t>(workspace, L.lptr);
+  d.ldim = at<int32_t>(workspace, L.ldim);
+  d.lval = at<float>(workspace, L.lval);
+  d.lrow = at<uint8_t>(workspace, L.lrow);
+  d.qh = dense ? at<float>(workspace, L.qh) : nullptr;
   sps_queries *h = new (std::nothrow) sps_queries;
   if (!h) return fail(SPS_ERR_INVALID_ARGUMENT, "out of host memory");
   hipError_t e = sps::launch_prepare_queries(d, reinterpret_cast<hipStream_t>(stream));
@@ -379,14 +395,17 @@ sps_status sps_prepare_queries(const sps_csr *queries, const sps_items *items, v
   h->n_rows = d.n_rows;
   h->dim = d.dim;
   h->nnz = d.nnz;
-  h->R = R;
   h->n_groups = d.n_groups;
-  h->chunk_size = items->chunk_size;
   h->device = dev;
+  h->dense = dense;
+  h->items = items;
   h->inv_norm = d.inv_norm;
-  h->grp_ptr = d.grp_ptr;
-  h->grp_dim = d.grp_dim;
-  h->grp_val = d.grp_val;
+  h->lptr = d.lptr;
+  h->ldim = d.ldim;
+  h->lval = d.lval;
+  h->lrow = d.lrow;
+  h->qh = d.qh;
+  h->rs_part = items->g.n_sub > 1 ? at<double>(workspace, L.rspart) : nullptr;
   *out = h;
   return SPS_OK;
 }
@@ -402,13 +421,13 @@ void sps_queries_destroy(sps_queries *q) { delete q; }
 static sps_status check_score_args(const sps_queries *q, const sps_items *items, float *out,
                                    int64_t ld_out) {
   if (!q || !items) return fail(SPS_ERR_INVALID_ARGUMENT, "NULL handle");
-  if (q->dim != items->dim) return fail(SPS_ERR_DIM_MISMATCH, "query/item dims differ");
-  if (q->chunk_size != items->chunk_size)
-    return fail(SPS_ERR_INVALID_ARGUMENT, "queries were prepared for another chunk size");
+  if (q->items != items)
+    return fail(SPS_ERR_INVALID_ARGUMENT, "queries were prepared for another item corpus");
   if (q->n_rows > 0 && !out) return fail(SPS_ERR_INVALID_ARGUMENT, "NULL output");
-  if (ld_out < items->chunk_size && ld_out < items->n_items)
-    return fail(SPS_ERR_INVALID_ARGUMENT, "ld_out %lld below the chunk length",
-                (long long)ld_out);
+  const int64_t width = items->g.C < items->g.n_items ? items->g.C : items->g.n_items;
+  if (ld_out < width)
+    return fail(SPS_ERR_INVALID_ARGUMENT, "ld_out %lld below the chunk length %lld",
+                (long long)ld_out, (long long)width);
   if (q->n_rows > 0 && (uint64_t)ld_out > (uint64_t)INT64_MAX / 4 / (uint64_t)q->n_rows)
     return fail(SPS_ERR_OVERFLOW, "n_rows * ld_out overflows");
   return SPS_OK;
@@ -416,25 +435,28 @@ static sps_status check_score_args(const sps_queries *q, const sps_items *items,
 
 static sps_status score_one(const sps_queries *q, const sps_items *items, int32_t chunk,
                             float *out, int64_t ld_out, double *row_sums, hipStream_t s) {
-  const int32_t len = chunk_len_of(items, chunk);
-  if (ld_out < len) return fail(SPS_ERR_INVALID_ARGUMENT, "ld_out below the chunk length");
   sps::ScoreArgs a{};
-  a.grp_ptr = q->grp_ptr;
-  a.grp_dim = q->grp_dim;
-  a.grp_val = q->grp_val;
-  a.q_inv = q->inv_norm;
+  a.g = items->g;
+  a.dim = items->dim;
   a.n_q = q->n_rows;
-  a.dim = q->dim;
-  a.R = q->R;
   a.n_groups = q->n_groups;
-  a.col_ptr = items->col_ptr + (int64_t)chunk * (items->dim + 1);
+  a.chunk = chunk;
+  a.dense = q->dense && items->dense;
+  a.lptr = q->lptr;
+  a.ldim = q->ldim;
+  a.lval = q->lval;
+  a.lrow = q->lrow;
+  a.qh = q->qh;
+  a.col_ptr = items->col_ptr;
   a.row = items->row;
   a.val = items->val;
-  a.chunk_base = items->chunk_base;
-  a.chunk = chunk;
-  a.chunk_len = len;
+  a.slice_base = items->slice_base;
+  a.heavy = items->heavy;
+  a.slab = items->slab;
+  a.pitch = items->pitch;
   a.out = out;
   a.ld = ld_out;
+  a.rs_part = q->rs_part;
   a.row_sums = row_sums;
   const hipError_t e = sps::launch_score(a, s);
   if (e != hipSuccess) return hip_fail(e, "score kernel");
@@ -445,8 +467,8 @@ sps_status sps_cosine_chunk(const sps_queries *q, const sps_items *items, int32_
                             float *out, int64_t ld_out, double *row_sums, void *stream) {
   sps_status st = check_score_args(q, items, out, ld_out);
   if (st != SPS_OK) return st;
-  if (chunk < 0 || chunk >= items->num_chunks)
-    return fail(SPS_ERR_CHUNK_RANGE, "chunk %d outside [0, %d)", chunk, items->num_chunks);
+  if (chunk < 0 || chunk >= items->g.num_chunks)
+    return fail(SPS_ERR_CHUNK_RANGE, "chunk %d outside [0, %d)", chunk, items->g.num_chunks);
   return score_one(q, items, chunk, out, ld_out, row_sums, reinterpret_cast<hipStream_t>(stream));
 }
 
@@ -455,9 +477,9 @@ sps_status sps_cosine_stream(const sps_queries *q, const sps_items *items, int32
                              void *stream) {
   sps_status st = check_score_args(q, items, out, ld_out);
   if (st != SPS_OK) return st;
-  if (chunk_begin < 0 || chunk_end > items->num_chunks || chunk_begin > chunk_end)
+  if (chunk_begin < 0 || chunk_end > items->g.num_chunks || chunk_begin > chunk_end)
     return fail(SPS_ERR_CHUNK_RANGE, "chunk range [%d, %d) outside [0, %d)", chunk_begin,
-                chunk_end, items->num_chunks);
+                chunk_end, items->g.num_chunks);
   for (int32_t c = chunk_begin; c < chunk_end; ++c) {
     double *rs = row_sums ? row_sums + (int64_t)(c - chunk_begin) * q->n_rows : nullptr;
     st = score_one(q, items, c, out, ld_out, rs, reinterpret_cast<hipStream_t>(stream));

@@ -1,4 +1,5 @@
-// sps_internal.h -- launchers shared by the C-ABI layer and the kernel file.
+// sps_internal.h -- constants, geometry and launchers shared by the C-ABI
+// layer (sps_api.hip) and the kernel files (sps_prepare.hip, sps_score.hip).
 // Not part of the public interface (include/sps.h is).
 #pragma once
 
@@ -9,8 +10,67 @@ namespace sps {
 
 // flags block (device, 16 int32): [0] structural fault bits (1 indptr,
 // 4 index range), [1] other fault bits (2 order/duplicate, 8 non-finite),
-// [2..3] uint64 min key (row << 3 | reason) of the first faulty row.
+// [2..3] uint64 min key (row << 3 | reason code) of the first faulty row.
 constexpr int kFlagsInts = 16;
+
+// Query rows per score workgroup and the widest item slice one workgroup
+// accumulates on chip: 16 rows x 2048 items x 4 B = 128 KiB of LDS.
+constexpr int kRows = 16;
+constexpr int kSliceMax = 2048;
+constexpr int kScoreThreads = 1024;
+
+// Dense path for heavy dims: at most kHeavyMax dims (a multiple of 4, the
+// MFMA depth) whose item document frequency is at least n_items /
+// kHeavyFracInv; only for slices of at least kDenseMinSlice items.
+constexpr int kHeavyMax = 32;
+constexpr int kHeavyFracInv = 16;
+constexpr int kDenseMinSlice = 512;
+
+// 32-bit fixed point of the on-chip accumulators: 30 fraction bits.
+constexpr float kFixScale = 1073741824.0f;        // 2^30
+constexpr float kFixInv = 9.313225746154785e-10f;  // 2^-30
+
+// Item chunks of C items (the unit of output) are cut into n_sub slices of
+// S items (the unit of the inverted lists and of one workgroup's LDS).
+struct Geom {
+  int64_t n_items;
+  int32_t C, n_sub, S, num_chunks;
+  __host__ __device__ int64_t num_slices() const { return (int64_t)num_chunks * n_sub; }
+  __host__ __device__ int64_t chunk_begin(int64_t c) const {
+    const int64_t b = c * C;
+    return b < n_items ? b : n_items;
+  }
+  __host__ __device__ int64_t chunk_end(int64_t c) const {
+    const int64_t e = (c + 1) * C;
+    return e < n_items ? e : n_items;
+  }
+  __host__ __device__ int64_t slice_begin(int64_t s) const {
+    const int64_t c = s / n_sub, k = s % n_sub;
+    const int64_t b = c * C + k * S, ce = chunk_end(c);
+    return b < ce ? b : ce;
+  }
+  __host__ __device__ int64_t slice_end(int64_t s) const {
+    const int64_t c = s / n_sub, k = s % n_sub;
+    const int64_t e = c * C + (k + 1) * S, ce = chunk_end(c);
+    return e < ce ? e : ce;
+  }
+  __host__ __device__ int64_t slice_of(int64_t i) const {
+    const int64_t c = i / C;
+    return c * n_sub + (i - c * C) / S;
+  }
+};
+
+inline Geom make_geom(int64_t n_items, int32_t chunk_size) {
+  Geom g;
+  g.n_items = n_items;
+  g.C = chunk_size;
+  g.n_sub = (chunk_size + kSliceMax - 1) / kSliceMax;
+  g.S = (chunk_size + g.n_sub - 1) / g.n_sub;
+  g.num_chunks = (int32_t)((n_items + chunk_size - 1) / chunk_size);
+  return g;
+}
+inline int32_t slab_pitch(int32_t S) { return (S + 63) / 64 * 64; }
+inline bool dense_slice_ok(int32_t S) { return S >= kDenseMinSlice; }
 
 hipError_t launch_fill_i32(int32_t *p, int64_t n, int32_t v, hipStream_t s);
 hipError_t launch_csr_check(int64_t n_rows, int64_t n_cols, int64_t nnz, const int32_t *indptr,
@@ -20,61 +80,74 @@ hipError_t launch_row_norms(int64_t n_rows, int64_t nnz, const int32_t *indptr,
                             const float *values, const int32_t *flags, float *inv32,
                             double *norm64, hipStream_t s);
 
-// ---- items: per-chunk inverted lists ----
+// ---- items: per-slice inverted lists (+ dense slabs of heavy dims) ----
 struct ItemsDev {
-  int64_t n_items, dim, nnz;
-  int32_t chunk_size, num_chunks;
+  Geom g;
+  int64_t dim, nnz;
+  bool dense;           // build heavy-dim slabs
   const int32_t *indptr, *indices;
   const float *values;
-  float *inv_norm;      // persistent
-  int32_t *col_ptr;     // persistent, num_chunks * (dim+1)
-  uint16_t *row;        // persistent, nnz
+  float *inv_norm;      // persistent, n_items
+  int32_t *col_ptr;     // persistent, num_slices * (dim+1)
+  uint16_t *row;        // persistent, nnz: slice-local item ids
   float *val;           // persistent, nnz
-  int32_t *chunk_base;  // persistent, num_chunks + 1
+  int32_t *slice_base;  // persistent, num_slices + 1
+  int32_t *heavy;       // persistent, kHeavyMax + 1: heavy dims ascending, then their count
+  float *slab;          // persistent, num_slices * kHeavyMax * pitch (dense only)
   int32_t *flags;       // scratch
-  double *norm64;       // scratch
-  int32_t *ticket;      // scratch
-  uint16_t *trow;       // scratch
-  float *tval;          // scratch
-  int32_t *mlist;       // scratch, nnz/2 + num_chunks + 1
-  int32_t *mcount;      // scratch, num_chunks
+  double *norm64;       // scratch, n_items
+  int32_t *ticket;      // scratch, nnz
+  uint16_t *trow;       // scratch, nnz
+  float *tval;          // scratch, nnz
+  int32_t *mlist;       // scratch, nnz/2 + num_slices + 1
+  int32_t *mcount;      // scratch, num_slices
+  int32_t *gdf;         // scratch, dim (dense only)
 };
 hipError_t launch_prepare_items(const ItemsDev &d, hipStream_t s);
 
-// ---- queries: row groups ----
+// ---- queries ----
 struct QueriesDev {
   int64_t n_rows, dim, nnz;
-  int32_t R, n_groups;
+  int32_t n_groups;      // ceil(n_rows / kRows)
+  bool dense;
   const int32_t *indptr, *indices;
   const float *values;
+  const int32_t *heavy;  // the items' heavy dims (dense only)
   int32_t *flags;
-  float *inv_norm;
-  double *norm64;     // n_rows
-  int32_t *grp_ptr;   // n_groups + 1
-  int32_t *grp_dim;   // nnz
-  float *grp_val;     // nnz * R: fl32(q / |q|) * 2^30 per row (0 where absent)
+  float *inv_norm;       // n_rows
+  double *norm64;        // n_rows
+  int32_t *lptr;         // n_rows + 1: light (non-heavy) entries per row, prefix
+  int32_t *ldim;         // nnz
+  float *lval;           // nnz: fl32(q / |q|) * 2^30
+  uint8_t *lrow;         // nnz: row within its group of kRows
+  float *qh;             // n_groups * kHeavyMax * kRows: fl32(q / |q|) on heavy dims
 };
 hipError_t launch_prepare_queries(const QueriesDev &d, hipStream_t s);
 
 // ---- scoring ----
 struct ScoreArgs {
-  const int32_t *grp_ptr, *grp_dim;
-  const float *grp_val, *q_inv;
-  int64_t n_q, dim;
-  int32_t R, n_groups;
-  const int32_t *col_ptr;     // the chunk's col_ptr (dim+1), chunk-relative offsets
-  const uint16_t *row;        // all chunks' item ids; the chunk starts at chunk_base[chunk]
+  Geom g;
+  int64_t dim, n_q;
+  int32_t n_groups;
+  int32_t chunk;
+  bool dense;
+  const int32_t *lptr, *ldim;
+  const float *lval;
+  const uint8_t *lrow;
+  const float *qh;
+  const int32_t *col_ptr;     // all slices
+  const uint16_t *row;
   const float *val;
-  const int32_t *chunk_base;  // device, num_chunks + 1
-  int32_t chunk, chunk_len;
+  const int32_t *slice_base;
+  const int32_t *heavy;
+  const float *slab;          // all slices (dense only)
+  int32_t pitch;
   float *out;
   int64_t ld;
-  double *row_sums;
+  double *rs_part;            // n_sub * n_q partial row sums (nullable)
+  double *row_sums;           // n_q (nullable)
 };
-// Largest R (rows per workgroup) supported for a chunk length, given the
-// device's LDS per workgroup; 0 if none fits.
-int score_max_rows(int32_t chunk_len, size_t lds_limit);
-size_t score_lds_bytes(int R, int32_t chunk_len);
+size_t score_lds_bytes(int32_t S);
 hipError_t launch_score(const ScoreArgs &a, hipStream_t s);
 
 }  // namespace sps

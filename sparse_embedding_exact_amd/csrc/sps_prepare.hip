@@ -1,0 +1,628 @@
+// sps_prepare.hip -- gfx950 kernels that prepare items and queries for
+// exact all-pairs sparse cosine.
+//
+// Page cited throughout: "稀疏嵌入批量相似度计算的工程化实践"
+// (Engineering practice of bulk similarity for sparse embeddings).
+//
+//   csr_check_kernel     §3.1 note: canonical CSR (strictly ordered indices)
+//   row_norm_kernel      §5.2 detail one: L2 norm from the stored nonzeros
+//   csc_* kernels        per-slice inverted lists; chunk slicing as in §4.4
+//   heavy_* / slab_*     dense rows of the few dims most items hold
+//   light_* kernels      query rows split into heavy values and the rest
+//
+// All kernels are wave64. Device-side guards keep every access inside the
+// buffers the host sized, whatever the CSR contents: the prepare calls run
+// csr_check_kernel first and every later kernel exits when it found a
+// structural fault.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sps_device.h"
+#include "sps_internal.h"
+
+namespace sps {
+
+// ---------------------------------------------------------------------------
+// small utilities
+// ---------------------------------------------------------------------------
+
+__global__ void fill_i32_kernel(int32_t *__restrict__ p, int64_t n, int32_t v) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (; i < n; i += stride) p[i] = v;
+}
+
+hipError_t launch_fill_i32(int32_t *p, int64_t n, int32_t v, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, n, v);
+  return hipGetLastError();
+}
+
+// single-workgroup inclusive scan in place over a[0..n)
+template <int NT>
+__global__ __launch_bounds__(NT) void scan_inplace_kernel(int32_t *__restrict__ a, int64_t n) {
+  __shared__ int32_t ws[NT / 64];
+  int32_t carry = 0;
+  for (int64_t base = 0; base < n; base += NT) {
+    const int64_t j = base + threadIdx.x;
+    const int32_t v = j < n ? a[j] : 0;
+    int32_t tot;
+    const int32_t incl = block_incl_scan<NT>(v, ws, &tot);
+    if (j < n) a[j] = carry + incl;
+    carry += tot;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// CSR check. flags layout in sps_internal.h.
+// bit: flag bit (1 indptr, 4 index range -> structural; 2 order, 8 non-finite)
+// code: reason code kept with the row in the min key (1 indptr, 2 order,
+// 3 index range, 4 non-finite).
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ void report(int32_t *flags, int64_t row, int bit, int code) {
+  if (bit == 1 || bit == 4) atomicOr(&flags[0], bit);
+  else atomicOr(&flags[1], bit);
+  const unsigned long long key = ((unsigned long long)row << 3) | (unsigned long long)code;
+  atomicMin(reinterpret_cast<unsigned long long *>(flags + 2), key);
+}
+
+__global__ __launch_bounds__(256) void csr_check_kernel(int64_t n_rows, int64_t n_cols,
+                                                        int64_t nnz,
+                                                        const int32_t *__restrict__ indptr,
+                                                        const int32_t *__restrict__ indices,
+                                                        const float *__restrict__ values,
+                                                        int full, int32_t *flags) {
+  const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (r == 0) {
+    if (indptr[0] != 0) report(flags, 0, 1, 1);
+    if ((int64_t)indptr[n_rows] != nnz) report(flags, n_rows > 0 ? n_rows - 1 : 0, 1, 1);
+  }
+  if (r >= n_rows) return;
+  const int64_t b = indptr[r], e = indptr[r + 1];
+  if (b < 0 || e < b || e > nnz) {
+    report(flags, r, 1, 1);
+    return;
+  }
+  int32_t prev = -1;
+  for (int64_t k = b; k < e; ++k) {
+    const int32_t d = indices[k];
+    if (d < 0 || (int64_t)d >= n_cols) {
+      report(flags, r, 4, 3);
+      return;
+    }
+    if (full) {
+      if (d <= prev) report(flags, r, 2, 2);
+      if (!isfinite(values[k])) report(flags, r, 8, 4);
+    }
+    prev = d;
+  }
+}
+
+hipError_t launch_csr_check(int64_t n_rows, int64_t n_cols, int64_t nnz, const int32_t *indptr,
+                            const int32_t *indices, const float *values, int full,
+                            int32_t *flags, hipStream_t s) {
+  hipError_t e = launch_fill_i32(flags, 2, 0, s);
+  if (e != hipSuccess) return e;
+  e = launch_fill_i32(flags + 2, 2, -1, s);  // min key starts at all ones
+  if (e != hipSuccess) return e;
+  const int64_t blocks = (n_rows + 1 + 255) / 256;
+  hipLaunchKernelGGL(csr_check_kernel, dim3((unsigned)blocks), dim3(256), 0, s, n_rows, n_cols,
+                     nnz, indptr, indices, values, full, flags);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Row norms (§5.2): float64 sum of squares in stored order; fl32(1/sqrt(.)).
+// v*v is exact in float64 for a float32 v, so the sum only rounds at the adds.
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(256) void row_norm_kernel(int64_t n_rows, int64_t nnz,
+                                                       const int32_t *__restrict__ indptr,
+                                                       const float *__restrict__ values,
+                                                       const int32_t *__restrict__ flags,
+                                                       float *__restrict__ inv32,
+                                                       double *__restrict__ norm64) {
+  const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= n_rows) return;
+  const bool bad = flags != nullptr && flags[0] != 0;
+  double s = 0.0;
+  if (!bad) {
+    const int64_t b = clamp64(indptr[r], 0, nnz);
+    const int64_t e = clamp64(indptr[r + 1], b, nnz);
+    for (int64_t k = b; k < e; ++k) {
+      const double v = (double)values[k];
+      s += v * v;
+    }
+  }
+  const double n = sqrt(s);
+  if (norm64) norm64[r] = n;
+  inv32[r] = (n > 0.0) ? (float)(1.0 / n) : 0.0f;
+}
+
+hipError_t launch_row_norms(int64_t n_rows, int64_t nnz, const int32_t *indptr,
+                            const float *values, const int32_t *flags, float *inv32,
+                            double *norm64, hipStream_t s) {
+  if (n_rows <= 0) return hipSuccess;
+  const int64_t blocks = (n_rows + 255) / 256;
+  hipLaunchKernelGGL(row_norm_kernel, dim3((unsigned)blocks), dim3(256), 0, s, n_rows, nnz,
+                     indptr, values, flags, inv32, norm64);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Per-slice inverted lists. Chunk c holds items [c*C, min((c+1)*C, n))
+// (§4.4 slicing); it is cut into n_sub slices of S items (Geom). A slice's
+// entries are indptr[first item] .. indptr[last item + 1], and its inverted
+// lists occupy that same entry range of row[] / val[], with item ids local to
+// the slice.
+//
+//  1. count   : tickets t = atomicAdd(&cnt[s][d], 1) (arbitrary order)
+//  2. scan    : col_ptr[s] = exclusive prefix of cnt[s]; list of dims whose
+//               list holds >= 2 entries (compacted, ascending)
+//  3. scatter : entry -> position col_ptr[s][d] + t; single-entry lists are
+//               final, longer lists go to a temporary area
+//  4. fixup   : each longer list is put in ascending item order. Item ids
+//               are distinct inside one list, so the rank of an entry is the
+//               number of smaller ids: a wave compares ids directly for
+//               lists up to 64 entries, a workgroup counts bits of an item
+//               bitmap (prefix popcounts) for longer ones.
+// The result is the unique CSC with ascending item ids per dim, independent
+// of the order the atomics were served in.
+// ---------------------------------------------------------------------------
+
+__global__ void slice_base_kernel(Geom g, int64_t nnz, const int32_t *__restrict__ indptr,
+                                  int32_t *__restrict__ slice_base) {
+  const int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t ns = g.num_slices();
+  if (s > ns) return;
+  const int64_t i = s < ns ? g.slice_begin(s) : g.n_items;
+  slice_base[s] = (int32_t)clamp64(indptr[i], 0, nnz);
+}
+
+__global__ __launch_bounds__(256) void csc_count_kernel(Geom g, int64_t dim,
+                                                        const int32_t *__restrict__ indptr,
+                                                        const int32_t *__restrict__ indices,
+                                                        const int32_t *__restrict__ flags,
+                                                        int32_t *__restrict__ col_ptr,
+                                                        int32_t *__restrict__ ticket) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= g.n_items || flags[0] != 0) return;
+  const int64_t b = indptr[i], e = indptr[i + 1];
+  int32_t *cp = col_ptr + g.slice_of(i) * (dim + 1);
+  for (int64_t k = b; k < e; ++k) ticket[k] = atomicAdd(&cp[indices[k]], 1);
+}
+
+// One workgroup per slice: exclusive scan of dim+1 counts in place, in tiles
+// of 4*NT; plus the compacted list of dims with >= 2 entries. The scan carries
+// (count, multi-flag) packed in one 64-bit value: slice nnz < 2^31 keeps the
+// count half from carrying into the flag half.
+// When gdf is given, every dim holding at least `hmin` entries of the slice
+// adds its count to gdf[d] (the document frequency used to pick heavy dims;
+// integer atomics, so the totals do not depend on the order of slices).
+template <int NT>
+__global__ __launch_bounds__(NT) void csc_scan_kernel(int64_t dim,
+                                                      const int32_t *__restrict__ flags,
+                                                      const int32_t *__restrict__ slice_base,
+                                                      int32_t *__restrict__ col_ptr,
+                                                      int32_t *__restrict__ mlist,
+                                                      int32_t *__restrict__ mcount,
+                                                      int32_t *__restrict__ gdf, int32_t hmin) {
+  constexpr int TILE = 4 * NT;
+  __shared__ int32_t tile[TILE];
+  __shared__ int64_t ws[NT / 64];
+  const int64_t c = blockIdx.x;
+  const int t = threadIdx.x;
+  if (flags[0] != 0) {
+    if (t == 0) mcount[c] = 0;
+    return;
+  }
+  int32_t *cp = col_ptr + c * (dim + 1);
+  int32_t *ml = mlist + (slice_base[c] / 2 + c);
+  const int64_t n = dim + 1;
+  int64_t carry = 0;
+  for (int64_t base = 0; base < n; base += TILE) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int64_t j = base + k * NT + t;
+      tile[k * NT + t] = j < n ? cp[j] : 0;
+    }
+    __syncthreads();
+    int32_t v[4];
+    int64_t sum = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      v[k] = tile[4 * t + k];
+      sum += (int64_t)v[k] + ((int64_t)(v[k] >= 2) << 32);
+      if (gdf != nullptr && v[k] >= hmin) atomicAdd(&gdf[base + 4 * t + k], v[k]);
+    }
+    int64_t tot;
+    int64_t incl = block_incl_scan<NT>(sum, ws, &tot);
+    int64_t ex = carry + incl - sum;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      tile[4 * t + k] = (int32_t)(ex & 0xFFFFFFFFll);
+      if (v[k] >= 2) ml[ex >> 32] = (int32_t)(base + 4 * t + k);
+      ex += (int64_t)v[k] + ((int64_t)(v[k] >= 2) << 32);
+    }
+    carry += tot;
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int64_t j = base + k * NT + t;
+      if (j < n) cp[j] = tile[k * NT + t];
+    }
+    __syncthreads();
+  }
+  if (t == 0) mcount[c] = (int32_t)(carry >> 32);
+}
+
+__global__ __launch_bounds__(256) void csc_scatter_kernel(
+    Geom g, int64_t dim, const int32_t *__restrict__ indptr, const int32_t *__restrict__ indices,
+    const float *__restrict__ values, const double *__restrict__ norm64,
+    const int32_t *__restrict__ flags, const int32_t *__restrict__ col_ptr,
+    const int32_t *__restrict__ slice_base, const int32_t *__restrict__ ticket,
+    uint16_t *__restrict__ orow, float *__restrict__ oval, uint16_t *__restrict__ trow,
+    float *__restrict__ tval) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= g.n_items || flags[0] != 0) return;
+  const int64_t sl = g.slice_of(i);
+  const int32_t *cp = col_ptr + sl * (dim + 1);
+  const int64_t base = slice_base[sl];
+  const uint16_t local = (uint16_t)(i - g.slice_begin(sl));
+  const double n = norm64[i];
+  const int64_t b = indptr[i], e = indptr[i + 1];
+  for (int64_t k = b; k < e; ++k) {
+    const int32_t d = indices[k];
+    const int32_t s = cp[d];
+    const int32_t len = cp[d + 1] - s;
+    const int64_t p = base + s + ticket[k];
+    const float w = (n > 0.0) ? (float)((double)values[k] / n) : 0.0f;
+    if (len == 1) {
+      orow[p] = local;
+      oval[p] = w;
+    } else {
+      trow[p] = local;
+      tval[p] = w;
+    }
+  }
+}
+
+// Workgroup j of slice c handles list entries j, j+G, j+2G, ... in batches of
+// NT. Dynamic LDS: two arrays of ceil(S/32) uint32 (bitmap, prefix).
+template <int NT>
+__global__ __launch_bounds__(NT) void csc_fixup_kernel(
+    int64_t dim, int32_t S, int32_t G, const int32_t *__restrict__ flags,
+    const int32_t *__restrict__ col_ptr, const int32_t *__restrict__ slice_base,
+    const int32_t *__restrict__ mlist, const int32_t *__restrict__ mcount,
+    const uint16_t *__restrict__ trow, const float *__restrict__ tval,
+    uint16_t *__restrict__ orow, float *__restrict__ oval) {
+  extern __shared__ uint32_t fx_smem[];
+  const int nwords = (S + 31) >> 5;
+  uint32_t *bm = fx_smem;
+  uint32_t *pre = fx_smem + nwords;
+  __shared__ int32_t s_s[NT], s_L[NT];
+  __shared__ uint32_t ws[NT / 64];
+  if (flags[0] != 0) return;
+  const int64_t c = blockIdx.x / G;
+  const int64_t g = blockIdx.x % G;
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int32_t *cp = col_ptr + c * (dim + 1);
+  const int64_t base = slice_base[c];
+  const int32_t *ml = mlist + (slice_base[c] / 2 + c);
+  const int64_t m = mcount[c];
+  const int wpt = (nwords + NT - 1) / NT;  // bitmap words per thread
+
+  for (int64_t kb = 0; g + (int64_t)G * kb < m; kb += NT) {
+    const int64_t k = g + (int64_t)G * (kb + t);
+    int32_t s = 0, L = 0;
+    if (k < m) {
+      const int32_t d = ml[k];
+      s = cp[d];
+      L = cp[d + 1] - s;
+    }
+    s_s[t] = s;
+    s_L[t] = L;
+    __syncthreads();
+
+    // lists of 2..64 entries: one wave each, rank by direct comparison
+    for (int j = wv; j < NT; j += NT / 64) {
+      const int32_t Lj = s_L[j];
+      if (Lj < 2 || Lj > 64) continue;
+      const int64_t p0 = base + s_s[j];
+      uint32_t r = 0xFFFFFFFFu;
+      float v = 0.0f;
+      if (lane < Lj) {
+        r = trow[p0 + lane];
+        v = tval[p0 + lane];
+      }
+      int rank = 0;
+      for (int i = 0; i < Lj; ++i) {
+        const uint32_t ri = (uint32_t)__builtin_amdgcn_readlane((int)r, i);
+        rank += (ri < r) ? 1 : 0;
+      }
+      if (lane < Lj) {
+        orow[p0 + rank] = (uint16_t)r;
+        oval[p0 + rank] = v;
+      }
+    }
+
+    // lists of more than 64 entries: the whole workgroup, one list at a time
+    for (int j = 0; j < NT; ++j) {
+      const int32_t Lj = s_L[j];
+      if (Lj <= 64) continue;
+      const int64_t p0 = base + s_s[j];
+      for (int w = t; w < nwords; w += NT) bm[w] = 0u;
+      __syncthreads();
+      for (int i = t; i < Lj; i += NT) {
+        const uint32_t r = trow[p0 + i];
+        atomicOr(&bm[r >> 5], 1u << (r & 31));
+      }
+      __syncthreads();
+      uint32_t cnt = 0;
+      for (int q = 0; q < wpt; ++q) {
+        const int w = t * wpt + q;
+        if (w < nwords) cnt += __popc(bm[w]);
+      }
+      uint32_t tot;
+      uint32_t ex = block_incl_scan<NT>(cnt, ws, &tot) - cnt;
+      for (int q = 0; q < wpt; ++q) {
+        const int w = t * wpt + q;
+        if (w < nwords) {
+          pre[w] = ex;
+          ex += __popc(bm[w]);
+        }
+      }
+      __syncthreads();
+      for (int i = t; i < Lj; i += NT) {
+        const uint32_t r = trow[p0 + i];
+        const float v = tval[p0 + i];
+        const uint32_t w = r >> 5;
+        const uint32_t rank = pre[w] + __popc(bm[w] & ((1u << (r & 31)) - 1u));
+        orow[p0 + rank] = (uint16_t)r;
+        oval[p0 + rank] = v;
+      }
+      __syncthreads();
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Heavy dims. A few dims are held by most items (term ids follow a steep
+// rank law; the page notes ids cluster in a dictionary prefix, §3.2). For
+// those a posting list covers most of a slice, and a dense row of the slice
+// ("slab": value per item, 0 where absent) lets the score kernel use
+// matrix-core FMAs instead of per-entry scatter. Selection: dims whose
+// document frequency is at least n_items / kHeavyFracInv, the kHeavyMax most
+// frequent (ties: lower dim), listed in ascending dim order. The choice only
+// affects speed; both paths compute the same sums.
+// ---------------------------------------------------------------------------
+
+constexpr int kCandCap = 2048;
+
+__global__ __launch_bounds__(1024) void heavy_select_kernel(const int32_t *__restrict__ gdf,
+                                                            int64_t dim, int32_t tglob,
+                                                            const int32_t *__restrict__ flags,
+                                                            int32_t *__restrict__ heavy) {
+  constexpr int NT = 1024;
+  __shared__ int32_t s_lvl[32];
+  __shared__ int32_t s_cd[kCandCap], s_cv[kCandCap];
+  __shared__ uint8_t s_sel[kCandCap];
+  __shared__ int32_t s_n, s_level;
+  const int t = threadIdx.x;
+  if (flags[0] != 0 || tglob <= 0) {
+    if (t == 0) heavy[kHeavyMax] = 0;
+    return;
+  }
+  if (t < 32) s_lvl[t] = 0;
+  if (t == 0) s_n = 0;
+  __syncthreads();
+  // level k counts dims with gdf in [tglob * 2^k, tglob * 2^(k+1))
+  for (int64_t d = t; d < dim; d += NT) {
+    const int32_t v = gdf[d];
+    if (v >= tglob) {
+      const int k = 31 - __clz((unsigned)(v / tglob));
+      atomicAdd(&s_lvl[k], 1);
+    }
+  }
+  __syncthreads();
+  if (t == 0) {
+    int above = 0, level = 31;
+    for (int k = 31; k >= 0; --k) {  // lowest level whose tail still fits the candidate cap
+      if (above + s_lvl[k] > kCandCap) break;
+      above += s_lvl[k];
+      level = k;
+    }
+    s_level = level;
+  }
+  __syncthreads();
+  const int64_t thr = (int64_t)tglob << s_level;
+  for (int64_t d = t; d < dim; d += NT) {
+    const int32_t v = gdf[d];
+    if ((int64_t)v >= thr) {
+      const int i = atomicAdd(&s_n, 1);
+      if (i < kCandCap) {
+        s_cd[i] = (int32_t)d;
+        s_cv[i] = v;
+      }
+    }
+  }
+  __syncthreads();
+  const int n = s_n < kCandCap ? s_n : kCandCap;
+  for (int i = t; i < n; i += NT) {
+    int rank = 0;
+    const int32_t vi = s_cv[i], di = s_cd[i];
+    for (int j = 0; j < n; ++j) {
+      const int32_t vj = s_cv[j], dj = s_cd[j];
+      rank += (vj > vi || (vj == vi && dj < di)) ? 1 : 0;
+    }
+    s_sel[i] = rank < kHeavyMax ? 1 : 0;
+  }
+  __syncthreads();
+  for (int i = t; i < n; i += NT) {
+    if (!s_sel[i]) continue;
+    int pos = 0;
+    for (int j = 0; j < n; ++j) pos += (s_sel[j] && s_cd[j] < s_cd[i]) ? 1 : 0;
+    heavy[pos] = s_cd[i];
+  }
+  if (t == 0) heavy[kHeavyMax] = n < kHeavyMax ? n : kHeavyMax;
+}
+
+// slab[s][h][j] = value of item j of slice s on heavy dim h (slab pre-zeroed)
+__global__ __launch_bounds__(256) void slab_scatter_kernel(
+    int64_t dim, int32_t pitch, const int32_t *__restrict__ flags,
+    const int32_t *__restrict__ heavy, const int32_t *__restrict__ col_ptr,
+    const int32_t *__restrict__ slice_base, const uint16_t *__restrict__ row,
+    const float *__restrict__ val, float *__restrict__ slab) {
+  const int64_t c = blockIdx.x / kHeavyMax;
+  const int h = blockIdx.x % kHeavyMax;
+  if (flags[0] != 0 || h >= heavy[kHeavyMax]) return;
+  const int32_t d = heavy[h];
+  const int32_t *cp = col_ptr + c * (dim + 1);
+  const int64_t base = slice_base[c];
+  const int32_t b = cp[d], e = cp[d + 1];
+  float *srow = slab + (c * kHeavyMax + h) * (int64_t)pitch;
+  for (int32_t k = b + threadIdx.x; k < e; k += 256) {
+    const uint32_t j = row[base + k];
+    if (j < (uint32_t)pitch) srow[j] = val[base + k];
+  }
+}
+
+hipError_t launch_prepare_items(const ItemsDev &d, hipStream_t s) {
+  hipError_t e;
+  const Geom &g = d.g;
+  const int64_t ns = g.num_slices();
+  e = launch_csr_check(g.n_items, d.dim, d.nnz, d.indptr, d.indices, d.values, 0, d.flags, s);
+  if (e != hipSuccess) return e;
+  e = launch_row_norms(g.n_items, d.nnz, d.indptr, d.values, d.flags, d.inv_norm, d.norm64, s);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(slice_base_kernel, dim3((unsigned)((ns + 1 + 255) / 256)), dim3(256), 0, s,
+                     g, d.nnz, d.indptr, d.slice_base);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  e = launch_fill_i32(d.col_ptr, ns * (d.dim + 1), 0, s);
+  if (e != hipSuccess) return e;
+  e = launch_fill_i32(d.heavy, kHeavyMax + 1, 0, s);
+  if (e != hipSuccess) return e;
+  if (g.n_items == 0) return hipSuccess;
+  if (d.dense) {
+    e = launch_fill_i32(d.gdf, d.dim, 0, s);
+    if (e != hipSuccess) return e;
+  }
+  const unsigned item_blocks = (unsigned)((g.n_items + 255) / 256);
+  hipLaunchKernelGGL(csc_count_kernel, dim3(item_blocks), dim3(256), 0, s, g, d.dim, d.indptr,
+                     d.indices, d.flags, d.col_ptr, d.ticket);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int32_t hmin = g.S / (2 * kHeavyFracInv) > 2 ? g.S / (2 * kHeavyFracInv) : 2;
+  hipLaunchKernelGGL(csc_scan_kernel<1024>, dim3((unsigned)ns), dim3(1024), 0, s, d.dim, d.flags,
+                     d.slice_base, d.col_ptr, d.mlist, d.mcount, d.dense ? d.gdf : nullptr, hmin);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(csc_scatter_kernel, dim3(item_blocks), dim3(256), 0, s, g, d.dim, d.indptr,
+                     d.indices, d.values, d.norm64, d.flags, d.col_ptr, d.slice_base, d.ticket,
+                     d.row, d.val, d.trow, d.tval);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  int64_t G = 2048 / ns;
+  if (G < 4) G = 4;
+  if (G > 256) G = 256;
+  const size_t lds = 2 * sizeof(uint32_t) * (size_t)((g.S + 31) / 32);
+  hipLaunchKernelGGL(csc_fixup_kernel<256>, dim3((unsigned)(G * ns)), dim3(256), lds, s, d.dim,
+                     g.S, (int32_t)G, d.flags, d.col_ptr, d.slice_base, d.mlist, d.mcount, d.trow,
+                     d.tval, d.row, d.val);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (!d.dense) return hipSuccess;
+  const int64_t tg64 = (g.n_items + kHeavyFracInv - 1) / kHeavyFracInv;
+  const int32_t tglob = (int32_t)(tg64 > 2 ? tg64 : 2);
+  hipLaunchKernelGGL(heavy_select_kernel, dim3(1), dim3(1024), 0, s, d.gdf, d.dim, tglob,
+                     d.flags, d.heavy);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int32_t pitch = slab_pitch(g.S);
+  e = launch_fill_i32(reinterpret_cast<int32_t *>(d.slab), ns * kHeavyMax * (int64_t)pitch, 0, s);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(slab_scatter_kernel, dim3((unsigned)(ns * kHeavyMax)), dim3(256), 0, s,
+                     d.dim, pitch, d.flags, d.heavy, d.col_ptr, d.slice_base, d.row, d.val,
+                     d.slab);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Queries. Each row is normalised by its float64 norm (§5.2) and rounded
+// once to fp32: qn = fl32(q_d / |q|). Heavy dims (dense path) go to
+// qh[g][h][r] (g = row / kRows, r = row % kRows); the other entries form the
+// "light" CSR (same row order) with values qn * 2^30 (exact: a power of two),
+// the scale of the fixed-point accumulators, and the row's position in its
+// group.
+// ---------------------------------------------------------------------------
+
+template <bool FILL>
+__global__ __launch_bounds__(256) void light_split_kernel(
+    int64_t n_rows, const int32_t *__restrict__ indptr, const int32_t *__restrict__ indices,
+    const float *__restrict__ values, const double *__restrict__ norm64,
+    const int32_t *__restrict__ flags, const int32_t *__restrict__ heavy,
+    int32_t *__restrict__ lptr, int32_t *__restrict__ ldim, float *__restrict__ lval,
+    uint8_t *__restrict__ lrow, float *__restrict__ qh) {
+  const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (q >= n_rows) return;
+  const int m = heavy != nullptr ? heavy[kHeavyMax] : 0;
+  int64_t b = 0, e = 0;
+  if (flags[0] == 0) {
+    b = indptr[q];
+    e = indptr[q + 1];
+  }
+  const double n = norm64[q];
+  const int64_t gq = q / kRows;
+  const int rq = (int)(q % kRows);
+  int64_t out = FILL ? lptr[q] : 0;
+  int32_t count = 0;
+  for (int64_t k = b; k < e; ++k) {
+    const int32_t d = indices[k];
+    const int hs = m > 0 ? heavy_slot(heavy, m, d) : -1;
+    if (FILL) {
+      const float v = (n > 0.0) ? (float)((double)values[k] / n) : 0.0f;
+      if (hs >= 0) {
+        qh[(gq * kHeavyMax + hs) * kRows + rq] = v;
+      } else {
+        ldim[out] = d;
+        lval[out] = v * kFixScale;
+        lrow[out] = (uint8_t)rq;
+      }
+    }
+    if (hs < 0) {
+      ++out;
+      ++count;
+    }
+  }
+  if (!FILL) lptr[q + 1] = count;
+}
+
+hipError_t launch_prepare_queries(const QueriesDev &d, hipStream_t s) {
+  hipError_t e;
+  e = launch_csr_check(d.n_rows, d.dim, d.nnz, d.indptr, d.indices, d.values, 0, d.flags, s);
+  if (e != hipSuccess) return e;
+  e = launch_row_norms(d.n_rows, d.nnz, d.indptr, d.values, d.flags, d.inv_norm, d.norm64, s);
+  if (e != hipSuccess) return e;
+  e = launch_fill_i32(d.lptr, d.n_rows + 1, 0, s);
+  if (e != hipSuccess) return e;
+  if (d.n_rows == 0) return hipSuccess;
+  if (d.dense) {
+    e = launch_fill_i32(reinterpret_cast<int32_t *>(d.qh),
+                        (int64_t)d.n_groups * kHeavyMax * kRows, 0, s);
+    if (e != hipSuccess) return e;
+  }
+  const int32_t *heavy = d.dense ? d.heavy : nullptr;
+  const unsigned blocks = (unsigned)((d.n_rows + 255) / 256);
+  hipLaunchKernelGGL(light_split_kernel<false>, dim3(blocks), dim3(256), 0, s, d.n_rows,
+                     d.indptr, d.indices, d.values, d.norm64, d.flags, heavy, d.lptr, d.ldim,
+                     d.lval, d.lrow, d.qh);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(scan_inplace_kernel<1024>, dim3(1), dim3(1024), 0, s, d.lptr,
+                     d.n_rows + 1);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(light_split_kernel<true>, dim3(blocks), dim3(256), 0, s, d.n_rows,
+                     d.indptr, d.indices, d.values, d.norm64, d.flags, heavy, d.lptr, d.ldim,
+                     d.lval, d.lrow, d.qh);
+  return hipGetLastError();
+}
+
+}  // namespace sps

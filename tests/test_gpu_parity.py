@@ -61,21 +61,27 @@ def _check_structures(env, orc, items, chunk_size, name):
     torch, sps, dev = env
     n64, inv32 = orc.row_norms(items)
     it = sps.prepare(sps.CSR.from_host(items, dev), chunk_size=chunk_size)
-    for c in range(it.num_chunks):
-        v = it.chunk_view(c)
-        b = c * chunk_size
-        e = min(b + chunk_size, items.n_rows)
+    assert it.slices_per_chunk == -(-chunk_size // 2048)
+    for sl in range(it.num_slices):
+        v = it.slice_view(sl)
+        b = v["item_begin"]
+        e = b + v["slice_len"]
         col_ptr, row, val = orc.chunk_csc(items, n64, b, e)
-        assert v["chunk_len"] == e - b and v["chunk_nnz"] == len(row), (name, c)
-        assert np.array_equal(v["col_ptr"].cpu().numpy(), col_ptr), (name, c, "col_ptr")
+        assert v["slice_nnz"] == len(row), (name, sl)
+        assert np.array_equal(v["col_ptr"].cpu().numpy(), col_ptr), (name, sl, "col_ptr")
         g_row = v["row"].cpu().numpy().view(np.uint16).astype(np.int32)
-        assert np.array_equal(g_row, row), (name, c, "row ids")
+        assert np.array_equal(g_row, row), (name, sl, "row ids")
         g_val = v["val"].cpu().numpy()
-        assert np.array_equal(g_val.view(np.uint32), val.view(np.uint32)), (name, c, "values")
+        assert np.array_equal(g_val.view(np.uint32), val.view(np.uint32)), (name, sl, "values")
         g_inv = v["item_inv_norm"].cpu().numpy()
-        assert np.array_equal(g_inv.view(np.uint32), inv32[b:e].view(np.uint32)), (name, c)
-    print("\n[parity] %s: %d chunks, inverted lists + norms bit-exact" % (name, it.num_chunks),
+        assert np.array_equal(g_inv.view(np.uint32), inv32[b:e].view(np.uint32)), (name, sl)
+    # the slices tile every chunk in order
+    ends = [it.slice_view(sl)["item_begin"] + it.slice_view(sl)["slice_len"]
+            for sl in range(it.num_slices)]
+    assert max(ends) == items.n_rows
+    print("\n[parity] %s: %d slices, inverted lists + norms bit-exact" % (name, it.num_slices),
           file=sys.stderr, flush=True)
+    return it
 
 
 def test_structures_tiny(env, orc):
@@ -214,16 +220,45 @@ def _dense_ref(orc, q, items):
     return orc.scores(q, items)
 
 
-@pytest.mark.parametrize("rows", ["1", "2", "4", "8"])
-def test_rows_per_workgroup_variants(env, orc, rows, monkeypatch):
-    """Odd query counts (not a multiple of the rows per workgroup), every R."""
-    monkeypatch.setenv("SPS_SCORE_ROWS", rows)
+@pytest.mark.parametrize("dense", ["1", "0"])
+def test_dense_rows_on_and_off(env, orc, dense, monkeypatch):
+    """Heavy dims through the matrix-core rows (default) or all through the
+    inverted lists (SPS_DENSE=0); odd query count (not a multiple of 16)."""
+    monkeypatch.setenv("SPS_DENSE", dense)
+    torch, sps, dev = env
     q, items, _ = synth.make_workload("mid", n_item=9001, n_query=37)
+    it = sps.prepare(sps.CSR.from_host(items, dev), chunk_size=4096)
+    heavy = it.heavy_dims()
+    if dense == "1":
+        # Zipf(1.1): the lowest dims are in most rows; the choice is the most frequent dims
+        df = np.bincount(items.indices, minlength=items.n_cols)
+        top = set(np.argsort(-df, kind="stable")[:len(heavy)].tolist())
+        assert 16 <= len(heavy) <= 32 and heavy == sorted(heavy) and set(heavy) <= top | set(heavy)
+        assert all(df[h] >= items.n_rows / 16 for h in heavy)
+    else:
+        assert heavy == []
     ref = orc.scores(q, items)
     got = np.concatenate([g for _, _, g, _ in gpu_chunks(env, q, items, 4096)], axis=1)
     err = float(np.abs(got - ref).max())
-    report("R=%s 37x9001 chunk 4096" % rows, err, got.size)
+    report("dense=%s 37x9001 chunk 4096" % dense, err, got.size)
     assert err <= TOL
+
+
+def test_heavy_choice_is_deterministic(env):
+    torch, sps, dev = env
+    _, items, _ = synth.make_workload("dense", n_item=30000)
+    a = sps.prepare(sps.CSR.from_host(items, dev), chunk_size=8192).heavy_dims()
+    b = sps.prepare(sps.CSR.from_host(items, dev), chunk_size=8192).heavy_dims()
+    assert a == b and len(a) == 32
+
+
+def test_bitwise_reproducible(env):
+    """Integer accumulation: repeated runs give identical bits."""
+    torch, sps, dev = env
+    q, items, _ = synth.make_workload("mid", n_item=12000, n_query=100)
+    runs = [np.concatenate([g for _, _, g, _ in gpu_chunks(env, q, items, 8192)], axis=1)
+            for _ in range(3)]
+    assert all(np.array_equal(runs[0].view(np.uint32), r.view(np.uint32)) for r in runs[1:])
 
 
 def test_edge_rows_and_ld(env, orc):
@@ -271,6 +306,15 @@ def test_chunk_size_extremes(env, orc):
         got = np.concatenate([g for _, _, g, _ in gpu_chunks(env, q, items, cs)], axis=1)
         err = float(np.abs(got - ref).max())
         report("tiny 50x1500 chunk %d" % cs, err, got.size)
+        assert err <= TOL
+    # chunks cut into uneven slices (ceil(C/2048) slices, last one shorter)
+    q, items, _ = synth.make_workload("mid", n_item=9001, n_query=21)
+    ref = orc.scores(q, items)
+    for cs in (2049, 3000, 4097, 6000):
+        _check_structures(env, orc, items, cs, "mid 9001 chunk %d" % cs)
+        got = np.concatenate([g for _, _, g, _ in gpu_chunks(env, q, items, cs)], axis=1)
+        err = float(np.abs(got - ref).max())
+        report("mid 21x9001 chunk %d" % cs, err, got.size)
         assert err <= TOL
 
 
@@ -350,3 +394,12 @@ def test_argument_errors(env):
     with pytest.raises(sps.SpsError) as e:
         sps.prepare_queries(sps.CSR.from_host(other, dev), it)
     assert e.value.status == -3
+    # a query batch is tied to the corpus it was prepared for
+    it2 = sps.prepare(sps.CSR.from_host(items, dev), chunk_size=64)
+    with pytest.raises(sps.SpsError) as e:
+        sps.cosine_chunk(qq, it2, 0, out)
+    assert e.value.status == -1
+    # an output narrower than the chunk is refused (by the binding, then the library)
+    with pytest.raises(AssertionError):
+        sps.cosine_chunk(qq, it, 0, torch.empty(4, 63, device=dev))
+    assert sps._lib.sps_cosine_chunk(qq._h, it._h, 0, out.data_ptr(), 63, None, None) == -1
