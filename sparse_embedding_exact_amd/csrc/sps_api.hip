@@ -71,6 +71,16 @@ bool dense_wanted(const sps::Geom &g) {
   return true;
 }
 
+// Most heavy dims to take, kHeavyMax unless SPS_HEAVY_MAX (0..kHeavyMax) says
+// otherwise (a tuning knob: results do not depend on it beyond rounding).
+int32_t heavy_cap() {
+  if (const char *env = getenv("SPS_HEAVY_MAX")) {
+    const int v = atoi(env);
+    if (v >= 0 && v <= sps::kHeavyMax) return v;
+  }
+  return sps::kHeavyMax;
+}
+
 template <typename T>
 T *at(void *base, size_t off) {
   return reinterpret_cast<T *>(reinterpret_cast<char *>(base) + off);
@@ -231,6 +241,7 @@ sps_status sps_prepare(const sps_csr *items, int32_t chunk_size, void *persisten
   d.dim = items->n_cols;
   d.nnz = items->nnz;
   d.dense = dense;
+  d.heavy_cap = heavy_cap();
   d.indptr = items->indptr;
   d.indices = items->indices;
   d.values = items->values;

@@ -14,10 +14,11 @@ namespace sps {
 constexpr int kFlagsInts = 16;
 
 // Query rows per score workgroup and the widest item slice one workgroup
-// accumulates on chip: 16 rows x 2048 items x 4 B = 128 KiB of LDS.
-constexpr int kRows = 16;
+// accumulates on chip: 8 rows x 2048 items x 4 B = 64 KiB of LDS, so two
+// workgroups (8 waves each, one per row) share a CU's 160 KiB.
+constexpr int kRows = 8;
 constexpr int kSliceMax = 2048;
-constexpr int kScoreThreads = 1024;
+constexpr int kScoreThreads = 512;
 
 // Dense path for heavy dims: at most kHeavyMax dims (a multiple of 4, the
 // MFMA depth) whose item document frequency is at least n_items /
@@ -69,7 +70,10 @@ inline Geom make_geom(int64_t n_items, int32_t chunk_size) {
   g.num_chunks = (int32_t)((n_items + chunk_size - 1) / chunk_size);
   return g;
 }
-inline int32_t slab_pitch(int32_t S) { return (S + 63) / 64 * 64; }
+// Row pitch (items) of a slice's dense slab and of the score kernel's LDS
+// accumulators: a whole number of 256-item groups (one wave's share in the
+// dense part).
+__host__ __device__ inline int32_t slab_pitch(int32_t S) { return (S + 255) / 256 * 256; }
 inline bool dense_slice_ok(int32_t S) { return S >= kDenseMinSlice; }
 
 hipError_t launch_fill_i32(int32_t *p, int64_t n, int32_t v, hipStream_t s);
@@ -85,6 +89,7 @@ struct ItemsDev {
   Geom g;
   int64_t dim, nnz;
   bool dense;           // build heavy-dim slabs
+  int32_t heavy_cap;    // at most this many heavy dims (<= kHeavyMax)
   const int32_t *indptr, *indices;
   const float *values;
   float *inv_norm;      // persistent, n_items
@@ -120,7 +125,7 @@ struct QueriesDev {
   int32_t *ldim;         // nnz
   float *lval;           // nnz: fl32(q / |q|) * 2^30
   uint8_t *lrow;         // nnz: row within its group of kRows
-  float *qh;             // n_groups * kHeavyMax * kRows: fl32(q / |q|) on heavy dims
+  float *qh;             // [n_groups * kRows][kHeavyMax]: fl32(q / |q|) on heavy dims
 };
 hipError_t launch_prepare_queries(const QueriesDev &d, hipStream_t s);
 

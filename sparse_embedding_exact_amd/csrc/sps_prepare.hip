@@ -404,7 +404,7 @@ __global__ __launch_bounds__(NT) void csc_fixup_kernel(
 constexpr int kCandCap = 2048;
 
 __global__ __launch_bounds__(1024) void heavy_select_kernel(const int32_t *__restrict__ gdf,
-                                                            int64_t dim, int32_t tglob,
+                                                            int64_t dim, int32_t tglob, int32_t cap,
                                                             const int32_t *__restrict__ flags,
                                                             int32_t *__restrict__ heavy) {
   constexpr int NT = 1024;
@@ -413,7 +413,7 @@ __global__ __launch_bounds__(1024) void heavy_select_kernel(const int32_t *__res
   __shared__ uint8_t s_sel[kCandCap];
   __shared__ int32_t s_n, s_level;
   const int t = threadIdx.x;
-  if (flags[0] != 0 || tglob <= 0) {
+  if (flags[0] != 0 || tglob <= 0 || cap <= 0) {
     if (t == 0) heavy[kHeavyMax] = 0;
     return;
   }
@@ -459,7 +459,7 @@ __global__ __launch_bounds__(1024) void heavy_select_kernel(const int32_t *__res
       const int32_t vj = s_cv[j], dj = s_cd[j];
       rank += (vj > vi || (vj == vi && dj < di)) ? 1 : 0;
     }
-    s_sel[i] = rank < kHeavyMax ? 1 : 0;
+    s_sel[i] = rank < cap ? 1 : 0;
   }
   __syncthreads();
   for (int i = t; i < n; i += NT) {
@@ -468,7 +468,7 @@ __global__ __launch_bounds__(1024) void heavy_select_kernel(const int32_t *__res
     for (int j = 0; j < n; ++j) pos += (s_sel[j] && s_cd[j] < s_cd[i]) ? 1 : 0;
     heavy[pos] = s_cd[i];
   }
-  if (t == 0) heavy[kHeavyMax] = n < kHeavyMax ? n : kHeavyMax;
+  if (t == 0) heavy[kHeavyMax] = n < cap ? n : cap;
 }
 
 // slab[s][h][j] = value of item j of slice s on heavy dim h (slab pre-zeroed)
@@ -534,7 +534,7 @@ hipError_t launch_prepare_items(const ItemsDev &d, hipStream_t s) {
   if (!d.dense) return hipSuccess;
   const int64_t tg64 = (g.n_items + kHeavyFracInv - 1) / kHeavyFracInv;
   const int32_t tglob = (int32_t)(tg64 > 2 ? tg64 : 2);
-  hipLaunchKernelGGL(heavy_select_kernel, dim3(1), dim3(1024), 0, s, d.gdf, d.dim, tglob,
+  hipLaunchKernelGGL(heavy_select_kernel, dim3(1), dim3(1024), 0, s, d.gdf, d.dim, tglob, d.heavy_cap,
                      d.flags, d.heavy);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int32_t pitch = slab_pitch(g.S);
@@ -549,7 +549,7 @@ hipError_t launch_prepare_items(const ItemsDev &d, hipStream_t s) {
 // ---------------------------------------------------------------------------
 // Queries. Each row is normalised by its float64 norm (§5.2) and rounded
 // once to fp32: qn = fl32(q_d / |q|). Heavy dims (dense path) go to
-// qh[g][h][r] (g = row / kRows, r = row % kRows); the other entries form the
+// qh[row][h] (rows padded to a multiple of kRows); the other entries form the
 // "light" CSR (same row order) with values qn * 2^30 (exact: a power of two),
 // the scale of the fixed-point accumulators, and the row's position in its
 // group.
@@ -571,7 +571,6 @@ __global__ __launch_bounds__(256) void light_split_kernel(
     e = indptr[q + 1];
   }
   const double n = norm64[q];
-  const int64_t gq = q / kRows;
   const int rq = (int)(q % kRows);
   int64_t out = FILL ? lptr[q] : 0;
   int32_t count = 0;
@@ -581,7 +580,7 @@ __global__ __launch_bounds__(256) void light_split_kernel(
     if (FILL) {
       const float v = (n > 0.0) ? (float)((double)values[k] / n) : 0.0f;
       if (hs >= 0) {
-        qh[(gq * kHeavyMax + hs) * kRows + rq] = v;
+        qh[q * kHeavyMax + hs] = v;
       } else {
         ldim[out] = d;
         lval[out] = v * kFixScale;

@@ -6,10 +6,10 @@
 // support divided by both norms), §4.4 (items streamed chunk by chunk),
 // §2.3 (full float32 output, no top-K).
 //
-// One workgroup (1024 threads, 16 waves) scores kRows = 16 query rows
-// against one slice (<= 2048 items) of the chunk. LDS holds acc[16][Sp]
-// (Sp = slice rounded up to 64) as 32-bit fixed point with 30 fraction bits:
-// 128 KiB, one workgroup per CU.
+// One workgroup (512 threads, 8 waves) scores kRows = 8 query rows against
+// one slice (<= 2048 items) of the chunk. LDS holds acc[8][Sp] (Sp = slice
+// rounded up to 128) as 32-bit fixed point with 30 fraction bits: 64 KiB, so
+// two workgroups share a CU and one's stores overlap the other's gathers.
 //
 // Why fixed point: on gfx950 the LDS float atomic (ds_add_f32) sustains about
 // 0.3 updates per CU cycle, the 32-bit integer one (ds_add_u32) about 14.
@@ -18,22 +18,25 @@
 // below 2^30 plus rounding, inside int32. Integer addition is exact and
 // order independent: the result does not depend on how waves interleave.
 //
-// Dense part (heavy dims): v_mfma_f32_16x16x4f32 with A = 16 rows x 4 dims of
-// query values (lane i + 16k holds row i, dim k) and B = 4 dims x 16 items
-// of the slice's dense slab (lane j + 16k holds dim k, item j). Item
-// 4j + t of each 64-item group feeds the t-th of four MFMAs, so lane l ends
-// with rows 4(l/16)..+3 of items 4(l%16)..+3: one float4 per row. fp32
-// products and sums in a fixed order over the dims; the sums are added to
-// the fixed-point accumulators once at the end.
+// Dense part (heavy dims): v_mfma_f32_4x4x1f32, 16 independent 4x4x1 blocks
+// per instruction (lanes 4b..4b+3 form block b; lane l's result i is
+// A[lane 4(l/4) + i] * B[lane l]). Every lane supplies one item of the
+// slice's dense slab as B and lane m the value of query row m % 4 (or
+// 4 + m % 4) as A, so one B load feeds two MFMAs (rows 0-3, rows 4-7) and
+// lane l accumulates all 8 rows of its items. fp32 products and sums in a
+// fixed order over the dims; the sums, rounded once to fixed point, start
+// the accumulators.
 //
-// Sparse part (all other dims): the 16 rows' light entries (dim, value,
-// row) are taken in batches of 1024; thread t looks up dim t's posting list
-// [col_ptr[d], col_ptr[d+1]) in the slice, a block scan lays the lists end to
-// end, and the threads stride through that flat range with U loads in flight
-// before their updates: acc[row][j] += rn(fl32(qs * w)) (ds_add_u32), with
-// qs = fl32(q_d / |q|) * 2^30, w = fl32(i_d / |i|) and rn rounding to the
-// nearest integer (ties up). Posting entries are addressed by 32-bit byte
-// offsets from the slice's base (the prepare call keeps nnz below 2^30).
+// Sparse part (all other dims): the 8 rows' light entries (dim, value,
+// row) are taken in batches of 512; thread t looks up entry t's posting list
+// [col_ptr[d], col_ptr[d+1]) in the slice. Lists are cut into segments of
+// 16 postings, a block scan numbers the segments and a table in LDS names
+// each one's list, so 16 lanes take one segment with no search: lane i of a
+// segment handles posting 16k + i of its list, loads (item, w) and applies
+// acc[row][item] += rn(fl32(qs * w)) (ds_add_u32), with qs = fl32(q_d / |q|)
+// * 2^30, w = fl32(i_d / |i|) and rn rounding to the nearest integer (ties
+// up). Posting entries are addressed by 32-bit byte offsets from the slice's
+// base (the prepare call keeps nnz below 2^30).
 //
 // Epilogue: wave w writes row w: out[q, j] = fl32(acc) * 2^-30, 16-byte
 // nontemporal stores when aligned (the scores are not re-read, so they
@@ -67,16 +70,24 @@ __device__ __forceinline__ T ld_off(const T *base, uint32_t byte_off) {
 constexpr int NT = kScoreThreads;
 constexpr int NW = NT / 64;
 static_assert(NW == kRows, "one wave per query row in the epilogue");
-static_assert(kSliceMax <= NW * 2 * 64, "two 64-item groups per wave cover a slice");
+static_assert(kRows == 8, "the dense part maps two 4-row MFMA blocks");
+static_assert(kSliceMax <= NW * 256, "256 items per wave cover a slice");
+static_assert(kRows * kHeavyMax / 4 <= NT, "one float4 of heavy query values per thread");
+// Sparse part: posting lists are cut into segments of kSeg entries, one per
+// 16 lanes; a segment is named by (list, index) in 16 bits.
+constexpr int kSeg = 16;
+constexpr int kSegMax = 2048;  // segments per round (LDS table)
+static_assert(NT * ((kSliceMax + kSeg - 1) / kSeg) <= 65536, "segment names fit 16 bits");
+static_assert((kSliceMax + kSeg - 1) / kSeg <= 128, "segment index fits 7 bits");
 
 template <bool DENSE, int U>
-__global__ __launch_bounds__(NT) void score_kernel(const ScoreArgs a, int vec4) {
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void score_kernel(
+    const ScoreArgs a, int vec4) {
   extern __shared__ int acc[];
-  __shared__ int32_t s_start[NT];    // posting start per batch entry
-  __shared__ float s_qv[NT];         // fixed-point-scaled query value per batch entry
-  __shared__ int32_t s_row[NT];      // LDS offset of the entry's row
-  __shared__ int32_t s_pre[NT + 1];  // flat offsets of the batch's lists
+  __shared__ int4 s_rec[NT];          // per batch entry: posting start, length, row offset, value
+  __shared__ uint16_t s_seg[kSegMax];  // segment table of a round
   __shared__ int32_t ws[NW];
+  __shared__ __align__(16) float s_qh[DENSE ? kRows * kHeavyMax : 4];  // the rows' heavy values
 
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const int64_t grp = blockIdx.x;
@@ -85,151 +96,153 @@ __global__ __launch_bounds__(NT) void score_kernel(const ScoreArgs a, int vec4) 
   const int64_t sl = (int64_t)a.chunk * g.n_sub + ks;
   const int64_t ib = g.slice_begin(sl);
   const int32_t slen = (int32_t)(g.slice_end(sl) - ib);
-  const int32_t Sp = (g.S + 63) & ~63;
+  const int32_t Sp = slab_pitch(g.S);
   const int64_t q0 = grp * kRows;
   const int64_t qe = q0 + kRows < a.n_q ? q0 + kRows : a.n_q;
 
-  int4 *acc4 = reinterpret_cast<int4 *>(acc);
-  for (int k = t; k < kRows * Sp / 4; k += NT) acc4[k] = make_int4(0, 0, 0, 0);
-
-  // ---- dense part: heavy dims on the matrix cores (registers only) ----
-  f32x4 dacc[2][4];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int u = 0; u < 4; ++u) dacc[i][u] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (DENSE) {
-    const int m = a.heavy[kHeavyMax];
-    const int m8 = (m + 7) & ~7;  // qh and the slab are zero past m, up to kHeavyMax
-    const float *qg = a.qh + grp * (kHeavyMax * kRows);
-    const float *sbase = a.slab + sl * (int64_t)kHeavyMax * a.pitch;
-    const int kk = lane >> 4, jj = lane & 15;
-    for (int h0 = 0; h0 < m8; h0 += 8) {
-      float av[2];
-      f32x4 sv[2][2];
-#pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        const int h = h0 + 4 * p + kk;
-        av[p] = qg[h * kRows + jj];
-        const float *srow = sbase + (int64_t)h * a.pitch;
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const int gp = wv + NW * i;
-          sv[p][i] = gp * 64 < Sp ? *reinterpret_cast<const f32x4 *>(srow + gp * 64 + 4 * jj)
-                                  : f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-      }
-#pragma unroll
-      for (int p = 0; p < 2; ++p)
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int u = 0; u < 4; ++u)
-            dacc[i][u] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[p], sv[p][i][u], dacc[i][u], 0, 0,
-                                                              0);
-    }
-  }
-  __syncthreads();  // accumulators zeroed before any update
-
-  // ---- sparse part: the rows' light entries, batch by batch ----
+  // First batch of light entries (see the sparse part): descriptors are
+  // fetched before the dense part so that their two dependent loads (entry,
+  // then posting range) overlap it.
   const int32_t *cps = a.col_ptr + sl * (a.dim + 1);
   const int32_t cb0 = a.slice_base[sl];
   const int32_t snnz = a.slice_base[sl + 1] - cb0 > 0 ? a.slice_base[sl + 1] - cb0 : 0;
-  const uint16_t *__restrict__ prow = a.row + cb0;
-  const float *__restrict__ pval = a.val + cb0;
   const int32_t e0 = a.lptr[q0], e1 = a.lptr[qe];
-  for (int32_t eb = e0; eb < e1; eb += NT) {
-    const int n = (e1 - eb) < NT ? (e1 - eb) : NT;
-    int32_t s = 0, L = 0;
-    if (t < n) {
+  int32_t b_s = 0, b_L = 0, b_row = 0;
+  float b_qv = 0.f;
+  auto fetch = [&](int32_t eb) {
+    b_s = 0;
+    b_L = 0;
+    if (eb + t < e1) {
       const int32_t d = a.ldim[eb + t];
+      b_qv = a.lval[eb + t];
+      b_row = (int32_t)(a.lrow[eb + t] & (kRows - 1)) * Sp;
       if ((uint32_t)d < (uint64_t)a.dim) {
         const int32_t lo = cps[d], hi = cps[d + 1];
-        s = (int32_t)clamp64(lo, 0, snnz);
-        L = (int32_t)clamp64(hi, s, snnz) - s;
+        b_s = (int32_t)clamp64(lo, 0, snnz);
+        b_L = (int32_t)clamp64(hi, b_s, snnz) - b_s;
+        b_L = b_L < kSliceMax ? b_L : kSliceMax;  // a slice holds a dim at most once per item
       }
-      s_qv[t] = a.lval[eb + t];
-      s_row[t] = (int32_t)(a.lrow[eb + t] & (kRows - 1)) * Sp;
     }
-    s_start[t] = s;
-    int32_t total;
-    const int32_t incl = block_incl_scan<NT>(L, ws, &total);
-    s_pre[t + 1] = incl;
-    if (t == 0) s_pre[0] = 0;
-    __syncthreads();
+  };
+  fetch(e0);
 
-    // Wave w walks the flat range [total*w/NW, total*(w+1)/NW), lanes side by
-    // side (coalesced loads; a lane crosses few list boundaries). A lane finds
-    // its first list by binary search, later ones incrementally.
-    const int32_t fb = (int32_t)(((int64_t)total * wv) / NW);
-    const int32_t fe = (int32_t)(((int64_t)total * (wv + 1)) / NW);
-    int gi = 0;
-    {
-      int lo = 0, hi = n;  // largest gi with s_pre[gi] <= fb + lane
-      const int32_t f = fb + lane;
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (s_pre[mid] <= f) lo = mid;
-        else hi = mid;
-      }
-      gi = lo;
-    }
-    // the lane's current list, kept in registers
-    int32_t t_end = s_pre[gi + 1], t_base = s_start[gi] - s_pre[gi], t_off = s_row[gi];
-    float t_qv = s_qv[gi];
-    for (int32_t f0 = fb + lane; f0 < fe; f0 += 64 * U) {
-      uint32_t pos[U];
-      int32_t aoff[U];
-      float qv[U];
-      bool ok[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int32_t f = f0 + u * 64;
-        ok[u] = f < fe;
-        if (ok[u] && f >= t_end) {
-          do {
-            ++gi;
-          } while (s_pre[gi + 1] <= f);
-          t_end = s_pre[gi + 1];
-          t_base = s_start[gi] - s_pre[gi];
-          t_off = s_row[gi];
-          t_qv = s_qv[gi];
-        }
-        pos[u] = ok[u] ? (uint32_t)(t_base + f) : 0u;
-        aoff[u] = t_off;
-        qv[u] = t_qv;
-      }
-      uint32_t rw[U];
-      float w[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        rw[u] = ld_off(prow, pos[u] * 2u);
-        w[u] = ld_off(pval, pos[u] * 4u);
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        if (ok[u] && rw[u] < (uint32_t)slen)
-          atomicAdd(&acc[aoff[u] + (int)rw[u]], round_fix(qv[u] * w[u]));
-      }
-    }
-    __syncthreads();
-  }
-
-  // ---- dense sums into the accumulators ----
+  // ---- dense part: heavy dims on the matrix cores ----
+  // Wave w owns items [256 w, 256 w + 256) of the slice, 4 per lane. Dims are
+  // taken 4 at a time, the next 4 loaded while the current ones are
+  // multiplied. qh and the slab hold zeros from the last heavy dim up to
+  // kHeavyMax, so rounding the dim count up to 8 only adds exact zeros. The
+  // sums, rounded to fixed point, are the accumulators' initial values.
+  const int32_t wcol = wv * 256;
   if (DENSE) {
-    const int kk = lane >> 4, jj = lane & 15;
+    const int mr = (a.heavy[kHeavyMax] + 7) & ~7;
+    const float *sb = a.slab + sl * (int64_t)kHeavyMax * a.pitch + (wcol < Sp ? wcol : 0) + 4 * lane;
+    f32x4 sv[2][4];
+    auto load = [&](int b, int h0) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int gp = wv + NW * i;
-      if (gp * 64 >= Sp) continue;
+      for (int p = 0; p < 4; ++p)
+        sv[b][p] = *reinterpret_cast<const f32x4 *>(sb + (int64_t)(h0 + p) * a.pitch);
+    };
+    if (mr > 0) load(0, 0);
+    if (t < kRows * kHeavyMax / 4)
+      reinterpret_cast<f32x4 *>(s_qh)[t] =
+          reinterpret_cast<const f32x4 *>(a.qh + grp * (kRows * kHeavyMax))[t];
+    __syncthreads();
+    f32x4 dacc[2][4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        int *dst = acc + (4 * kk + r) * Sp + gp * 64 + 4 * jj;
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int u = 0; u < 4; ++u) atomicAdd(dst + u, round_fix(dacc[i][u][r] * kFixScale));
+      for (int u = 0; u < 4; ++u) dacc[i][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // A operands: lane m supplies query row m % 4 (block 0) and 4 + m % 4
+    // (block 1), four dims per LDS read.
+    const float *qa = s_qh + (lane & 3) * kHeavyMax;
+    auto mma = [&](int b, int h0) {
+      const f32x4 alo = *reinterpret_cast<const f32x4 *>(qa + h0);
+      const f32x4 ahi = *reinterpret_cast<const f32x4 *>(qa + 4 * kHeavyMax + h0);
+#pragma unroll
+      for (int p = 0; p < 4; ++p)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          dacc[0][u] = __builtin_amdgcn_mfma_f32_4x4x1f32(alo[p], sv[b][p][u], dacc[0][u], 0, 0, 0);
+          dacc[1][u] = __builtin_amdgcn_mfma_f32_4x4x1f32(ahi[p], sv[b][p][u], dacc[1][u], 0, 0, 0);
+        }
+    };
+    if (wcol < Sp) {
+      for (int h0 = 0; h0 < mr; h0 += 8) {
+        load(1, h0 + 4);
+        mma(0, h0);
+        if (h0 + 8 < mr) load(0, h0 + 8);
+        mma(1, h0 + 4);
+      }
+      // lane l holds rows 4b + i of items 4l + u in dacc[b][u][i]
+#pragma unroll
+      for (int r = 0; r < kRows; ++r) {
+        const int b = r >> 2, i = r & 3;
+        reinterpret_cast<int4 *>(acc + r * Sp + wcol)[lane] =
+            make_int4(round_fix(dacc[b][0][i] * kFixScale), round_fix(dacc[b][1][i] * kFixScale),
+                      round_fix(dacc[b][2][i] * kFixScale), round_fix(dacc[b][3][i] * kFixScale));
       }
     }
-    __syncthreads();
+  } else {
+    int4 *acc4 = reinterpret_cast<int4 *>(acc);
+    for (int k = t; k < kRows * Sp / 4; k += NT) acc4[k] = make_int4(0, 0, 0, 0);
+  }
+  __syncthreads();  // accumulators initialised before any sparse update
+
+  // ---- sparse part: the rows' light entries, batch by batch ----
+  const uint16_t *__restrict__ prow = a.row + cb0;
+  const float *__restrict__ pval = a.val + cb0;
+  for (int32_t eb = e0; eb < e1; eb += NT) {
+    // list record of entry t: posting start, length, LDS row offset, value
+    s_rec[t] = make_int4(b_s, b_L, b_row, __float_as_int(b_qv));
+    const int32_t nseg = (b_L + kSeg - 1) / kSeg;
+    int32_t total;
+    const int32_t sp0 = block_incl_scan<NT>(nseg, ws, &total) - nseg;  // barrier inside
+    if (eb + NT < e1) fetch(eb + NT);  // next batch's descriptors, in flight during this one
+    for (int32_t r0 = 0; r0 < total; r0 += kSegMax) {
+      // segment table of the round: list id and segment index within the list
+      const int32_t sb = sp0 > r0 ? sp0 : r0;
+      const int32_t se = sp0 + nseg < r0 + kSegMax ? sp0 + nseg : r0 + kSegMax;
+      for (int32_t sg = sb; sg < se; ++sg) s_seg[sg - r0] = (uint16_t)((t << 7) | (sg - sp0));
+      __syncthreads();
+      const int32_t nr = total - r0 < kSegMax ? total - r0 : kSegMax;
+      // wave w takes segment quads w, w + NW, ...; lanes 16i..16i+15 segment i of a quad
+      for (int32_t k0 = wv; 4 * k0 < nr; k0 += NW * U) {
+        uint32_t pos[U];
+        int32_t aoff[U];
+        float qv[U];
+        bool ok[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int32_t sg = 4 * (k0 + NW * u) + (lane >> 4);
+          const bool in = sg < nr;
+          const uint32_t desc = s_seg[in ? sg : 0];
+          const int4 rec = s_rec[desc >> 7];
+          const int32_t j = (int32_t)(desc & 127) * kSeg + (lane & 15);
+          ok[u] = in && j < rec.y;
+          pos[u] = ok[u] ? (uint32_t)(rec.x + j) : 0u;
+          aoff[u] = rec.z;
+          qv[u] = __int_as_float(rec.w);
+        }
+        uint16_t rw[U];
+        float w[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          rw[u] = ld_off(prow, pos[u] * 2u);
+          w[u] = ld_off(pval, pos[u] * 4u);
+        }
+        // all 2U loads are in flight before the first is waited on (keeps the
+        // compiler from sinking a load into the masked update below it)
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < U; ++u) asm volatile("" ::"v"(rw[u]), "v"(w[u]));
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          if (ok[u] && (int32_t)rw[u] < slen)
+            atomicAdd(&acc[aoff[u] + (int)rw[u]], round_fix(qv[u] * w[u]));
+        }
+      }
+      __syncthreads();
+    }
   }
 
   // ---- epilogue: wave w writes row w ----
@@ -275,8 +288,9 @@ __global__ void fold_row_sums_kernel(int64_t n_q, int32_t n_sub, const double *_
 }
 
 size_t score_lds_bytes(int32_t S) {
-  const size_t Sp = (size_t)((S + 63) & ~63);
-  return (size_t)kRows * Sp * sizeof(int) + NT * 4 * 3 + (NT + 1) * 4 + NW * 4;
+  const size_t Sp = (size_t)slab_pitch(S);
+  return (size_t)kRows * Sp * sizeof(int) + NT * 16 + kSegMax * 2 + NW * 4 +
+         kRows * kHeavyMax * 4;
 }
 
 static int env_unroll() {
@@ -293,7 +307,7 @@ static int env_unroll() {
 
 template <bool DENSE, int U>
 static hipError_t launch_t(const ScoreArgs &a, hipStream_t s) {
-  const int32_t Sp = (a.g.S + 63) & ~63;
+  const int32_t Sp = slab_pitch(a.g.S);
   const size_t dyn = (size_t)kRows * Sp * sizeof(int);
   auto kern = score_kernel<DENSE, U>;
   // dynamic LDS above 64 KiB needs an explicit opt-in per kernel
