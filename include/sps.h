@@ -99,13 +99,14 @@ sps_status sps_items_workspace_size(int64_t n_items, int64_t dim, int64_t nnz,
  *     over the stored nonzeros in index order (§5.2); 0 for a zero norm;
  *  2. chunk c covers items [c*chunk_size, min((c+1)*chunk_size, n_items))
  *     (§4.4 slicing). Each chunk is cut into slices_per_chunk =
- *     ceil(chunk_size / 2048) slices of slice_size = ceil(chunk_size /
+ *     ceil(chunk_size / 1024) slices of slice_size = ceil(chunk_size /
  *     slices_per_chunk) items (the last slice of a chunk may be shorter): a
  *     slice is what one workgroup accumulates on chip;
  *  3. per slice, the inverted lists: col_ptr[dim+1] (slice-relative offsets,
- *     col_ptr[0] = 0, col_ptr[dim] = slice nnz), and for every entry the
- *     slice-local item id (uint16) and value fl32(v / ||item||) rounded once
- *     from float64 (0 if the item norm is 0). Item ids ascend within each dim;
+ *     col_ptr[0] = 0, col_ptr[dim] = slice nnz), and for every entry an
+ *     sps_posting: the slice-local item id and the value fl32(v / ||item||)
+ *     rounded once from float64 (0 if the item norm is 0). Item ids ascend
+ *     within each dim;
  *  4. when slices hold at least 512 items: the "heavy" dims (at most 32, the
  *     most frequent among those held by at least 1/16 of the items) and, per
  *     slice, their values as dense rows (0 where an item lacks the dim). This
@@ -124,18 +125,25 @@ sps_status sps_items_info(const sps_items *h, int64_t *n_items, int64_t *dim, in
 sps_status sps_items_slices(const sps_items *h, int32_t *slice_size, int32_t *slices_per_chunk,
                             int64_t *num_slices);
 
+/* One entry of a slice's inverted lists: the slice-local item id and the
+ * value fl32(v / ||item||). Stored together (8 bytes) so that one load
+ * fetches both. */
+typedef struct {
+  uint32_t item;
+  float value;
+} sps_posting;
+
 /* Device views of one prepared slice (for parity tests and tooling).
  * SYNCHRONOUS: reads the slice's entry range back from the device after
- * synchronising `stream`. col_ptr: DEVICE int32[dim+1]; row: DEVICE
- * uint16[slice_nnz]; val: DEVICE float[slice_nnz]; item_inv_norm: DEVICE
- * float[slice_len] (the slice's first item onwards). */
+ * synchronising `stream`. col_ptr: DEVICE int32[dim+1]; post: DEVICE
+ * sps_posting[slice_nnz]; item_inv_norm: DEVICE float[slice_len] (the
+ * slice's first item onwards). */
 typedef struct {
   int64_t item_begin;
   int32_t slice_len;
   int32_t slice_nnz;
   const int32_t *col_ptr;
-  const uint16_t *row;
-  const float *val;
+  const sps_posting *post;
   const float *item_inv_norm;
 } sps_slice_view;
 
@@ -163,7 +171,7 @@ sps_status sps_queries_workspace_size(const sps_items *items, int64_t n_rows, in
 /* Prepare a query batch for the prepared items `items` (asynchronous):
  * inverse norms as for items (§5.2); every row normalised by its float64
  * norm and rounded once to fp32, fl32(q_d / ||q||); values on the items'
- * heavy dims gathered into dense blocks of 8 rows, the rest kept as a CSR of
+ * heavy dims gathered into dense blocks of 16 rows, the rest kept as a CSR of
  * "light" entries. The query CSR may be released once this stream work has
  * completed. The batch can only be scored against `items`. Free the handle
  * with sps_queries_destroy. */

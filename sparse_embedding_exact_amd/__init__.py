@@ -51,7 +51,7 @@ class _Csr(ctypes.Structure):
 class _SliceView(ctypes.Structure):
     _fields_ = [("item_begin", ctypes.c_int64), ("slice_len", ctypes.c_int32),
                 ("slice_nnz", ctypes.c_int32), ("col_ptr", ctypes.c_void_p),
-                ("row", ctypes.c_void_p), ("val", ctypes.c_void_p),
+                ("post", ctypes.c_void_p),
                 ("item_inv_norm", ctypes.c_void_p)]
 
 
@@ -210,8 +210,8 @@ class Items:
         return {
             "item_begin": v.item_begin, "slice_len": v.slice_len, "slice_nnz": v.slice_nnz,
             "col_ptr": view(v.col_ptr, self.dim + 1, torch.int32, 4),
-            "row": view(v.row, v.slice_nnz, torch.int16, 2),
-            "val": view(v.val, v.slice_nnz, torch.float32, 4),
+            # sps_posting records: int32 pairs (item id, value bits)
+            "post": view(v.post, v.slice_nnz, torch.int32, 8).view(-1, 2),
             "item_inv_norm": view(v.item_inv_norm, v.slice_len, torch.float32, 4),
         }
 

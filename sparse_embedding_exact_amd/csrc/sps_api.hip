@@ -87,7 +87,7 @@ T *at(void *base, size_t off) {
 }
 
 struct ItemsLayout {
-  size_t inv, colp, row, val, sbase, heavy, slab, persistent;
+  size_t inv, colp, post, sbase, heavy, slab, persistent;
   size_t flags, norm64, ticket, trow, tval, mlist, mcount, gdf, scratch;
   bool overflow;
 };
@@ -98,8 +98,7 @@ ItemsLayout items_layout(const sps::Geom &g, int64_t dim, int64_t nnz, bool dens
   Layout p;
   L.inv = p.add(g.n_items, 4);
   L.colp = p.add((uint64_t)ns * (uint64_t)(dim + 1), 4);
-  L.row = p.add(nnz, 2);
-  L.val = p.add(nnz, 4);
+  L.post = p.add(nnz, 8);
   L.sbase = p.add(ns + 1, 4);
   L.heavy = p.add(sps::kHeavyMax + 1, 4);
   L.slab = p.add(dense ? (uint64_t)ns * sps::kHeavyMax * (uint64_t)sps::slab_pitch(g.S) : 0, 4);
@@ -151,8 +150,7 @@ struct sps_items {
   int32_t pitch;  // slab row pitch (items), dense only
   float *inv_norm;
   int32_t *col_ptr;
-  uint16_t *row;
-  float *val;
+  uint2 *post;
   int32_t *slice_base;
   int32_t *heavy;
   float *slab;
@@ -247,8 +245,7 @@ sps_status sps_prepare(const sps_csr *items, int32_t chunk_size, void *persisten
   d.values = items->values;
   d.inv_norm = at<float>(persistent, L.inv);
   d.col_ptr = at<int32_t>(persistent, L.colp);
-  d.row = at<uint16_t>(persistent, L.row);
-  d.val = at<float>(persistent, L.val);
+  d.post = at<uint2>(persistent, L.post);
   d.slice_base = at<int32_t>(persistent, L.sbase);
   d.heavy = at<int32_t>(persistent, L.heavy);
   d.slab = dense ? at<float>(persistent, L.slab) : nullptr;
@@ -276,8 +273,7 @@ sps_status sps_prepare(const sps_csr *items, int32_t chunk_size, void *persisten
   h->pitch = dense ? sps::slab_pitch(g.S) : 0;
   h->inv_norm = d.inv_norm;
   h->col_ptr = d.col_ptr;
-  h->row = d.row;
-  h->val = d.val;
+  h->post = d.post;
   h->slice_base = d.slice_base;
   h->heavy = d.heavy;
   h->slab = d.slab;
@@ -320,8 +316,7 @@ sps_status sps_items_slice_view(const sps_items *h, int64_t slice, void *stream,
   view->slice_len = (int32_t)(h->g.slice_end(slice) - view->item_begin);
   view->slice_nnz = be[1] - be[0];
   view->col_ptr = h->col_ptr + slice * (h->dim + 1);
-  view->row = h->row + be[0];
-  view->val = h->val + be[0];
+  view->post = reinterpret_cast<const sps_posting *>(h->post + be[0]);
   view->item_inv_norm = h->inv_norm + view->item_begin;
   return SPS_OK;
 }
@@ -441,6 +436,10 @@ static sps_status check_score_args(const sps_queries *q, const sps_items *items,
                 (long long)ld_out, (long long)width);
   if (q->n_rows > 0 && (uint64_t)ld_out > (uint64_t)INT64_MAX / 4 / (uint64_t)q->n_rows)
     return fail(SPS_ERR_OVERFLOW, "n_rows * ld_out overflows");
+  // one workgroup per (row group, slice) in a one-dimensional grid
+  if ((int64_t)q->n_groups * items->g.n_sub > kI32Max)
+    return fail(SPS_ERR_OVERFLOW, "%lld row groups x %d slices exceed the launch grid",
+                (long long)q->n_groups, items->g.n_sub);
   return SPS_OK;
 }
 
@@ -459,8 +458,7 @@ static sps_status score_one(const sps_queries *q, const sps_items *items, int32_
   a.lrow = q->lrow;
   a.qh = q->qh;
   a.col_ptr = items->col_ptr;
-  a.row = items->row;
-  a.val = items->val;
+  a.post = items->post;
   a.slice_base = items->slice_base;
   a.heavy = items->heavy;
   a.slab = items->slab;

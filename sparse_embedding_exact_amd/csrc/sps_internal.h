@@ -14,10 +14,10 @@ namespace sps {
 constexpr int kFlagsInts = 16;
 
 // Query rows per score workgroup and the widest item slice one workgroup
-// accumulates on chip: 8 rows x 2048 items x 4 B = 64 KiB of LDS, so two
-// workgroups (8 waves each, one per row) share a CU's 160 KiB.
-constexpr int kRows = 8;
-constexpr int kSliceMax = 2048;
+// accumulates on chip: 16 rows x 1024 items x 4 B = 64 KiB of LDS, so two
+// workgroups (8 waves each) share a CU's 160 KiB.
+constexpr int kRows = 16;
+constexpr int kSliceMax = 1024;
 constexpr int kScoreThreads = 512;
 
 // Dense path for heavy dims: at most kHeavyMax dims (a multiple of 4, the
@@ -70,10 +70,12 @@ inline Geom make_geom(int64_t n_items, int32_t chunk_size) {
   g.num_chunks = (int32_t)((n_items + chunk_size - 1) / chunk_size);
   return g;
 }
-// Row pitch (items) of a slice's dense slab and of the score kernel's LDS
-// accumulators: a whole number of 256-item groups (one wave's share in the
-// dense part).
-__host__ __device__ inline int32_t slab_pitch(int32_t S) { return (S + 255) / 256 * 256; }
+// Row pitch (items) of a slice's dense slab: a whole number of 128-item
+// groups (one wave's share in the dense part).
+__host__ __device__ inline int32_t slab_pitch(int32_t S) { return (S + 127) / 128 * 128; }
+// Row pitch (ints) of the score kernel's LDS accumulators: the slab pitch
+// plus 4, so that rows start 16 bytes apart modulo the LDS bank period.
+__host__ __device__ inline int32_t acc_pitch(int32_t S) { return slab_pitch(S) + 4; }
 inline bool dense_slice_ok(int32_t S) { return S >= kDenseMinSlice; }
 
 hipError_t launch_fill_i32(int32_t *p, int64_t n, int32_t v, hipStream_t s);
@@ -94,8 +96,7 @@ struct ItemsDev {
   const float *values;
   float *inv_norm;      // persistent, n_items
   int32_t *col_ptr;     // persistent, num_slices * (dim+1)
-  uint16_t *row;        // persistent, nnz: slice-local item ids
-  float *val;           // persistent, nnz
+  uint2 *post;          // persistent, nnz: (slice-local item id, value bits)
   int32_t *slice_base;  // persistent, num_slices + 1
   int32_t *heavy;       // persistent, kHeavyMax + 1: heavy dims ascending, then their count
   float *slab;          // persistent, num_slices * kHeavyMax * pitch (dense only)
@@ -141,8 +142,7 @@ struct ScoreArgs {
   const uint8_t *lrow;
   const float *qh;
   const int32_t *col_ptr;     // all slices
-  const uint16_t *row;
-  const float *val;
+  const uint2 *post;          // all slices: (slice-local item id, value bits)
   const int32_t *slice_base;
   const int32_t *heavy;
   const float *slab;          // all slices (dense only)

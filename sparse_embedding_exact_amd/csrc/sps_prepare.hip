@@ -264,8 +264,7 @@ __global__ __launch_bounds__(256) void csc_scatter_kernel(
     const float *__restrict__ values, const double *__restrict__ norm64,
     const int32_t *__restrict__ flags, const int32_t *__restrict__ col_ptr,
     const int32_t *__restrict__ slice_base, const int32_t *__restrict__ ticket,
-    uint16_t *__restrict__ orow, float *__restrict__ oval, uint16_t *__restrict__ trow,
-    float *__restrict__ tval) {
+    uint2 *__restrict__ post, uint16_t *__restrict__ trow, float *__restrict__ tval) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= g.n_items || flags[0] != 0) return;
   const int64_t sl = g.slice_of(i);
@@ -281,8 +280,7 @@ __global__ __launch_bounds__(256) void csc_scatter_kernel(
     const int64_t p = base + s + ticket[k];
     const float w = (n > 0.0) ? (float)((double)values[k] / n) : 0.0f;
     if (len == 1) {
-      orow[p] = local;
-      oval[p] = w;
+      post[p] = make_uint2(local, __float_as_uint(w));
     } else {
       trow[p] = local;
       tval[p] = w;
@@ -298,7 +296,7 @@ __global__ __launch_bounds__(NT) void csc_fixup_kernel(
     const int32_t *__restrict__ col_ptr, const int32_t *__restrict__ slice_base,
     const int32_t *__restrict__ mlist, const int32_t *__restrict__ mcount,
     const uint16_t *__restrict__ trow, const float *__restrict__ tval,
-    uint16_t *__restrict__ orow, float *__restrict__ oval) {
+    uint2 *__restrict__ post) {
   extern __shared__ uint32_t fx_smem[];
   const int nwords = (S + 31) >> 5;
   uint32_t *bm = fx_smem;
@@ -343,10 +341,7 @@ __global__ __launch_bounds__(NT) void csc_fixup_kernel(
         const uint32_t ri = (uint32_t)__builtin_amdgcn_readlane((int)r, i);
         rank += (ri < r) ? 1 : 0;
       }
-      if (lane < Lj) {
-        orow[p0 + rank] = (uint16_t)r;
-        oval[p0 + rank] = v;
-      }
+      if (lane < Lj) post[p0 + rank] = make_uint2(r, __float_as_uint(v));
     }
 
     // lists of more than 64 entries: the whole workgroup, one list at a time
@@ -381,8 +376,7 @@ __global__ __launch_bounds__(NT) void csc_fixup_kernel(
         const float v = tval[p0 + i];
         const uint32_t w = r >> 5;
         const uint32_t rank = pre[w] + __popc(bm[w] & ((1u << (r & 31)) - 1u));
-        orow[p0 + rank] = (uint16_t)r;
-        oval[p0 + rank] = v;
+        post[p0 + rank] = make_uint2(r, __float_as_uint(v));
       }
       __syncthreads();
     }
@@ -475,8 +469,8 @@ __global__ __launch_bounds__(1024) void heavy_select_kernel(const int32_t *__res
 __global__ __launch_bounds__(256) void slab_scatter_kernel(
     int64_t dim, int32_t pitch, const int32_t *__restrict__ flags,
     const int32_t *__restrict__ heavy, const int32_t *__restrict__ col_ptr,
-    const int32_t *__restrict__ slice_base, const uint16_t *__restrict__ row,
-    const float *__restrict__ val, float *__restrict__ slab) {
+    const int32_t *__restrict__ slice_base, const uint2 *__restrict__ post,
+    float *__restrict__ slab) {
   const int64_t c = blockIdx.x / kHeavyMax;
   const int h = blockIdx.x % kHeavyMax;
   if (flags[0] != 0 || h >= heavy[kHeavyMax]) return;
@@ -486,8 +480,8 @@ __global__ __launch_bounds__(256) void slab_scatter_kernel(
   const int32_t b = cp[d], e = cp[d + 1];
   float *srow = slab + (c * kHeavyMax + h) * (int64_t)pitch;
   for (int32_t k = b + threadIdx.x; k < e; k += 256) {
-    const uint32_t j = row[base + k];
-    if (j < (uint32_t)pitch) srow[j] = val[base + k];
+    const uint2 pe = post[base + k];
+    if (pe.x < (uint32_t)pitch) srow[pe.x] = __uint_as_float(pe.y);
   }
 }
 
@@ -521,7 +515,7 @@ hipError_t launch_prepare_items(const ItemsDev &d, hipStream_t s) {
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(csc_scatter_kernel, dim3(item_blocks), dim3(256), 0, s, g, d.dim, d.indptr,
                      d.indices, d.values, d.norm64, d.flags, d.col_ptr, d.slice_base, d.ticket,
-                     d.row, d.val, d.trow, d.tval);
+                     d.post, d.trow, d.tval);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   int64_t G = 2048 / ns;
   if (G < 4) G = 4;
@@ -529,7 +523,7 @@ hipError_t launch_prepare_items(const ItemsDev &d, hipStream_t s) {
   const size_t lds = 2 * sizeof(uint32_t) * (size_t)((g.S + 31) / 32);
   hipLaunchKernelGGL(csc_fixup_kernel<256>, dim3((unsigned)(G * ns)), dim3(256), lds, s, d.dim,
                      g.S, (int32_t)G, d.flags, d.col_ptr, d.slice_base, d.mlist, d.mcount, d.trow,
-                     d.tval, d.row, d.val);
+                     d.tval, d.post);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (!d.dense) return hipSuccess;
   const int64_t tg64 = (g.n_items + kHeavyFracInv - 1) / kHeavyFracInv;
@@ -541,8 +535,7 @@ hipError_t launch_prepare_items(const ItemsDev &d, hipStream_t s) {
   e = launch_fill_i32(reinterpret_cast<int32_t *>(d.slab), ns * kHeavyMax * (int64_t)pitch, 0, s);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(slab_scatter_kernel, dim3((unsigned)(ns * kHeavyMax)), dim3(256), 0, s,
-                     d.dim, pitch, d.flags, d.heavy, d.col_ptr, d.slice_base, d.row, d.val,
-                     d.slab);
+                     d.dim, pitch, d.flags, d.heavy, d.col_ptr, d.slice_base, d.post, d.slab);
   return hipGetLastError();
 }
 

@@ -6,10 +6,11 @@
 // support divided by both norms), §4.4 (items streamed chunk by chunk),
 // §2.3 (full float32 output, no top-K).
 //
-// One workgroup (512 threads, 8 waves) scores kRows = 8 query rows against
-// one slice (<= 2048 items) of the chunk. LDS holds acc[8][Sp] (Sp = slice
-// rounded up to 128) as 32-bit fixed point with 30 fraction bits: 64 KiB, so
-// two workgroups share a CU and one's stores overlap the other's gathers.
+// One workgroup (512 threads, 8 waves) scores kRows = 16 query rows against
+// one slice (<= 1024 items) of the chunk. LDS holds acc[16][Lp] (Lp = slice
+// rounded up to 128, plus 4 against bank conflicts) as 32-bit fixed point
+// with 30 fraction bits: 64 KiB, so two workgroups share a CU. Workgroups
+// are numbered slice-fastest (see the kernel).
 //
 // Why fixed point: on gfx950 the LDS float atomic (ds_add_f32) sustains about
 // 0.3 updates per CU cycle, the 32-bit integer one (ds_add_u32) about 14.
@@ -18,30 +19,27 @@
 // below 2^30 plus rounding, inside int32. Integer addition is exact and
 // order independent: the result does not depend on how waves interleave.
 //
-// Dense part (heavy dims): v_mfma_f32_4x4x1f32, 16 independent 4x4x1 blocks
-// per instruction (lanes 4b..4b+3 form block b; lane l's result i is
-// A[lane 4(l/4) + i] * B[lane l]). Every lane supplies one item of the
-// slice's dense slab as B and lane m the value of query row m % 4 (or
-// 4 + m % 4) as A, so one B load feeds two MFMAs (rows 0-3, rows 4-7) and
-// lane l accumulates all 8 rows of its items. fp32 products and sums in a
-// fixed order over the dims; the sums, rounded once to fixed point, start
-// the accumulators.
+// Dense part (heavy dims): v_mfma_f32_16x16x4f32 (A[i][k] from lane i + 16k,
+// B[k][j] from lane j + 16k, lane l receiving rows 4(l/16)..+3 of column
+// l%16). A is the 16 rows' values on 4 heavy dims, B 4 dims x 16 items of
+// the slice's dense slab, so each slab value loaded feeds all 16 rows. fp32
+// products and sums in a fixed order over the dims; the sums, rounded once
+// to fixed point, start the accumulators.
 //
-// Sparse part (all other dims): the 8 rows' light entries (dim, value,
-// row) are taken in batches of 512; thread t looks up entry t's posting list
-// [col_ptr[d], col_ptr[d+1]) in the slice. Lists are cut into segments of
-// 16 postings, a block scan numbers the segments and a table in LDS names
-// each one's list, so 16 lanes take one segment with no search: lane i of a
-// segment handles posting 16k + i of its list, loads (item, w) and applies
-// acc[row][item] += rn(fl32(qs * w)) (ds_add_u32), with qs = fl32(q_d / |q|)
-// * 2^30, w = fl32(i_d / |i|) and rn rounding to the nearest integer (ties
-// up). Posting entries are addressed by 32-bit byte offsets from the slice's
-// base (the prepare call keeps nnz below 2^30).
+// Sparse part (all other dims): the 16 rows' light entries (dim, value,
+// row) are taken in batches of 1024, two per thread; each looks up its
+// posting list [col_ptr[d], col_ptr[d+1]) in the slice. Lists are cut into
+// segments of 16 postings, a block scan numbers the segments and an LDS
+// table records each one (first posting, value, row, length), so 16 lanes
+// take one segment with no search: lane i handles posting i of it, loads
+// (item, w) with one 8-byte load and applies acc[row][item] += rn(fl32(qs *
+// w)) (ds_add_u32), with qs = fl32(q_d / |q|) * 2^30, w = fl32(i_d / |i|)
+// and rn rounding to the nearest integer (ties up).
 //
-// Epilogue: wave w writes row w: out[q, j] = fl32(acc) * 2^-30, 16-byte
-// nontemporal stores when aligned (the scores are not re-read, so they
-// should not displace posting lists from L2), and the float64 sum of what it
-// wrote (a per-chunk checksum; slices are folded in a fixed order).
+// Epilogue: wave w writes rows w and w + 8: out[q, j] = fl32(acc) * 2^-30,
+// 16-byte nontemporal stores when aligned (the scores are not re-read, so
+// they should not displace posting lists from L2), and the float64 sum of
+// what it wrote (a per-chunk checksum; slices are folded in a fixed order).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -69,189 +67,235 @@ __device__ __forceinline__ T ld_off(const T *base, uint32_t byte_off) {
 
 constexpr int NT = kScoreThreads;
 constexpr int NW = NT / 64;
-static_assert(NW == kRows, "one wave per query row in the epilogue");
-static_assert(kRows == 8, "the dense part maps two 4-row MFMA blocks");
-static_assert(kSliceMax <= NW * 256, "256 items per wave cover a slice");
-static_assert(kRows * kHeavyMax / 4 <= NT, "one float4 of heavy query values per thread");
+constexpr int kBatch = 2 * NT;  // light entries per batch, two per thread
+static_assert(kRows == 16, "the dense part maps one 16-row MFMA block");
+static_assert(kRows % NW == 0, "whole rows per wave in the epilogue");
+static_assert(kSliceMax <= NW * 128, "128 items per wave cover a slice");
+static_assert(kRows * kHeavyMax <= NT, "one heavy query value per thread");
 // Sparse part: posting lists are cut into segments of kSeg entries, one per
-// 16 lanes; a segment is named by (list, index) in 16 bits.
+// 16 lanes, described in an LDS table.
 constexpr int kSeg = 16;
-constexpr int kSegMax = 2048;  // segments per round (LDS table)
-static_assert(NT * ((kSliceMax + kSeg - 1) / kSeg) <= 65536, "segment names fit 16 bits");
-static_assert((kSliceMax + kSeg - 1) / kSeg <= 128, "segment index fits 7 bits");
+constexpr int kSegMax = 896;         // segments per round
+constexpr int kSegPad = 4 * NW * 4;  // one step of quads past the end (U <= 4)
+static_assert(kRows * kSliceMax * 4 < (1 << 27), "row byte offset fits the segment record");
 
 template <bool DENSE, int U>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void score_kernel(
     const ScoreArgs a, int vec4) {
+  static_assert(U <= 4, "the segment table pads one step of at most 4 quads per wave");
   extern __shared__ int acc[];
-  __shared__ int4 s_rec[NT];          // per batch entry: posting start, length, row offset, value
-  __shared__ uint16_t s_seg[kSegMax];  // segment table of a round
+  // segment table of a round: first posting, query value, and the LDS byte
+  // offset of the row << 5 | postings in the segment (1..16; 0 pads the
+  // table past its last segment)
+  __shared__ uint32_t s_spos[kSegMax + kSegPad], s_sqv[kSegMax + kSegPad],
+      s_smeta[kSegMax + kSegPad];
   __shared__ int32_t ws[NW];
-  __shared__ __align__(16) float s_qh[DENSE ? kRows * kHeavyMax : 4];  // the rows' heavy values
+  // the rows' heavy values, row pitch kHeavyMax + 1 (conflict-free column reads)
+  __shared__ float s_qh[DENSE ? kRows * (kHeavyMax + 1) : 1];
 
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
-  const int64_t grp = blockIdx.x;
-  const int ks = blockIdx.y;
   const Geom &g = a.g;
+  // Slice-fastest order: consecutive workgroups take the slices of one row
+  // group, and workgroups are dealt to the 8 XCDs in turn, so with n_sub
+  // dividing 8 each XCD keeps to the same slice of the chunk (its posting
+  // lists and slab stay in that XCD's L2) while the rows written at any
+  // time span whole output rows.
+  const int64_t grp = blockIdx.x / g.n_sub;
+  const int ks = (int)(blockIdx.x % g.n_sub);
   const int64_t sl = (int64_t)a.chunk * g.n_sub + ks;
   const int64_t ib = g.slice_begin(sl);
   const int32_t slen = (int32_t)(g.slice_end(sl) - ib);
-  const int32_t Sp = slab_pitch(g.S);
+  const int32_t Sp = slab_pitch(g.S);  // slab row pitch (items)
+  const int32_t Lp = acc_pitch(g.S);   // accumulator row pitch (ints)
   const int64_t q0 = grp * kRows;
   const int64_t qe = q0 + kRows < a.n_q ? q0 + kRows : a.n_q;
 
-  // First batch of light entries (see the sparse part): descriptors are
-  // fetched before the dense part so that their two dependent loads (entry,
-  // then posting range) overlap it.
+  // Batch descriptors (see the sparse part), two entries per thread: fetched
+  // before the dense part so that their two dependent loads (entry, then
+  // posting range) overlap it.
   const int32_t *cps = a.col_ptr + sl * (a.dim + 1);
   const int32_t cb0 = a.slice_base[sl];
   const int32_t snnz = a.slice_base[sl + 1] - cb0 > 0 ? a.slice_base[sl + 1] - cb0 : 0;
   const int32_t e0 = a.lptr[q0], e1 = a.lptr[qe];
-  int32_t b_s = 0, b_L = 0, b_row = 0;
-  float b_qv = 0.f;
+  int32_t b_s[2], b_L[2], b_row[2];
+  float b_qv[2];
   auto fetch = [&](int32_t eb) {
-    b_s = 0;
-    b_L = 0;
-    if (eb + t < e1) {
-      const int32_t d = a.ldim[eb + t];
-      b_qv = a.lval[eb + t];
-      b_row = (int32_t)(a.lrow[eb + t] & (kRows - 1)) * Sp;
-      if ((uint32_t)d < (uint64_t)a.dim) {
-        const int32_t lo = cps[d], hi = cps[d + 1];
-        b_s = (int32_t)clamp64(lo, 0, snnz);
-        b_L = (int32_t)clamp64(hi, b_s, snnz) - b_s;
-        b_L = b_L < kSliceMax ? b_L : kSliceMax;  // a slice holds a dim at most once per item
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int32_t e = eb + t + i * NT;
+      b_s[i] = 0;
+      b_L[i] = 0;
+      b_row[i] = 0;
+      b_qv[i] = 0.f;
+      if (e < e1) {
+        const int32_t d = a.ldim[e];
+        b_qv[i] = a.lval[e];
+        b_row[i] = a.lrow[e] & (kRows - 1);
+        if ((uint32_t)d < (uint64_t)a.dim) {
+          const int32_t lo = cps[d], hi = cps[d + 1];
+          b_s[i] = (int32_t)clamp64(lo, 0, snnz);
+          const int32_t L = (int32_t)clamp64(hi, b_s[i], snnz) - b_s[i];
+          b_L[i] = L < kSliceMax ? L : kSliceMax;  // a slice holds a dim once per item
+        }
       }
     }
   };
   fetch(e0);
 
   // ---- dense part: heavy dims on the matrix cores ----
-  // Wave w owns items [256 w, 256 w + 256) of the slice, 4 per lane. Dims are
-  // taken 4 at a time, the next 4 loaded while the current ones are
-  // multiplied. qh and the slab hold zeros from the last heavy dim up to
-  // kHeavyMax, so rounding the dim count up to 8 only adds exact zeros. The
-  // sums, rounded to fixed point, are the accumulators' initial values.
-  const int32_t wcol = wv * 256;
+  // Wave w owns items [128 w, 128 w + 128) of the slice as two 64-item
+  // groups. Dims are taken 8 at a time (two MFMA k-steps), the next 8 loaded
+  // while the current ones are multiplied. qh and the slab hold zeros from
+  // the last heavy dim up to kHeavyMax, so rounding the dim count up to 16
+  // only adds exact zeros. The sums, rounded to fixed point, are the
+  // accumulators' initial values.
+  const int32_t wcol = wv * 128;
   if (DENSE) {
-    const int mr = (a.heavy[kHeavyMax] + 7) & ~7;
-    const float *sb = a.slab + sl * (int64_t)kHeavyMax * a.pitch + (wcol < Sp ? wcol : 0) + 4 * lane;
-    f32x4 sv[2][4];
+    const int mr = (a.heavy[kHeavyMax] + 15) & ~15;
+    // B: lane l loads items 4(l%16)..+3 of a group on dim h + l/16
+    const float *sb = a.slab + sl * (int64_t)kHeavyMax * a.pitch + (wcol < Sp ? wcol : 0) +
+                      4 * (lane & 15) + (int64_t)(lane >> 4) * a.pitch;
+    f32x4 sv[2][2][2];  // [buffer][k-step][group]
     auto load = [&](int b, int h0) {
 #pragma unroll
-      for (int p = 0; p < 4; ++p)
-        sv[b][p] = *reinterpret_cast<const f32x4 *>(sb + (int64_t)(h0 + p) * a.pitch);
+      for (int k = 0; k < 2; ++k)
+#pragma unroll
+        for (int gi = 0; gi < 2; ++gi)
+          sv[b][k][gi] =
+              *reinterpret_cast<const f32x4 *>(sb + (int64_t)(h0 + 4 * k) * a.pitch + 64 * gi);
     };
     if (mr > 0) load(0, 0);
-    if (t < kRows * kHeavyMax / 4)
-      reinterpret_cast<f32x4 *>(s_qh)[t] =
-          reinterpret_cast<const f32x4 *>(a.qh + grp * (kRows * kHeavyMax))[t];
+    if (t < kRows * kHeavyMax)
+      s_qh[(t / kHeavyMax) * (kHeavyMax + 1) + t % kHeavyMax] = a.qh[grp * (kRows * kHeavyMax) + t];
     __syncthreads();
     f32x4 dacc[2][4];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int gi = 0; gi < 2; ++gi)
 #pragma unroll
-      for (int u = 0; u < 4; ++u) dacc[i][u] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // A operands: lane m supplies query row m % 4 (block 0) and 4 + m % 4
-    // (block 1), four dims per LDS read.
-    const float *qa = s_qh + (lane & 3) * kHeavyMax;
+      for (int u = 0; u < 4; ++u) dacc[gi][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // A: lane l supplies row l%16 on dim h + l/16
+    const float *qa = s_qh + (lane & 15) * (kHeavyMax + 1) + (lane >> 4);
     auto mma = [&](int b, int h0) {
-      const f32x4 alo = *reinterpret_cast<const f32x4 *>(qa + h0);
-      const f32x4 ahi = *reinterpret_cast<const f32x4 *>(qa + 4 * kHeavyMax + h0);
 #pragma unroll
-      for (int p = 0; p < 4; ++p)
+      for (int k = 0; k < 2; ++k) {
+        const float av = qa[h0 + 4 * k];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          dacc[0][u] = __builtin_amdgcn_mfma_f32_4x4x1f32(alo[p], sv[b][p][u], dacc[0][u], 0, 0, 0);
-          dacc[1][u] = __builtin_amdgcn_mfma_f32_4x4x1f32(ahi[p], sv[b][p][u], dacc[1][u], 0, 0, 0);
-        }
+        for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            dacc[gi][u] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, sv[b][k][gi][u], dacc[gi][u], 0, 0, 0);
+      }
     };
     if (wcol < Sp) {
-      for (int h0 = 0; h0 < mr; h0 += 8) {
-        load(1, h0 + 4);
+      for (int h0 = 0; h0 < mr; h0 += 16) {
+        load(1, h0 + 8);
         mma(0, h0);
-        if (h0 + 8 < mr) load(0, h0 + 8);
-        mma(1, h0 + 4);
+        if (h0 + 16 < mr) load(0, h0 + 16);
+        mma(1, h0 + 8);
       }
-      // lane l holds rows 4b + i of items 4l + u in dacc[b][u][i]
+      // lane l holds rows 4(l/16) + i of items 64 gi + 4(l%16) + u in dacc[gi][u][i]
 #pragma unroll
-      for (int r = 0; r < kRows; ++r) {
-        const int b = r >> 2, i = r & 3;
-        reinterpret_cast<int4 *>(acc + r * Sp + wcol)[lane] =
-            make_int4(round_fix(dacc[b][0][i] * kFixScale), round_fix(dacc[b][1][i] * kFixScale),
-                      round_fix(dacc[b][2][i] * kFixScale), round_fix(dacc[b][3][i] * kFixScale));
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * (lane >> 4) + i;
+#pragma unroll
+        for (int gi = 0; gi < 2; ++gi)
+          *reinterpret_cast<int4 *>(acc + r * Lp + wcol + 64 * gi + 4 * (lane & 15)) =
+              make_int4(round_fix(dacc[gi][0][i] * kFixScale), round_fix(dacc[gi][1][i] * kFixScale),
+                        round_fix(dacc[gi][2][i] * kFixScale), round_fix(dacc[gi][3][i] * kFixScale));
       }
     }
   } else {
     int4 *acc4 = reinterpret_cast<int4 *>(acc);
-    for (int k = t; k < kRows * Sp / 4; k += NT) acc4[k] = make_int4(0, 0, 0, 0);
+    for (int k = t; k < kRows * Lp / 4; k += NT) acc4[k] = make_int4(0, 0, 0, 0);
   }
   __syncthreads();  // accumulators initialised before any sparse update
 
   // ---- sparse part: the rows' light entries, batch by batch ----
-  const uint16_t *__restrict__ prow = a.row + cb0;
-  const float *__restrict__ pval = a.val + cb0;
-  for (int32_t eb = e0; eb < e1; eb += NT) {
-    // list record of entry t: posting start, length, LDS row offset, value
-    s_rec[t] = make_int4(b_s, b_L, b_row, __float_as_int(b_qv));
-    const int32_t nseg = (b_L + kSeg - 1) / kSeg;
+  const uint2 *__restrict__ ppost = a.post + cb0;
+  for (int32_t eb = e0; eb < e1; eb += kBatch) {
+    int32_t nseg[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) nseg[i] = (b_L[i] + kSeg - 1) / kSeg;
     int32_t total;
-    const int32_t sp0 = block_incl_scan<NT>(nseg, ws, &total) - nseg;  // barrier inside
-    if (eb + NT < e1) fetch(eb + NT);  // next batch's descriptors, in flight during this one
+    const int32_t pend = block_incl_scan<NT>(nseg[0] + nseg[1], ws, &total);  // barrier inside
+    const int32_t sp[2] = {pend - nseg[0] - nseg[1], pend - nseg[1]};
+    // this batch's lists, kept while the next batch's descriptors load
+    int32_t c_s[2], c_L[2], c_off[2];
+    uint32_t c_qv[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      c_s[i] = b_s[i];
+      c_L[i] = b_L[i];
+      c_off[i] = b_row[i] * Lp;
+      c_qv[i] = __float_as_uint(b_qv[i]);
+    }
+    if (eb + kBatch < e1) fetch(eb + kBatch);  // next batch's descriptors, in flight during this one
     for (int32_t r0 = 0; r0 < total; r0 += kSegMax) {
-      // segment table of the round: list id and segment index within the list
-      const int32_t sb = sp0 > r0 ? sp0 : r0;
-      const int32_t se = sp0 + nseg < r0 + kSegMax ? sp0 + nseg : r0 + kSegMax;
-      for (int32_t sg = sb; sg < se; ++sg) s_seg[sg - r0] = (uint16_t)((t << 7) | (sg - sp0));
-      __syncthreads();
+      // the segments of this round that belong to this thread's lists
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int32_t sb0 = sp[i] > r0 ? sp[i] : r0;
+        const int32_t se = sp[i] + nseg[i] < r0 + kSegMax ? sp[i] + nseg[i] : r0 + kSegMax;
+        for (int32_t sg = sb0; sg < se; ++sg) {
+          const int32_t j0 = (sg - sp[i]) * kSeg;
+          const int32_t n = c_L[i] - j0 < kSeg ? c_L[i] - j0 : kSeg;
+          s_spos[sg - r0] = (uint32_t)(c_s[i] + j0);
+          s_sqv[sg - r0] = c_qv[i];
+          s_smeta[sg - r0] = (uint32_t)n | ((uint32_t)c_off[i] << 7);  // byte offset << 5
+        }
+      }
       const int32_t nr = total - r0 < kSegMax ? total - r0 : kSegMax;
-      // wave w takes segment quads w, w + NW, ...; lanes 16i..16i+15 segment i of a quad
+      if (t < kSegPad) s_smeta[nr + t] = 0u;
+      __syncthreads();
+      // Wave w takes segment quads w, w + NW, ...; lanes 16i..16i+15 take
+      // segment i of a quad, U quads per step.
+      const int32_t jl = lane & 15;
       for (int32_t k0 = wv; 4 * k0 < nr; k0 += NW * U) {
         uint32_t pos[U];
-        int32_t aoff[U];
+        uint32_t aoff[U];
         float qv[U];
         bool ok[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
+          // entries past nr are padding (no postings)
           const int32_t sg = 4 * (k0 + NW * u) + (lane >> 4);
-          const bool in = sg < nr;
-          const uint32_t desc = s_seg[in ? sg : 0];
-          const int4 rec = s_rec[desc >> 7];
-          const int32_t j = (int32_t)(desc & 127) * kSeg + (lane & 15);
-          ok[u] = in && j < rec.y;
-          pos[u] = ok[u] ? (uint32_t)(rec.x + j) : 0u;
-          aoff[u] = rec.z;
-          qv[u] = __int_as_float(rec.w);
+          const uint32_t meta = s_smeta[sg];
+          const uint32_t sp0 = s_spos[sg];
+          ok[u] = jl < (int32_t)(meta & 31u);
+          pos[u] = ok[u] ? sp0 + jl : 0u;
+          aoff[u] = meta >> 5;
+          qv[u] = __uint_as_float(s_sqv[sg]);
         }
-        uint16_t rw[U];
-        float w[U];
+        uint2 pe[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-          rw[u] = ld_off(prow, pos[u] * 2u);
-          w[u] = ld_off(pval, pos[u] * 4u);
-        }
-        // all 2U loads are in flight before the first is waited on (keeps the
+        for (int u = 0; u < U; ++u) pe[u] = ld_off(ppost, pos[u] * 8u);
+        // all U loads are in flight before the first is waited on (keeps the
         // compiler from sinking a load into the masked update below it)
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int u = 0; u < U; ++u) asm volatile("" ::"v"(rw[u]), "v"(w[u]));
+        for (int u = 0; u < U; ++u) asm volatile("" ::"v"(pe[u].x), "v"(pe[u].y));
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-          if (ok[u] && (int32_t)rw[u] < slen)
-            atomicAdd(&acc[aoff[u] + (int)rw[u]], round_fix(qv[u] * w[u]));
+          if (ok[u] && pe[u].x < (uint32_t)slen)
+            atomicAdd(reinterpret_cast<int *>(reinterpret_cast<char *>(acc) + aoff[u] + 4 * pe[u].x),
+                      round_fix(qv[u] * __uint_as_float(pe[u].y)));
         }
       }
       __syncthreads();
     }
   }
 
-  // ---- epilogue: wave w writes row w ----
-  const int64_t q = q0 + wv;
-  if (q < a.n_q) {
-    const int64_t col0 = ib - g.chunk_begin(a.chunk);
+  // ---- epilogue: wave w writes rows w, w + NW, ... ----
+  const int64_t col0 = ib - g.chunk_begin(a.chunk);
+  const bool v4 = vec4 && (col0 % 4 == 0);
+  double *rsum = g.n_sub == 1 ? a.row_sums : a.rs_part;
+#pragma unroll
+  for (int rr = 0; rr < kRows / NW; ++rr) {
+    const int r = wv + NW * rr;
+    const int64_t q = q0 + r;
+    if (q >= a.n_q) break;
     float *orow = a.out + q * a.ld + col0;
-    const bool v4 = vec4 && (col0 % 4 == 0);
-    const int4 *arow = reinterpret_cast<const int4 *>(acc + wv * Sp);
+    const int4 *arow = reinterpret_cast<const int4 *>(acc + r * Lp);
     double rs = 0.0;
     for (int j0 = 4 * lane; j0 < slen; j0 += 256) {
       const int4 x = arow[j0 >> 2];
@@ -269,7 +313,6 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void sc
           }
       }
     }
-    double *rsum = g.n_sub == 1 ? a.row_sums : a.rs_part;
     if (rsum != nullptr) {
       rs = wave_sum(rs);
       if (lane == 0) rsum[(g.n_sub == 1 ? 0 : (int64_t)ks * a.n_q) + q] = rs;
@@ -288,9 +331,8 @@ __global__ void fold_row_sums_kernel(int64_t n_q, int32_t n_sub, const double *_
 }
 
 size_t score_lds_bytes(int32_t S) {
-  const size_t Sp = (size_t)slab_pitch(S);
-  return (size_t)kRows * Sp * sizeof(int) + NT * 16 + kSegMax * 2 + NW * 4 +
-         kRows * kHeavyMax * 4;
+  return (size_t)kRows * acc_pitch(S) * sizeof(int) + (kSegMax + kSegPad) * 12 + NW * 4 +
+         kRows * (kHeavyMax + 1) * 4;
 }
 
 static int env_unroll() {
@@ -299,7 +341,7 @@ static int env_unroll() {
     v = 4;
     if (const char *e = getenv("SPS_SCORE_UNROLL")) {
       const int x = atoi(e);
-      if (x == 2 || x == 4 || x == 8) v = x;
+      if (x == 2 || x == 4) v = x;
     }
   }
   return v;
@@ -307,8 +349,7 @@ static int env_unroll() {
 
 template <bool DENSE, int U>
 static hipError_t launch_t(const ScoreArgs &a, hipStream_t s) {
-  const int32_t Sp = slab_pitch(a.g.S);
-  const size_t dyn = (size_t)kRows * Sp * sizeof(int);
+  const size_t dyn = (size_t)kRows * acc_pitch(a.g.S) * sizeof(int);
   auto kern = score_kernel<DENSE, U>;
   // dynamic LDS above 64 KiB needs an explicit opt-in per kernel
   static size_t opted = 65536;
@@ -319,7 +360,7 @@ static hipError_t launch_t(const ScoreArgs &a, hipStream_t s) {
     opted = dyn;
   }
   const int vec4 = (a.ld % 4 == 0) && ((reinterpret_cast<uintptr_t>(a.out) & 15) == 0);
-  hipLaunchKernelGGL(kern, dim3((unsigned)a.n_groups, (unsigned)a.g.n_sub), dim3(NT), dyn, s, a,
+  hipLaunchKernelGGL(kern, dim3((unsigned)((int64_t)a.n_groups * a.g.n_sub)), dim3(NT), dyn, s, a,
                      vec4);
   return hipGetLastError();
 }
@@ -329,10 +370,9 @@ hipError_t launch_score(const ScoreArgs &a, hipStream_t s) {
   const int u = env_unroll();
   hipError_t e;
   if (a.dense) {
-    e = u == 8 ? launch_t<true, 8>(a, s) : (u == 2 ? launch_t<true, 2>(a, s) : launch_t<true, 4>(a, s));
+    e = u == 2 ? launch_t<true, 2>(a, s) : launch_t<true, 4>(a, s);
   } else {
-    e = u == 8 ? launch_t<false, 8>(a, s)
-               : (u == 2 ? launch_t<false, 2>(a, s) : launch_t<false, 4>(a, s));
+    e = u == 2 ? launch_t<false, 2>(a, s) : launch_t<false, 4>(a, s);
   }
   if (e != hipSuccess) return e;
   if (a.row_sums != nullptr && a.g.n_sub > 1) {

@@ -16,6 +16,7 @@ import synth
 pytestmark = pytest.mark.gpu
 
 TOL = 1e-5
+SLICE_MAX = 1024  # items per slice at most (the prepare call's slice rule)
 
 
 @pytest.fixture(scope="module")
@@ -61,7 +62,7 @@ def _check_structures(env, orc, items, chunk_size, name):
     torch, sps, dev = env
     n64, inv32 = orc.row_norms(items)
     it = sps.prepare(sps.CSR.from_host(items, dev), chunk_size=chunk_size)
-    assert it.slices_per_chunk == -(-chunk_size // 2048)
+    assert it.slices_per_chunk == -(-chunk_size // SLICE_MAX)
     for sl in range(it.num_slices):
         v = it.slice_view(sl)
         b = v["item_begin"]
@@ -69,9 +70,10 @@ def _check_structures(env, orc, items, chunk_size, name):
         col_ptr, row, val = orc.chunk_csc(items, n64, b, e)
         assert v["slice_nnz"] == len(row), (name, sl)
         assert np.array_equal(v["col_ptr"].cpu().numpy(), col_ptr), (name, sl, "col_ptr")
-        g_row = v["row"].cpu().numpy().view(np.uint16).astype(np.int32)
+        post = v["post"].cpu().numpy()
+        g_row = post[:, 0]
         assert np.array_equal(g_row, row), (name, sl, "row ids")
-        g_val = v["val"].cpu().numpy()
+        g_val = post[:, 1].copy().view(np.float32)
         assert np.array_equal(g_val.view(np.uint32), val.view(np.uint32)), (name, sl, "values")
         g_inv = v["item_inv_norm"].cpu().numpy()
         assert np.array_equal(g_inv.view(np.uint32), inv32[b:e].view(np.uint32)), (name, sl)
@@ -307,7 +309,7 @@ def test_chunk_size_extremes(env, orc):
         err = float(np.abs(got - ref).max())
         report("tiny 50x1500 chunk %d" % cs, err, got.size)
         assert err <= TOL
-    # chunks cut into uneven slices (ceil(C/2048) slices, last one shorter)
+    # chunks cut into uneven slices (ceil(C/1024) slices, last one shorter)
     q, items, _ = synth.make_workload("mid", n_item=9001, n_query=21)
     ref = orc.scores(q, items)
     for cs in (2049, 3000, 4097, 6000):
