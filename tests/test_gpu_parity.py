@@ -29,8 +29,9 @@ def env():
     return torch, sps, torch.device("cuda:0")
 
 
-def report(name, err, n):
-    line = "[parity] %-44s n=%-11d max|err|=%.3g (bar 1e-5; page goal 1e-6)" % (name, n, err)
+def report(name, err, n, bar=TOL):
+    line = "[parity] %-44s n=%-11d max|err|=%.3g (bar %.3g; page goal 1e-6 per score)" % (
+        name, n, err, bar)
     print("\n" + line, file=sys.stderr, flush=True)
     path = os.environ.get("SPS_PARITY_LOG")
     if path:
@@ -190,7 +191,7 @@ def _sampled(env, orc, name, n_rows_sampled, self_scores=False):
     # each row sum adds at most chunk_len fp32 errors of the scores
     report("%s %d sampled rows x all items" % (name, len(rows)), worst, n)
     report("%s row sums, %d chunks x %d rows" % (name, it.num_chunks, q.n_rows), worst_sum,
-           it.num_chunks * q.n_rows)
+           it.num_chunks * q.n_rows, bar=TOL * w.chunk_size)
     assert worst <= TOL
     assert worst_sum <= TOL * w.chunk_size
     if self_scores:
