@@ -101,7 +101,7 @@ ItemsLayout items_layout(const sps::Geom &g, int64_t dim, int64_t nnz, bool dens
   L.post = p.add(nnz, 8);
   L.sbase = p.add(ns + 1, 4);
   L.heavy = p.add(sps::kHeavyMax + 1, 4);
-  L.slab = p.add(dense ? (uint64_t)ns * sps::kHeavyMax * (uint64_t)sps::slab_pitch(g.S) : 0, 4);
+  L.slab = p.add(dense ? (uint64_t)ns * sps::kHeavyRec * (uint64_t)sps::slab_pitch(g.S) : 0, 2);
   L.persistent = p.off;
   Layout s;
   L.flags = s.add(sps::kFlagsInts, 4);
@@ -130,10 +130,12 @@ QueriesLayout queries_layout(int64_t n, int64_t nnz, int32_t n_sub, bool dense) 
   L.inv = p.add(n, 4);
   L.norm64 = p.add(n, 8);
   L.lptr = p.add(n + 1, 4);
-  L.ldim = p.add(nnz, 4);
-  L.lval = p.add(nnz, 4);
-  L.lrow = p.add(nnz, 1);
-  L.qh = p.add(dense ? (uint64_t)ng * sps::kHeavyMax * sps::kRows : 0, 4);
+  // at least one light entry each: the score kernel may read entry 0 of an
+  // empty batch (and ignores it)
+  L.ldim = p.add(nnz > 0 ? nnz : 1, 4);
+  L.lval = p.add(nnz > 0 ? nnz : 1, 4);
+  L.lrow = p.add(nnz > 0 ? nnz : 1, 1);
+  L.qh = p.add(dense ? (uint64_t)ng * sps::kHeavyRec * sps::kRows : 0, 2);
   L.rspart = p.add(n_sub > 1 ? (uint64_t)n_sub * (uint64_t)n : 0, 8);
   L.total = p.off;
   L.overflow = p.overflow;
@@ -153,7 +155,7 @@ struct sps_items {
   uint2 *post;
   int32_t *slice_base;
   int32_t *heavy;
-  float *slab;
+  uint16_t *slab;
 };
 
 struct sps_queries {
@@ -166,7 +168,7 @@ struct sps_queries {
   int32_t *lptr, *ldim;
   float *lval;
   uint8_t *lrow;
-  float *qh;
+  uint16_t *qh;
   double *rs_part;
 };
 
@@ -248,7 +250,7 @@ sps_status sps_prepare(const sps_csr *items, int32_t chunk_size, void *persisten
   d.post = at<uint2>(persistent, L.post);
   d.slice_base = at<int32_t>(persistent, L.sbase);
   d.heavy = at<int32_t>(persistent, L.heavy);
-  d.slab = dense ? at<float>(persistent, L.slab) : nullptr;
+  d.slab = dense ? at<uint16_t>(persistent, L.slab) : nullptr;
   d.flags = at<int32_t>(scratch, L.flags);
   d.norm64 = at<double>(scratch, L.norm64);
   d.ticket = at<int32_t>(scratch, L.ticket);
@@ -390,7 +392,7 @@ sps_status sps_prepare_queries(const sps_csr *queries, const sps_items *items, v
   d.ldim = at<int32_t>(workspace, L.ldim);
   d.lval = at<float>(workspace, L.lval);
   d.lrow = at<uint8_t>(workspace, L.lrow);
-  d.qh = dense ? at<float>(workspace, L.qh) : nullptr;
+  d.qh = dense ? at<uint16_t>(workspace, L.qh) : nullptr;
   sps_queries *h = new (std::nothrow) sps_queries;
   if (!h) return fail(SPS_ERR_INVALID_ARGUMENT, "out of host memory");
   hipError_t e = sps::launch_prepare_queries(d, reinterpret_cast<hipStream_t>(stream));

@@ -70,8 +70,32 @@ inline Geom make_geom(int64_t n_items, int32_t chunk_size) {
   g.num_chunks = (int32_t)((n_items + chunk_size - 1) / chunk_size);
   return g;
 }
-// Row pitch (items) of a slice's dense slab: a whole number of 128-item
-// groups (one wave's share in the dense part).
+// Heavy-dim values are kept as split fp16 pairs for the matrix cores: with
+// X = 256 x (exact), hi = fp16(X) and lo = fp16((X - hi) * 2048), so that
+// X = hi + lo / 2048 up to 2^-22 |X|. Items (and query rows) are stored in
+// tiles of 16: a tile is kTileHalves halves, the hi part then the lo part,
+// each [dim block of 8][item of the tile][8 dims] -- exactly the per-lane
+// operand order of v_mfma_f32_16x16x32_f16 (lane l = item l%16, dim block
+// l/16), so one 16-byte load per lane reads 1 KiB of contiguous memory.
+// Dims past the heavy count are zero.
+constexpr int kHeavyRec = 2 * kHeavyMax;   // halves per item
+constexpr int kTileHalves = 16 * kHeavyRec;
+constexpr float kHeavyScale = 256.0f;  // X = x * 256
+constexpr float kLoScale = 2048.0f;    // lo = (X - hi) * 2048
+// position of (item j, heavy dim h, part 0 hi / 1 lo) from its tile's start
+__host__ __device__ inline int heavy_tile_index(int j, int h, int part) {
+  return part * (16 * kHeavyMax) + (h >> 3) * 128 + (j & 15) * 8 + (h & 7);
+}
+__device__ inline void split_fp16(float x, uint16_t &hi, uint16_t &lo) {
+  const float X = x * kHeavyScale;
+  const _Float16 h = (_Float16)X;
+  const _Float16 l = (_Float16)((X - (float)h) * kLoScale);
+  hi = __builtin_bit_cast(uint16_t, h);
+  lo = __builtin_bit_cast(uint16_t, l);
+}
+
+// Item pitch of a slice's heavy-dim slab: a whole number of 128-item groups
+// (one wave's share in the dense part).
 __host__ __device__ inline int32_t slab_pitch(int32_t S) { return (S + 127) / 128 * 128; }
 // Row pitch (ints) of the score kernel's LDS accumulators: the slab pitch
 // plus 4, so that rows start 16 bytes apart modulo the LDS bank period.
@@ -99,7 +123,7 @@ struct ItemsDev {
   uint2 *post;          // persistent, nnz: (slice-local item id, value bits)
   int32_t *slice_base;  // persistent, num_slices + 1
   int32_t *heavy;       // persistent, kHeavyMax + 1: heavy dims ascending, then their count
-  float *slab;          // persistent, num_slices * kHeavyMax * pitch (dense only)
+  uint16_t *slab;       // persistent, [num_slices][pitch / 16 tiles] split fp16 (dense only)
   int32_t *flags;       // scratch
   double *norm64;       // scratch, n_items
   int32_t *ticket;      // scratch, nnz
@@ -126,7 +150,7 @@ struct QueriesDev {
   int32_t *ldim;         // nnz
   float *lval;           // nnz: fl32(q / |q|) * 2^30
   uint8_t *lrow;         // nnz: row within its group of kRows
-  float *qh;             // [n_groups * kRows][kHeavyMax]: fl32(q / |q|) on heavy dims
+  uint16_t *qh;          // [n_groups] tiles of split fp16: fl32(q / |q|) on heavy dims
 };
 hipError_t launch_prepare_queries(const QueriesDev &d, hipStream_t s);
 
@@ -140,12 +164,12 @@ struct ScoreArgs {
   const int32_t *lptr, *ldim;
   const float *lval;
   const uint8_t *lrow;
-  const float *qh;
+  const uint16_t *qh;         // [row groups] tiles of split fp16 (dense only)
   const int32_t *col_ptr;     // all slices
   const uint2 *post;          // all slices: (slice-local item id, value bits)
   const int32_t *slice_base;
   const int32_t *heavy;
-  const float *slab;          // all slices (dense only)
+  const uint16_t *slab;       // [slices][pitch / 16] tiles of split fp16 (dense only)
   int32_t pitch;
   float *out;
   int64_t ld;

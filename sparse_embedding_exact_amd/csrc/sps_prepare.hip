@@ -465,12 +465,12 @@ __global__ __launch_bounds__(1024) void heavy_select_kernel(const int32_t *__res
   if (t == 0) heavy[kHeavyMax] = n < cap ? n : cap;
 }
 
-// slab[s][h][j] = value of item j of slice s on heavy dim h (slab pre-zeroed)
+// slab of slice s: item j's split-fp16 heavy values in its tile (pre-zeroed)
 __global__ __launch_bounds__(256) void slab_scatter_kernel(
     int64_t dim, int32_t pitch, const int32_t *__restrict__ flags,
     const int32_t *__restrict__ heavy, const int32_t *__restrict__ col_ptr,
     const int32_t *__restrict__ slice_base, const uint2 *__restrict__ post,
-    float *__restrict__ slab) {
+    uint16_t *__restrict__ slab) {
   const int64_t c = blockIdx.x / kHeavyMax;
   const int h = blockIdx.x % kHeavyMax;
   if (flags[0] != 0 || h >= heavy[kHeavyMax]) return;
@@ -478,10 +478,16 @@ __global__ __launch_bounds__(256) void slab_scatter_kernel(
   const int32_t *cp = col_ptr + c * (dim + 1);
   const int64_t base = slice_base[c];
   const int32_t b = cp[d], e = cp[d + 1];
-  float *srow = slab + (c * kHeavyMax + h) * (int64_t)pitch;
+  uint16_t *sl = slab + c * (int64_t)pitch * kHeavyRec;
   for (int32_t k = b + threadIdx.x; k < e; k += 256) {
     const uint2 pe = post[base + k];
-    if (pe.x < (uint32_t)pitch) srow[pe.x] = __uint_as_float(pe.y);
+    if (pe.x < (uint32_t)pitch) {
+      uint16_t hi, lo;
+      split_fp16(__uint_as_float(pe.y), hi, lo);
+      uint16_t *tile = sl + (int64_t)(pe.x >> 4) * kTileHalves;
+      tile[heavy_tile_index(pe.x, h, 0)] = hi;
+      tile[heavy_tile_index(pe.x, h, 1)] = lo;
+    }
   }
 }
 
@@ -532,7 +538,7 @@ hipError_t launch_prepare_items(const ItemsDev &d, hipStream_t s) {
                      d.flags, d.heavy);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int32_t pitch = slab_pitch(g.S);
-  e = launch_fill_i32(reinterpret_cast<int32_t *>(d.slab), ns * kHeavyMax * (int64_t)pitch, 0, s);
+  e = launch_fill_i32(reinterpret_cast<int32_t *>(d.slab), ns * (int64_t)pitch * kHeavyRec / 2, 0, s);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(slab_scatter_kernel, dim3((unsigned)(ns * kHeavyMax)), dim3(256), 0, s,
                      d.dim, pitch, d.flags, d.heavy, d.col_ptr, d.slice_base, d.post, d.slab);
@@ -541,8 +547,9 @@ hipError_t launch_prepare_items(const ItemsDev &d, hipStream_t s) {
 
 // ---------------------------------------------------------------------------
 // Queries. Each row is normalised by its float64 norm (§5.2) and rounded
-// once to fp32: qn = fl32(q_d / |q|). Heavy dims (dense path) go to
-// qh[row][h] (rows padded to a multiple of kRows); the other entries form the
+// once to fp32: qn = fl32(q_d / |q|). Heavy dims (dense path) go to the
+// row's split-fp16 record in qh (rows padded to a multiple of kRows); the
+// other entries form the
 // "light" CSR (same row order) with values qn * 2^30 (exact: a power of two),
 // the scale of the fixed-point accumulators, and the row's position in its
 // group.
@@ -554,7 +561,7 @@ __global__ __launch_bounds__(256) void light_split_kernel(
     const float *__restrict__ values, const double *__restrict__ norm64,
     const int32_t *__restrict__ flags, const int32_t *__restrict__ heavy,
     int32_t *__restrict__ lptr, int32_t *__restrict__ ldim, float *__restrict__ lval,
-    uint8_t *__restrict__ lrow, float *__restrict__ qh) {
+    uint8_t *__restrict__ lrow, uint16_t *__restrict__ qh) {
   const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (q >= n_rows) return;
   const int m = heavy != nullptr ? heavy[kHeavyMax] : 0;
@@ -573,7 +580,11 @@ __global__ __launch_bounds__(256) void light_split_kernel(
     if (FILL) {
       const float v = (n > 0.0) ? (float)((double)values[k] / n) : 0.0f;
       if (hs >= 0) {
-        qh[q * kHeavyMax + hs] = v;
+        uint16_t hi, lo;
+        split_fp16(v, hi, lo);
+        uint16_t *tile = qh + (q / kRows) * kTileHalves;
+        tile[heavy_tile_index((int)(q % kRows), hs, 0)] = hi;
+        tile[heavy_tile_index((int)(q % kRows), hs, 1)] = lo;
       } else {
         ldim[out] = d;
         lval[out] = v * kFixScale;
@@ -599,7 +610,7 @@ hipError_t launch_prepare_queries(const QueriesDev &d, hipStream_t s) {
   if (d.n_rows == 0) return hipSuccess;
   if (d.dense) {
     e = launch_fill_i32(reinterpret_cast<int32_t *>(d.qh),
-                        (int64_t)d.n_groups * kHeavyMax * kRows, 0, s);
+                        (int64_t)d.n_groups * kRows * kHeavyRec / 2, 0, s);
     if (e != hipSuccess) return e;
   }
   const int32_t *heavy = d.dense ? d.heavy : nullptr;

@@ -50,6 +50,10 @@
 namespace sps {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h16x8 __attribute__((ext_vector_type(8)));
+
+// dense sums are of values scaled by kHeavyScale on both sides
+constexpr float kDenseToFix = kFixScale / (kHeavyScale * kHeavyScale);  // 2^14
 
 // x rounded to the nearest integer, ties upward: floor(x + 0.5) in one
 // instruction (|x| <= 2^30 here, so no saturation).
@@ -68,10 +72,9 @@ __device__ __forceinline__ T ld_off(const T *base, uint32_t byte_off) {
 constexpr int NT = kScoreThreads;
 constexpr int NW = NT / 64;
 constexpr int kBatch = 2 * NT;  // light entries per batch, two per thread
-static_assert(kRows == 16, "the dense part maps one 16-row MFMA block");
 static_assert(kRows % NW == 0, "whole rows per wave in the epilogue");
 static_assert(kSliceMax <= NW * 128, "128 items per wave cover a slice");
-static_assert(kRows * kHeavyMax <= NT, "one heavy query value per thread");
+static_assert(kRows == 16 && kHeavyMax == 32, "one 16x16x32 MFMA tile covers the rows and heavy dims");
 // Sparse part: posting lists are cut into segments of kSeg entries, one per
 // 16 lanes, described in an LDS table.
 constexpr int kSeg = 16;
@@ -90,8 +93,6 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void sc
   __shared__ uint32_t s_spos[kSegMax + kSegPad], s_sqv[kSegMax + kSegPad],
       s_smeta[kSegMax + kSegPad];
   __shared__ int32_t ws[NW];
-  // the rows' heavy values, row pitch kHeavyMax + 1 (conflict-free column reads)
-  __shared__ float s_qh[DENSE ? kRows * (kHeavyMax + 1) : 1];
 
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const Geom &g = a.g;
@@ -119,95 +120,99 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void sc
   const int32_t e0 = a.lptr[q0], e1 = a.lptr[qe];
   int32_t b_s[2], b_L[2], b_row[2];
   float b_qv[2];
-  auto fetch = [&](int32_t eb) {
+  // Three stages, so that other loads can be issued between them and no
+  // arithmetic on a loaded value forces an early wait: entry loads (raw),
+  // then the dependent posting-range loads (raw), then the range arithmetic.
+  int32_t r_d[2], r_lo[2], r_hi[2];
+  uint32_t r_qv[2], r_row[2];
+  bool r_ok[2];
+  auto fetch_entries = [&](int32_t eb) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int32_t e = eb + t + i * NT;
-      b_s[i] = 0;
-      b_L[i] = 0;
-      b_row[i] = 0;
-      b_qv[i] = 0.f;
-      if (e < e1) {
-        const int32_t d = a.ldim[e];
-        b_qv[i] = a.lval[e];
-        b_row[i] = a.lrow[e] & (kRows - 1);
-        if ((uint32_t)d < (uint64_t)a.dim) {
-          const int32_t lo = cps[d], hi = cps[d + 1];
-          b_s[i] = (int32_t)clamp64(lo, 0, snnz);
-          const int32_t L = (int32_t)clamp64(hi, b_s[i], snnz) - b_s[i];
-          b_L[i] = L < kSliceMax ? L : kSliceMax;  // a slice holds a dim once per item
-        }
-      }
+      r_ok[i] = e < e1;
+      // a readable entry (the light arrays hold at least one) when e is past the end
+      const int32_t ec = e < e1 ? e : (e1 > 0 ? e1 - 1 : 0);
+      r_d[i] = a.ldim[ec];
+      r_qv[i] = __float_as_uint(a.lval[ec]);
+      r_row[i] = a.lrow[ec];
     }
   };
-  fetch(e0);
+  auto fetch_ranges = [&]() {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int32_t d = (uint32_t)r_d[i] < (uint64_t)a.dim ? r_d[i] : 0;
+      r_lo[i] = cps[d];
+      r_hi[i] = cps[d + 1];
+    }
+  };
+  auto finish_ranges = [&]() {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const bool ok = r_ok[i] && (uint32_t)r_d[i] < (uint64_t)a.dim;
+      b_s[i] = ok ? (int32_t)clamp64(r_lo[i], 0, snnz) : 0;
+      const int32_t L = ok ? (int32_t)clamp64(r_hi[i], b_s[i], snnz) - b_s[i] : 0;
+      b_L[i] = L < kSliceMax ? L : kSliceMax;  // a slice holds a dim once per item
+      b_row[i] = (int32_t)(r_row[i] & (kRows - 1));
+      b_qv[i] = __uint_as_float(r_qv[i]);
+    }
+  };
+  fetch_entries(e0);
 
   // ---- dense part: heavy dims on the matrix cores ----
-  // Wave w owns items [128 w, 128 w + 128) of the slice as two 64-item
-  // groups. Dims are taken 8 at a time (two MFMA k-steps), the next 8 loaded
-  // while the current ones are multiplied. qh and the slab hold zeros from
-  // the last heavy dim up to kHeavyMax, so rounding the dim count up to 16
-  // only adds exact zeros. The sums, rounded to fixed point, are the
-  // accumulators' initial values.
+  // Wave w owns items [128 w, 128 w + 128) of the slice as 8 tiles of 16.
+  // Per tile, three v_mfma_f32_16x16x32_f16 over all kHeavyMax dims:
+  // main = hi.hi and cross = hi.lo + lo.hi of the split values, so that the
+  // dot of the scaled values is main + cross / 2048 (fp32). Scaled back by
+  // 2^-16 and to fixed point (2^30), it is the accumulators' initial value.
   const int32_t wcol = wv * 128;
+  // Load order matters: the vector-memory counter drains in issue order, so
+  // the slab loads go out after the entry loads and before the dependent
+  // range loads; the MFMAs then wait for the slab only, and the range
+  // lookups (random, often an L2 miss) overlap the dense work.
+  constexpr int kTiles = 8;
+  h16x8 a_hi, a_lo, b_hi[kTiles], b_lo[kTiles];
+  const bool wdense = DENSE && wcol < Sp;
+  if (DENSE) {  // unconditional (a wave past the slice loads tile 0 and drops it), so that
+                // the counter waits below see one path
+    // A: lane l holds row l%16, dims 8(l/16)..+7 (hi, lo); B: item l%16 of
+    // the tile, the same dims. Both are tiles in the MFMA operand order.
+    static_assert(kTileHalves == 2 * 64 * 8, "a tile is one 16-byte load per lane per part");
+    const h16x8 *qt = reinterpret_cast<const h16x8 *>(a.qh + grp * (int64_t)kTileHalves);
+    a_hi = qt[lane];
+    a_lo = qt[64 + lane];
+    const h16x8 *st = reinterpret_cast<const h16x8 *>(
+        a.slab + (sl * (int64_t)a.pitch + (wdense ? wcol : 0)) * kHeavyRec);
+#pragma unroll
+    for (int tt = 0; tt < kTiles; ++tt) {
+      b_hi[tt] = st[tt * 128 + lane];
+      b_lo[tt] = st[tt * 128 + 64 + lane];
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  fetch_ranges();
+  __builtin_amdgcn_sched_barrier(0);
   if (DENSE) {
-    const int mr = (a.heavy[kHeavyMax] + 15) & ~15;
-    // B: lane l loads items 4(l%16)..+3 of a group on dim h + l/16
-    const float *sb = a.slab + sl * (int64_t)kHeavyMax * a.pitch + (wcol < Sp ? wcol : 0) +
-                      4 * (lane & 15) + (int64_t)(lane >> 4) * a.pitch;
-    f32x4 sv[2][2][2];  // [buffer][k-step][group]
-    auto load = [&](int b, int h0) {
+    if (wdense) {
 #pragma unroll
-      for (int k = 0; k < 2; ++k)
+      for (int tt = 0; tt < kTiles; ++tt) {
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        const f32x4 mn = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_hi, b_hi[tt], z, 0, 0, 0);
+        f32x4 cr = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_hi, b_lo[tt], z, 0, 0, 0);
+        cr = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_lo, b_hi[tt], cr, 0, 0, 0);
+        // lane l holds rows 4(l/16) + i of item 16 tt + l%16
+        int *dst = acc + (4 * (lane >> 4)) * Lp + wcol + 16 * tt + (lane & 15);
 #pragma unroll
-        for (int gi = 0; gi < 2; ++gi)
-          sv[b][k][gi] =
-              *reinterpret_cast<const f32x4 *>(sb + (int64_t)(h0 + 4 * k) * a.pitch + 64 * gi);
-    };
-    if (mr > 0) load(0, 0);
-    if (t < kRows * kHeavyMax)
-      s_qh[(t / kHeavyMax) * (kHeavyMax + 1) + t % kHeavyMax] = a.qh[grp * (kRows * kHeavyMax) + t];
-    __syncthreads();
-    f32x4 dacc[2][4];
-#pragma unroll
-    for (int gi = 0; gi < 2; ++gi)
-#pragma unroll
-      for (int u = 0; u < 4; ++u) dacc[gi][u] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // A: lane l supplies row l%16 on dim h + l/16
-    const float *qa = s_qh + (lane & 15) * (kHeavyMax + 1) + (lane >> 4);
-    auto mma = [&](int b, int h0) {
-#pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const float av = qa[h0 + 4 * k];
-#pragma unroll
-        for (int gi = 0; gi < 2; ++gi)
-#pragma unroll
-          for (int u = 0; u < 4; ++u)
-            dacc[gi][u] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, sv[b][k][gi][u], dacc[gi][u], 0, 0, 0);
-      }
-    };
-    if (wcol < Sp) {
-      for (int h0 = 0; h0 < mr; h0 += 16) {
-        load(1, h0 + 8);
-        mma(0, h0);
-        if (h0 + 16 < mr) load(0, h0 + 16);
-        mma(1, h0 + 8);
-      }
-      // lane l holds rows 4(l/16) + i of items 64 gi + 4(l%16) + u in dacc[gi][u][i]
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 4 * (lane >> 4) + i;
-#pragma unroll
-        for (int gi = 0; gi < 2; ++gi)
-          *reinterpret_cast<int4 *>(acc + r * Lp + wcol + 64 * gi + 4 * (lane & 15)) =
-              make_int4(round_fix(dacc[gi][0][i] * kFixScale), round_fix(dacc[gi][1][i] * kFixScale),
-                        round_fix(dacc[gi][2][i] * kFixScale), round_fix(dacc[gi][3][i] * kFixScale));
+        for (int i = 0; i < 4; ++i)
+          dst[i * Lp] = round_fix((mn[i] + cr[i] * (1.0f / kLoScale)) * kDenseToFix);
       }
     }
   } else {
     int4 *acc4 = reinterpret_cast<int4 *>(acc);
     for (int k = t; k < kRows * Lp / 4; k += NT) acc4[k] = make_int4(0, 0, 0, 0);
   }
+  __builtin_amdgcn_sched_barrier(0);
+  finish_ranges();
   __syncthreads();  // accumulators initialised before any sparse update
 
   // ---- sparse part: the rows' light entries, batch by batch ----
@@ -229,7 +234,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void sc
       c_off[i] = b_row[i] * Lp;
       c_qv[i] = __float_as_uint(b_qv[i]);
     }
-    if (eb + kBatch < e1) fetch(eb + kBatch);  // next batch's descriptors, in flight during this one
+    if (eb + kBatch < e1) {  // next batch's descriptors, in flight during this one
+      fetch_entries(eb + kBatch);
+      fetch_ranges();
+      finish_ranges();
+    }
     for (int32_t r0 = 0; r0 < total; r0 += kSegMax) {
       // the segments of this round that belong to this thread's lists
 #pragma unroll
@@ -331,8 +340,7 @@ __global__ void fold_row_sums_kernel(int64_t n_q, int32_t n_sub, const double *_
 }
 
 size_t score_lds_bytes(int32_t S) {
-  return (size_t)kRows * acc_pitch(S) * sizeof(int) + (kSegMax + kSegPad) * 12 + NW * 4 +
-         kRows * (kHeavyMax + 1) * 4;
+  return (size_t)kRows * acc_pitch(S) * sizeof(int) + (kSegMax + kSegPad) * 12 + NW * 4;
 }
 
 static int env_unroll() {
