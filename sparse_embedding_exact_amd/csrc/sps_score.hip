@@ -72,6 +72,7 @@ __device__ __forceinline__ T ld_off(const T *base, uint32_t byte_off) {
 constexpr int NT = kScoreThreads;
 constexpr int NW = NT / 64;
 constexpr int kBatch = 2 * NT;  // light entries per batch, two per thread
+constexpr int kGroups = 2;      // row groups per workgroup (they share the slab loads)
 static_assert(kRows % NW == 0, "whole rows per wave in the epilogue");
 static_assert(kSliceMax <= NW * 128, "128 items per wave cover a slice");
 static_assert(kRows == 16 && kHeavyMax == 32, "one 16x16x32 MFMA tile covers the rows and heavy dims");
@@ -79,13 +80,13 @@ static_assert(kRows == 16 && kHeavyMax == 32, "one 16x16x32 MFMA tile covers the
 // 16 lanes, described in an LDS table.
 constexpr int kSeg = 16;
 constexpr int kSegMax = 896;         // segments per round
-constexpr int kSegPad = 4 * NW * 4;  // one step of quads past the end (U <= 4)
+constexpr int kSegPad = 4 * NW * 8;  // one step of quads past the end (U <= 8)
 static_assert(kRows * kSliceMax * 4 < (1 << 27), "row byte offset fits the segment record");
 
 template <bool DENSE, int U>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void score_kernel(
     const ScoreArgs a, int vec4) {
-  static_assert(U <= 4, "the segment table pads one step of at most 4 quads per wave");
+  static_assert(U <= 8, "the segment table pads one step of at most 8 quads per wave");
   extern __shared__ int acc[];
   // segment table of a round: first posting, query value, and the LDS byte
   // offset of the row << 5 | postings in the segment (1..16; 0 pads the
@@ -96,43 +97,47 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void sc
 
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const Geom &g = a.g;
-  // Slice-fastest order: consecutive workgroups take the slices of one row
-  // group, and workgroups are dealt to the 8 XCDs in turn, so with n_sub
-  // dividing 8 each XCD keeps to the same slice of the chunk (its posting
-  // lists and slab stay in that XCD's L2) while the rows written at any
-  // time span whole output rows.
-  const int64_t grp = blockIdx.x / g.n_sub;
+  // Slice-fastest order: consecutive workgroups take the slices of one pair
+  // of row groups, and workgroups are dealt to the 8 XCDs in turn, so with
+  // n_sub dividing 8 each XCD keeps to the same slice of the chunk (its
+  // posting lists and slab stay in that XCD's L2) while the rows written at
+  // any time span whole output rows.
+  const int64_t grp0 = (blockIdx.x / g.n_sub) * kGroups;
   const int ks = (int)(blockIdx.x % g.n_sub);
+  const int ng = (int)(a.n_groups - grp0 < kGroups ? a.n_groups - grp0 : kGroups);  // 1 or 2
   const int64_t sl = (int64_t)a.chunk * g.n_sub + ks;
   const int64_t ib = g.slice_begin(sl);
   const int32_t slen = (int32_t)(g.slice_end(sl) - ib);
   const int32_t Sp = slab_pitch(g.S);  // slab row pitch (items)
   const int32_t Lp = acc_pitch(g.S);   // accumulator row pitch (ints)
-  const int64_t q0 = grp * kRows;
-  const int64_t qe = q0 + kRows < a.n_q ? q0 + kRows : a.n_q;
 
-  // Batch descriptors (see the sparse part), two entries per thread: fetched
-  // before the dense part so that their two dependent loads (entry, then
-  // posting range) overlap it.
   const int32_t *cps = a.col_ptr + sl * (a.dim + 1);
   const int32_t cb0 = a.slice_base[sl];
   const int32_t snnz = a.slice_base[sl + 1] - cb0 > 0 ? a.slice_base[sl + 1] - cb0 : 0;
-  const int32_t e0 = a.lptr[q0], e1 = a.lptr[qe];
+  // light entries of group gi: [ge[gi], ge[gi + 1]) (the rows are consecutive)
+  int32_t ge[kGroups + 1];
+#pragma unroll
+  for (int gi = 0; gi <= kGroups; ++gi) {
+    const int64_t q = (grp0 + (gi < ng ? gi : ng)) * kRows;
+    ge[gi] = a.lptr[q < a.n_q ? q : a.n_q];
+  }
+
+  // Batch descriptors (see the sparse part), two entries per thread. Three
+  // stages, so that other loads can be issued between them and no arithmetic
+  // on a loaded value forces an early wait: entry loads (raw), then the
+  // dependent posting-range loads (raw), then the range arithmetic.
   int32_t b_s[2], b_L[2], b_row[2];
   float b_qv[2];
-  // Three stages, so that other loads can be issued between them and no
-  // arithmetic on a loaded value forces an early wait: entry loads (raw),
-  // then the dependent posting-range loads (raw), then the range arithmetic.
   int32_t r_d[2], r_lo[2], r_hi[2];
   uint32_t r_qv[2], r_row[2];
   bool r_ok[2];
-  auto fetch_entries = [&](int32_t eb) {
+  auto fetch_entries = [&](int32_t eb, int32_t ee) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int32_t e = eb + t + i * NT;
-      r_ok[i] = e < e1;
+      r_ok[i] = e < ee;
       // a readable entry (the light arrays hold at least one) when e is past the end
-      const int32_t ec = e < e1 ? e : (e1 > 0 ? e1 - 1 : 0);
+      const int32_t ec = e < ee ? e : (ee > 0 ? ee - 1 : 0);
       r_d[i] = a.ldim[ec];
       r_qv[i] = __float_as_uint(a.lval[ec]);
       r_row[i] = a.lrow[ec];
@@ -157,30 +162,37 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void sc
       b_qv[i] = __uint_as_float(r_qv[i]);
     }
   };
-  fetch_entries(e0);
+  fetch_entries(ge[0], ge[1]);
 
   // ---- dense part: heavy dims on the matrix cores ----
   // Wave w owns items [128 w, 128 w + 128) of the slice as 8 tiles of 16.
-  // Per tile, three v_mfma_f32_16x16x32_f16 over all kHeavyMax dims:
-  // main = hi.hi and cross = hi.lo + lo.hi of the split values, so that the
-  // dot of the scaled values is main + cross / 2048 (fp32). Scaled back by
-  // 2^-16 and to fixed point (2^30), it is the accumulators' initial value.
+  // Per tile and row group, three v_mfma_f32_16x16x32_f16 over all
+  // kHeavyMax dims: main = hi.hi and cross = hi.lo + lo.hi of the split
+  // values, so that the dot of the scaled values is main + cross / 2048
+  // (fp32). Scaled back by 2^-16 and to fixed point (2^30) it is the
+  // accumulators' initial value: group 0's is written to LDS at once, group
+  // 1's waits in registers. Each slab tile loaded serves both groups.
   const int32_t wcol = wv * 128;
   // Load order matters: the vector-memory counter drains in issue order, so
   // the slab loads go out after the entry loads and before the dependent
   // range loads; the MFMAs then wait for the slab only, and the range
   // lookups (random, often an L2 miss) overlap the dense work.
   constexpr int kTiles = 8;
-  h16x8 a_hi, a_lo, b_hi[kTiles], b_lo[kTiles];
+  h16x8 a_hi[kGroups], a_lo[kGroups], b_hi[kTiles], b_lo[kTiles];
+  int32_t dpend[kTiles][4];  // group 1's initial values, fixed point
   const bool wdense = DENSE && wcol < Sp;
   if (DENSE) {  // unconditional (a wave past the slice loads tile 0 and drops it), so that
                 // the counter waits below see one path
     // A: lane l holds row l%16, dims 8(l/16)..+7 (hi, lo); B: item l%16 of
     // the tile, the same dims. Both are tiles in the MFMA operand order.
     static_assert(kTileHalves == 2 * 64 * 8, "a tile is one 16-byte load per lane per part");
-    const h16x8 *qt = reinterpret_cast<const h16x8 *>(a.qh + grp * (int64_t)kTileHalves);
-    a_hi = qt[lane];
-    a_lo = qt[64 + lane];
+#pragma unroll
+    for (int gi = 0; gi < kGroups; ++gi) {
+      const h16x8 *qt = reinterpret_cast<const h16x8 *>(
+          a.qh + (grp0 + (gi < ng ? gi : 0)) * (int64_t)kTileHalves);
+      a_hi[gi] = qt[lane];
+      a_lo[gi] = qt[64 + lane];
+    }
     const h16x8 *st = reinterpret_cast<const h16x8 *>(
         a.slab + (sl * (int64_t)a.pitch + (wdense ? wcol : 0)) * kHeavyRec);
 #pragma unroll
@@ -192,19 +204,25 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void sc
   __builtin_amdgcn_sched_barrier(0);
   fetch_ranges();
   __builtin_amdgcn_sched_barrier(0);
+  // lane l holds rows 4(l/16) + i of item 16 tt + l%16
+  int *const dbase = acc + (4 * (lane >> 4)) * Lp + wcol + (lane & 15);
   if (DENSE) {
     if (wdense) {
 #pragma unroll
       for (int tt = 0; tt < kTiles; ++tt) {
-        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        const f32x4 mn = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_hi, b_hi[tt], z, 0, 0, 0);
-        f32x4 cr = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_hi, b_lo[tt], z, 0, 0, 0);
-        cr = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_lo, b_hi[tt], cr, 0, 0, 0);
-        // lane l holds rows 4(l/16) + i of item 16 tt + l%16
-        int *dst = acc + (4 * (lane >> 4)) * Lp + wcol + 16 * tt + (lane & 15);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          dst[i * Lp] = round_fix((mn[i] + cr[i] * (1.0f / kLoScale)) * kDenseToFix);
+        for (int gi = 0; gi < kGroups; ++gi) {
+          const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+          const f32x4 mn = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_hi[gi], b_hi[tt], z, 0, 0, 0);
+          f32x4 cr = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_hi[gi], b_lo[tt], z, 0, 0, 0);
+          cr = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_lo[gi], b_hi[tt], cr, 0, 0, 0);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int v = round_fix((mn[i] + cr[i] * (1.0f / kLoScale)) * kDenseToFix);
+            if (gi == 0) dbase[i * Lp + 16 * tt] = v;
+            else dpend[tt][i] = v;
+          }
+        }
       }
     }
   } else {
@@ -215,116 +233,143 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void sc
   finish_ranges();
   __syncthreads();  // accumulators initialised before any sparse update
 
-  // ---- sparse part: the rows' light entries, batch by batch ----
   const uint2 *__restrict__ ppost = a.post + cb0;
-  for (int32_t eb = e0; eb < e1; eb += kBatch) {
-    int32_t nseg[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) nseg[i] = (b_L[i] + kSeg - 1) / kSeg;
-    int32_t total;
-    const int32_t pend = block_incl_scan<NT>(nseg[0] + nseg[1], ws, &total);  // barrier inside
-    const int32_t sp[2] = {pend - nseg[0] - nseg[1], pend - nseg[1]};
-    // this batch's lists, kept while the next batch's descriptors load
-    int32_t c_s[2], c_L[2], c_off[2];
-    uint32_t c_qv[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      c_s[i] = b_s[i];
-      c_L[i] = b_L[i];
-      c_off[i] = b_row[i] * Lp;
-      c_qv[i] = __float_as_uint(b_qv[i]);
-    }
-    if (eb + kBatch < e1) {  // next batch's descriptors, in flight during this one
-      fetch_entries(eb + kBatch);
-      fetch_ranges();
-      finish_ranges();
-    }
-    for (int32_t r0 = 0; r0 < total; r0 += kSegMax) {
-      // the segments of this round that belong to this thread's lists
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int32_t sb0 = sp[i] > r0 ? sp[i] : r0;
-        const int32_t se = sp[i] + nseg[i] < r0 + kSegMax ? sp[i] + nseg[i] : r0 + kSegMax;
-        for (int32_t sg = sb0; sg < se; ++sg) {
-          const int32_t j0 = (sg - sp[i]) * kSeg;
-          const int32_t n = c_L[i] - j0 < kSeg ? c_L[i] - j0 : kSeg;
-          s_spos[sg - r0] = (uint32_t)(c_s[i] + j0);
-          s_sqv[sg - r0] = c_qv[i];
-          s_smeta[sg - r0] = (uint32_t)n | ((uint32_t)c_off[i] << 7);  // byte offset << 5
-        }
-      }
-      const int32_t nr = total - r0 < kSegMax ? total - r0 : kSegMax;
-      if (t < kSegPad) s_smeta[nr + t] = 0u;
-      __syncthreads();
-      // Wave w takes segment quads w, w + NW, ...; lanes 16i..16i+15 take
-      // segment i of a quad, U quads per step.
-      const int32_t jl = lane & 15;
-      for (int32_t k0 = wv; 4 * k0 < nr; k0 += NW * U) {
-        uint32_t pos[U];
-        uint32_t aoff[U];
-        float qv[U];
-        bool ok[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          // entries past nr are padding (no postings)
-          const int32_t sg = 4 * (k0 + NW * u) + (lane >> 4);
-          const uint32_t meta = s_smeta[sg];
-          const uint32_t sp0 = s_spos[sg];
-          ok[u] = jl < (int32_t)(meta & 31u);
-          pos[u] = ok[u] ? sp0 + jl : 0u;
-          aoff[u] = meta >> 5;
-          qv[u] = __uint_as_float(s_sqv[sg]);
-        }
-        uint2 pe[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) pe[u] = ld_off(ppost, pos[u] * 8u);
-        // all U loads are in flight before the first is waited on (keeps the
-        // compiler from sinking a load into the masked update below it)
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int u = 0; u < U; ++u) asm volatile("" ::"v"(pe[u].x), "v"(pe[u].y));
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          if (ok[u] && pe[u].x < (uint32_t)slen)
-            atomicAdd(reinterpret_cast<int *>(reinterpret_cast<char *>(acc) + aoff[u] + 4 * pe[u].x),
-                      round_fix(qv[u] * __uint_as_float(pe[u].y)));
-        }
-      }
-      __syncthreads();
-    }
-  }
-
-  // ---- epilogue: wave w writes rows w, w + NW, ... ----
   const int64_t col0 = ib - g.chunk_begin(a.chunk);
   const bool v4 = vec4 && (col0 % 4 == 0);
   double *rsum = g.n_sub == 1 ? a.row_sums : a.rs_part;
+  for (int gi = 0; gi < ng; ++gi) {
+    const int64_t q0 = (grp0 + gi) * kRows;
+    if (gi > 0) {
+      // the previous group's epilogue has read the accumulators
+      __syncthreads();
+      if (DENSE) {
+        if (wdense) {
 #pragma unroll
-  for (int rr = 0; rr < kRows / NW; ++rr) {
-    const int r = wv + NW * rr;
-    const int64_t q = q0 + r;
-    if (q >= a.n_q) break;
-    float *orow = a.out + q * a.ld + col0;
-    const int4 *arow = reinterpret_cast<const int4 *>(acc + r * Lp);
-    double rs = 0.0;
-    for (int j0 = 4 * lane; j0 < slen; j0 += 256) {
-      const int4 x = arow[j0 >> 2];
-      const f32x4 v = {(float)x.x * kFixInv, (float)x.y * kFixInv, (float)x.z * kFixInv,
-                       (float)x.w * kFixInv};
-      if (v4 && j0 + 3 < slen) {
-        __builtin_nontemporal_store(v, reinterpret_cast<f32x4 *>(orow + j0));
-        rs += ((double)v[0] + (double)v[1]) + ((double)v[2] + (double)v[3]);
+          for (int tt = 0; tt < kTiles; ++tt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dbase[i * Lp + 16 * tt] = dpend[tt][i];
+        }
       } else {
+        int4 *acc4 = reinterpret_cast<int4 *>(acc);
+        for (int k = t; k < kRows * Lp / 4; k += NT) acc4[k] = make_int4(0, 0, 0, 0);
+      }
+      __syncthreads();
+    }
+
+    // ---- sparse part: the rows' light entries, batch by batch ----
+    const int32_t e1 = ge[gi + 1];
+    for (int32_t eb = ge[gi]; eb < e1; eb += kBatch) {
+      int32_t nseg[2];
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-          if (j0 + u < slen) {
-            __builtin_nontemporal_store(v[u], orow + j0 + u);
-            rs += (double)v[u];
+      for (int i = 0; i < 2; ++i) nseg[i] = (b_L[i] + kSeg - 1) / kSeg;
+      int32_t total;
+      const int32_t pend = block_incl_scan<NT>(nseg[0] + nseg[1], ws, &total);  // barrier inside
+      const int32_t sp[2] = {pend - nseg[0] - nseg[1], pend - nseg[1]};
+      // this batch's lists, kept while the next batch's descriptors load
+      int32_t c_s[2], c_L[2], c_off[2];
+      uint32_t c_qv[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        c_s[i] = b_s[i];
+        c_L[i] = b_L[i];
+        c_off[i] = b_row[i] * Lp;
+        c_qv[i] = __float_as_uint(b_qv[i]);
+      }
+      // the next batch's descriptors (this group's, else the next group's
+      // first), in flight during this one
+      if (eb + kBatch < e1) {
+        fetch_entries(eb + kBatch, e1);
+        fetch_ranges();
+        finish_ranges();
+      } else if (gi + 1 < ng) {
+        fetch_entries(ge[gi + 1], ge[gi + 2]);
+        fetch_ranges();
+        finish_ranges();
+      }
+      for (int32_t r0 = 0; r0 < total; r0 += kSegMax) {
+        // the segments of this round that belong to this thread's lists
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int32_t sb0 = sp[i] > r0 ? sp[i] : r0;
+          const int32_t se = sp[i] + nseg[i] < r0 + kSegMax ? sp[i] + nseg[i] : r0 + kSegMax;
+          for (int32_t sg = sb0; sg < se; ++sg) {
+            const int32_t j0 = (sg - sp[i]) * kSeg;
+            const int32_t n = c_L[i] - j0 < kSeg ? c_L[i] - j0 : kSeg;
+            s_spos[sg - r0] = (uint32_t)(c_s[i] + j0);
+            s_sqv[sg - r0] = c_qv[i];
+            s_smeta[sg - r0] = (uint32_t)n | ((uint32_t)c_off[i] << 7);  // byte offset << 5
           }
+        }
+        const int32_t nr = total - r0 < kSegMax ? total - r0 : kSegMax;
+        for (int k = t; k < kSegPad; k += NT) s_smeta[nr + k] = 0u;
+        __syncthreads();
+        // Wave w takes segment quads w, w + NW, ...; lanes 16i..16i+15 take
+        // segment i of a quad, U quads per step.
+        const int32_t jl = lane & 15;
+        for (int32_t k0 = wv; 4 * k0 < nr; k0 += NW * U) {
+          uint32_t pos[U];
+          uint32_t aoff[U];
+          float qv[U];
+          bool ok[U];
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            // entries past nr are padding (no postings)
+            const int32_t sg = 4 * (k0 + NW * u) + (lane >> 4);
+            const uint32_t meta = s_smeta[sg];
+            const uint32_t sp0 = s_spos[sg];
+            ok[u] = jl < (int32_t)(meta & 31u);
+            pos[u] = ok[u] ? sp0 + jl : 0u;
+            aoff[u] = meta >> 5;
+            qv[u] = __uint_as_float(s_sqv[sg]);
+          }
+          uint2 pe[U];
+#pragma unroll
+          for (int u = 0; u < U; ++u) pe[u] = ld_off(ppost, pos[u] * 8u);
+          // all U loads are in flight before the first is waited on (keeps the
+          // compiler from sinking a load into the masked update below it)
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int u = 0; u < U; ++u) asm volatile("" ::"v"(pe[u].x), "v"(pe[u].y));
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            if (ok[u] && pe[u].x < (uint32_t)slen)
+              atomicAdd(reinterpret_cast<int *>(reinterpret_cast<char *>(acc) + aoff[u] + 4 * pe[u].x),
+                        round_fix(qv[u] * __uint_as_float(pe[u].y)));
+          }
+        }
+        __syncthreads();
       }
     }
-    if (rsum != nullptr) {
-      rs = wave_sum(rs);
-      if (lane == 0) rsum[(g.n_sub == 1 ? 0 : (int64_t)ks * a.n_q) + q] = rs;
+
+    // ---- epilogue: wave w writes rows w, w + NW, ... of the group ----
+#pragma unroll
+    for (int rr = 0; rr < kRows / NW; ++rr) {
+      const int r = wv + NW * rr;
+      const int64_t q = q0 + r;
+      if (q >= a.n_q) break;
+      float *orow = a.out + q * a.ld + col0;
+      const int4 *arow = reinterpret_cast<const int4 *>(acc + r * Lp);
+      double rs = 0.0;
+      for (int j0 = 4 * lane; j0 < slen; j0 += 256) {
+        const int4 x = arow[j0 >> 2];
+        const f32x4 v = {(float)x.x * kFixInv, (float)x.y * kFixInv, (float)x.z * kFixInv,
+                         (float)x.w * kFixInv};
+        if (v4 && j0 + 3 < slen) {
+          __builtin_nontemporal_store(v, reinterpret_cast<f32x4 *>(orow + j0));
+          rs += ((double)v[0] + (double)v[1]) + ((double)v[2] + (double)v[3]);
+        } else {
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            if (j0 + u < slen) {
+              __builtin_nontemporal_store(v[u], orow + j0 + u);
+              rs += (double)v[u];
+            }
+        }
+      }
+      if (rsum != nullptr) {
+        rs = wave_sum(rs);
+        if (lane == 0) rsum[(g.n_sub == 1 ? 0 : (int64_t)ks * a.n_q) + q] = rs;
+      }
     }
   }
 }
@@ -349,7 +394,7 @@ static int env_unroll() {
     v = 4;
     if (const char *e = getenv("SPS_SCORE_UNROLL")) {
       const int x = atoi(e);
-      if (x == 2 || x == 4) v = x;
+      if (x == 2 || x == 4 || x == 8) v = x;
     }
   }
   return v;
@@ -368,8 +413,8 @@ static hipError_t launch_t(const ScoreArgs &a, hipStream_t s) {
     opted = dyn;
   }
   const int vec4 = (a.ld % 4 == 0) && ((reinterpret_cast<uintptr_t>(a.out) & 15) == 0);
-  hipLaunchKernelGGL(kern, dim3((unsigned)((int64_t)a.n_groups * a.g.n_sub)), dim3(NT), dyn, s, a,
-                     vec4);
+  const int64_t pairs = (a.n_groups + kGroups - 1) / kGroups;
+  hipLaunchKernelGGL(kern, dim3((unsigned)(pairs * a.g.n_sub)), dim3(NT), dyn, s, a, vec4);
   return hipGetLastError();
 }
 
@@ -378,9 +423,11 @@ hipError_t launch_score(const ScoreArgs &a, hipStream_t s) {
   const int u = env_unroll();
   hipError_t e;
   if (a.dense) {
-    e = u == 2 ? launch_t<true, 2>(a, s) : launch_t<true, 4>(a, s);
+    e = u == 8 ? launch_t<true, 8>(a, s)
+               : (u == 2 ? launch_t<true, 2>(a, s) : launch_t<true, 4>(a, s));
   } else {
-    e = u == 2 ? launch_t<false, 2>(a, s) : launch_t<false, 4>(a, s);
+    e = u == 8 ? launch_t<false, 8>(a, s)
+               : (u == 2 ? launch_t<false, 2>(a, s) : launch_t<false, 4>(a, s));
   }
   if (e != hipSuccess) return e;
   if (a.row_sums != nullptr && a.g.n_sub > 1) {
