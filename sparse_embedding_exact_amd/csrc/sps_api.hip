@@ -97,7 +97,7 @@ ItemsLayout items_layout(const sps::Geom &g, int64_t dim, int64_t nnz, bool dens
   ItemsLayout L{};
   Layout p;
   L.inv = p.add(g.n_items, 4);
-  L.colp = p.add((uint64_t)ns * (uint64_t)(dim + 1), 4);
+  L.colp = p.add((uint64_t)ns * (uint64_t)sps::cp_pitch(dim), 4);
   L.post = p.add(nnz, 8);
   L.sbase = p.add(ns + 1, 4);
   L.heavy = p.add(sps::kHeavyMax + 1, 4);
@@ -317,7 +317,7 @@ sps_status sps_items_slice_view(const sps_items *h, int64_t slice, void *stream,
   view->item_begin = h->g.slice_begin(slice);
   view->slice_len = (int32_t)(h->g.slice_end(slice) - view->item_begin);
   view->slice_nnz = be[1] - be[0];
-  view->col_ptr = h->col_ptr + slice * (h->dim + 1);
+  view->col_ptr = h->col_ptr + slice * sps::cp_pitch(h->dim);
   view->post = reinterpret_cast<const sps_posting *>(h->post + be[0]);
   view->item_inv_norm = h->inv_norm + view->item_begin;
   return SPS_OK;

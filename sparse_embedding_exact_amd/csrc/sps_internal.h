@@ -97,6 +97,9 @@ __device__ inline void split_fp16(float x, uint16_t &hi, uint16_t &lo) {
 // Item pitch of a slice's heavy-dim slab: a whole number of 128-item groups
 // (one wave's share in the dense part).
 __host__ __device__ inline int32_t slab_pitch(int32_t S) { return (S + 127) / 128 * 128; }
+// Pitch (ints) of one slice's col_ptr[dim + 1]: rounded up to 4, so that each
+// slice's array starts 16-byte aligned.
+__host__ __device__ inline int64_t cp_pitch(int64_t dim) { return (dim + 1 + 3) / 4 * 4; }
 // Row pitch (ints) of the score kernel's LDS accumulators: the slab pitch
 // plus 4, so that rows start 16 bytes apart modulo the LDS bank period.
 __host__ __device__ inline int32_t acc_pitch(int32_t S) { return slab_pitch(S) + 4; }
@@ -119,7 +122,7 @@ struct ItemsDev {
   const int32_t *indptr, *indices;
   const float *values;
   float *inv_norm;      // persistent, n_items
-  int32_t *col_ptr;     // persistent, num_slices * (dim+1)
+  int32_t *col_ptr;     // persistent, num_slices * cp_pitch(dim)
   uint2 *post;          // persistent, nnz: (slice-local item id, value bits)
   int32_t *slice_base;  // persistent, num_slices + 1
   int32_t *heavy;       // persistent, kHeavyMax + 1: heavy dims ascending, then their count

@@ -182,23 +182,29 @@ __global__ void slice_base_kernel(Geom g, int64_t nnz, const int32_t *__restrict
   slice_base[s] = (int32_t)clamp64(indptr[i], 0, nnz);
 }
 
+// 16 lanes per item, so that a row's indices are read coalesced.
+constexpr int kLanesPerItem = 16;
+
 __global__ __launch_bounds__(256) void csc_count_kernel(Geom g, int64_t dim,
                                                         const int32_t *__restrict__ indptr,
                                                         const int32_t *__restrict__ indices,
                                                         const int32_t *__restrict__ flags,
                                                         int32_t *__restrict__ col_ptr,
                                                         int32_t *__restrict__ ticket) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t gt = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t i = gt / kLanesPerItem;
+  const int sub = (int)(gt % kLanesPerItem);
   if (i >= g.n_items || flags[0] != 0) return;
   const int64_t b = indptr[i], e = indptr[i + 1];
-  int32_t *cp = col_ptr + g.slice_of(i) * (dim + 1);
-  for (int64_t k = b; k < e; ++k) ticket[k] = atomicAdd(&cp[indices[k]], 1);
+  int32_t *cp = col_ptr + g.slice_of(i) * cp_pitch(dim);
+  for (int64_t k = b + sub; k < e; k += kLanesPerItem) ticket[k] = atomicAdd(&cp[indices[k]], 1);
 }
 
-// One workgroup per slice: exclusive scan of dim+1 counts in place, in tiles
-// of 4*NT; plus the compacted list of dims with >= 2 entries. The scan carries
-// (count, multi-flag) packed in one 64-bit value: slice nnz < 2^31 keeps the
-// count half from carrying into the flag half.
+// One workgroup per slice: exclusive scan of dim+1 counts in place, each
+// thread owning 16 consecutive counts of a tile (four 16-byte loads); plus
+// the compacted list of dims with >= 2 entries. The scan carries (count,
+// multi-flag) packed in one 64-bit value: slice nnz < 2^31 keeps the count
+// half from carrying into the flag half.
 // When gdf is given, every dim holding at least `hmin` entries of the slice
 // adds its count to gdf[d] (the document frequency used to pick heavy dims;
 // integer atomics, so the totals do not depend on the order of slices).
@@ -210,8 +216,8 @@ __global__ __launch_bounds__(NT) void csc_scan_kernel(int64_t dim,
                                                       int32_t *__restrict__ mlist,
                                                       int32_t *__restrict__ mcount,
                                                       int32_t *__restrict__ gdf, int32_t hmin) {
-  constexpr int TILE = 4 * NT;
-  __shared__ int32_t tile[TILE];
+  constexpr int PER = 16;
+  constexpr int TILE = PER * NT;
   __shared__ int64_t ws[NT / 64];
   const int64_t c = blockIdx.x;
   const int t = threadIdx.x;
@@ -219,42 +225,52 @@ __global__ __launch_bounds__(NT) void csc_scan_kernel(int64_t dim,
     if (t == 0) mcount[c] = 0;
     return;
   }
-  int32_t *cp = col_ptr + c * (dim + 1);
+  const int64_t pitch = cp_pitch(dim);  // a multiple of 4: the int4 accesses stay inside
+  int4 *cp4 = reinterpret_cast<int4 *>(col_ptr + c * pitch);
   int32_t *ml = mlist + (slice_base[c] / 2 + c);
   const int64_t n = dim + 1;
   int64_t carry = 0;
   for (int64_t base = 0; base < n; base += TILE) {
+    const int64_t j0 = base + (int64_t)PER * t;
+    int32_t v[PER];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int64_t j = base + k * NT + t;
-      tile[k * NT + t] = j < n ? cp[j] : 0;
+    for (int k = 0; k < PER / 4; ++k) {
+      const int64_t j = j0 + 4 * k;
+      const int4 x = j < pitch ? cp4[j >> 2] : make_int4(0, 0, 0, 0);
+      v[4 * k] = j < n ? x.x : 0;
+      v[4 * k + 1] = j + 1 < n ? x.y : 0;
+      v[4 * k + 2] = j + 2 < n ? x.z : 0;
+      v[4 * k + 3] = j + 3 < n ? x.w : 0;
     }
-    __syncthreads();
-    int32_t v[4];
     int64_t sum = 0;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      v[k] = tile[4 * t + k];
+    for (int k = 0; k < PER; ++k) {
       sum += (int64_t)v[k] + ((int64_t)(v[k] >= 2) << 32);
-      if (gdf != nullptr && v[k] >= hmin) atomicAdd(&gdf[base + 4 * t + k], v[k]);
+      if (gdf != nullptr && v[k] >= hmin) atomicAdd(&gdf[j0 + k], v[k]);
     }
     int64_t tot;
-    int64_t incl = block_incl_scan<NT>(sum, ws, &tot);
+    const int64_t incl = block_incl_scan<NT>(sum, ws, &tot);
     int64_t ex = carry + incl - sum;
+    int32_t o[PER];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      tile[4 * t + k] = (int32_t)(ex & 0xFFFFFFFFll);
-      if (v[k] >= 2) ml[ex >> 32] = (int32_t)(base + 4 * t + k);
+    for (int k = 0; k < PER; ++k) {
+      o[k] = (int32_t)(ex & 0xFFFFFFFFll);
+      if (v[k] >= 2) ml[ex >> 32] = (int32_t)(j0 + k);
       ex += (int64_t)v[k] + ((int64_t)(v[k] >= 2) << 32);
     }
-    carry += tot;
-    __syncthreads();
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int64_t j = base + k * NT + t;
-      if (j < n) cp[j] = tile[k * NT + t];
+    for (int k = 0; k < PER / 4; ++k) {
+      const int64_t j = j0 + 4 * k;
+      if (j + 3 < n) {
+        cp4[j >> 2] = make_int4(o[4 * k], o[4 * k + 1], o[4 * k + 2], o[4 * k + 3]);
+      } else {
+        int32_t *cp = col_ptr + c * pitch;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (j + u < n) cp[j + u] = o[4 * k + u];
+      }
     }
-    __syncthreads();
+    carry += tot;
   }
   if (t == 0) mcount[c] = (int32_t)(carry >> 32);
 }
@@ -265,15 +281,17 @@ __global__ __launch_bounds__(256) void csc_scatter_kernel(
     const int32_t *__restrict__ flags, const int32_t *__restrict__ col_ptr,
     const int32_t *__restrict__ slice_base, const int32_t *__restrict__ ticket,
     uint2 *__restrict__ post, uint16_t *__restrict__ trow, float *__restrict__ tval) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t gt = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t i = gt / kLanesPerItem;
+  const int sub = (int)(gt % kLanesPerItem);
   if (i >= g.n_items || flags[0] != 0) return;
   const int64_t sl = g.slice_of(i);
-  const int32_t *cp = col_ptr + sl * (dim + 1);
+  const int32_t *cp = col_ptr + sl * cp_pitch(dim);
   const int64_t base = slice_base[sl];
   const uint16_t local = (uint16_t)(i - g.slice_begin(sl));
   const double n = norm64[i];
   const int64_t b = indptr[i], e = indptr[i + 1];
-  for (int64_t k = b; k < e; ++k) {
+  for (int64_t k = b + sub; k < e; k += kLanesPerItem) {
     const int32_t d = indices[k];
     const int32_t s = cp[d];
     const int32_t len = cp[d + 1] - s;
@@ -307,7 +325,7 @@ __global__ __launch_bounds__(NT) void csc_fixup_kernel(
   const int64_t c = blockIdx.x / G;
   const int64_t g = blockIdx.x % G;
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
-  const int32_t *cp = col_ptr + c * (dim + 1);
+  const int32_t *cp = col_ptr + c * cp_pitch(dim);
   const int64_t base = slice_base[c];
   const int32_t *ml = mlist + (slice_base[c] / 2 + c);
   const int64_t m = mcount[c];
@@ -475,7 +493,7 @@ __global__ __launch_bounds__(256) void slab_scatter_kernel(
   const int h = blockIdx.x % kHeavyMax;
   if (flags[0] != 0 || h >= heavy[kHeavyMax]) return;
   const int32_t d = heavy[h];
-  const int32_t *cp = col_ptr + c * (dim + 1);
+  const int32_t *cp = col_ptr + c * cp_pitch(dim);
   const int64_t base = slice_base[c];
   const int32_t b = cp[d], e = cp[d + 1];
   uint16_t *sl = slab + c * (int64_t)pitch * kHeavyRec;
@@ -502,7 +520,7 @@ hipError_t launch_prepare_items(const ItemsDev &d, hipStream_t s) {
   hipLaunchKernelGGL(slice_base_kernel, dim3((unsigned)((ns + 1 + 255) / 256)), dim3(256), 0, s,
                      g, d.nnz, d.indptr, d.slice_base);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  e = launch_fill_i32(d.col_ptr, ns * (d.dim + 1), 0, s);
+  e = launch_fill_i32(d.col_ptr, ns * cp_pitch(d.dim), 0, s);
   if (e != hipSuccess) return e;
   e = launch_fill_i32(d.heavy, kHeavyMax + 1, 0, s);
   if (e != hipSuccess) return e;
@@ -511,7 +529,7 @@ hipError_t launch_prepare_items(const ItemsDev &d, hipStream_t s) {
     e = launch_fill_i32(d.gdf, d.dim, 0, s);
     if (e != hipSuccess) return e;
   }
-  const unsigned item_blocks = (unsigned)((g.n_items + 255) / 256);
+  const unsigned item_blocks = (unsigned)((g.n_items * kLanesPerItem + 255) / 256);
   hipLaunchKernelGGL(csc_count_kernel, dim3(item_blocks), dim3(256), 0, s, g, d.dim, d.indptr,
                      d.indices, d.flags, d.col_ptr, d.ticket);
   if ((e = hipGetLastError()) != hipSuccess) return e;

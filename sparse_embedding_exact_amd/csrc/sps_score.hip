@@ -111,7 +111,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void sc
   const int32_t Sp = slab_pitch(g.S);  // slab row pitch (items)
   const int32_t Lp = acc_pitch(g.S);   // accumulator row pitch (ints)
 
-  const int32_t *cps = a.col_ptr + sl * (a.dim + 1);
+  const int32_t *cps = a.col_ptr + sl * cp_pitch(a.dim);
   const int32_t cb0 = a.slice_base[sl];
   const int32_t snnz = a.slice_base[sl + 1] - cb0 > 0 ? a.slice_base[sl + 1] - cb0 : 0;
   // light entries of group gi: [ge[gi], ge[gi + 1]) (the rows are consecutive)
