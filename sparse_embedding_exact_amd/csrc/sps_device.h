@@ -50,6 +50,43 @@ __device__ __forceinline__ T block_incl_scan(T v, T *ws, T *total) {
   return x + off;
 }
 
+// Inclusive scan of a 32-bit int over a wave64 with DPP lane moves (no LDS
+// traffic): a Hillis-Steele scan inside each row of 16 lanes (row_shr 1, 2,
+// 4, 8), then row 1 adds lane 15 and row 3 lane 47 (row_bcast:15), and rows
+// 2 and 3 add lane 31 (row_bcast:31). Lanes a move has no source for get 0.
+__device__ __forceinline__ int32_t wave_incl_scan_dpp(int32_t x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return x;
+}
+
+// Block-wide inclusive scan of a 32-bit int with one barrier. `ws` is NT/64
+// ints of LDS that the caller must not reuse before another barrier: two
+// calls need a barrier between them (the second would overwrite `ws` while
+// slower waves of the first still read it).
+template <int NT>
+__device__ __forceinline__ int32_t block_incl_scan_1b(int32_t v, int32_t *ws, int32_t *total) {
+  constexpr int NW = NT / 64;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  int32_t x = wave_incl_scan_dpp(v);
+  asm volatile("" : "+v"(x));  // keep the scan, not its partial terms, across the barrier
+  if (lane == 63) ws[w] = x;
+  __syncthreads();
+  int32_t off = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    const int32_t s = ws[i];
+    if (i < w) off += s;
+    tot += s;
+  }
+  *total = tot;
+  return x + off;
+}
+
 // position of d in the ascending list heavy[0..m), or -1
 __device__ __forceinline__ int heavy_slot(const int32_t *__restrict__ heavy, int m, int32_t d) {
   int lo = 0, hi = m;

@@ -6,11 +6,12 @@
 // support divided by both norms), §4.4 (items streamed chunk by chunk),
 // §2.3 (full float32 output, no top-K).
 //
-// One workgroup (512 threads, 8 waves) scores kRows = 16 query rows against
-// one slice (<= 1024 items) of the chunk. LDS holds acc[16][Lp] (Lp = slice
-// rounded up to 128, plus 4 against bank conflicts) as 32-bit fixed point
-// with 30 fraction bits: 64 KiB, so two workgroups share a CU. Workgroups
-// are numbered slice-fastest (see the kernel).
+// One workgroup (512 threads, 8 waves) scores two groups of kRows = 16 query
+// rows, one after the other, against one slice (<= 1024 items) of the chunk.
+// LDS holds acc[16][Lp] (Lp = slice rounded up to 128, plus 4 against bank
+// conflicts) as 32-bit fixed point with 30 fraction bits: 64 KiB, so two
+// workgroups share a CU. Workgroups are numbered slice-fastest (see the
+// kernel).
 //
 // Why fixed point: on gfx950 the LDS float atomic (ds_add_f32) sustains about
 // 0.3 updates per CU cycle, the 32-bit integer one (ds_add_u32) about 14.
@@ -19,12 +20,14 @@
 // below 2^30 plus rounding, inside int32. Integer addition is exact and
 // order independent: the result does not depend on how waves interleave.
 //
-// Dense part (heavy dims): v_mfma_f32_16x16x4f32 (A[i][k] from lane i + 16k,
-// B[k][j] from lane j + 16k, lane l receiving rows 4(l/16)..+3 of column
-// l%16). A is the 16 rows' values on 4 heavy dims, B 4 dims x 16 items of
-// the slice's dense slab, so each slab value loaded feeds all 16 rows. fp32
-// products and sums in a fixed order over the dims; the sums, rounded once
-// to fixed point, start the accumulators.
+// Dense part (heavy dims): v_mfma_f32_16x16x32_f16 on values split in two
+// fp16 halves (hi, lo) after scaling by 256, so the dot of two values is
+// hi.hi + (hi.lo + lo.hi) / 2048 up to 3 * 2^-22 of |x y| (the lo.lo term is
+// dropped). A is the 16 rows' values on the 32 heavy dims, B the slab's 16
+// items of a tile, both stored in the MFMA operand order (A[i][k] in lane
+// i + 16 (k / 8), element k % 8). Each slab value loaded feeds all 16 rows of
+// both row groups. fp32 sums, rounded once to fixed point, start the
+// accumulators.
 //
 // Sparse part (all other dims): the 16 rows' light entries (dim, value,
 // row) are taken in batches of 1024, two per thread; each looks up its
@@ -122,47 +125,63 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void sc
     ge[gi] = a.lptr[q < a.n_q ? q : a.n_q];
   }
 
-  // Batch descriptors (see the sparse part), two entries per thread. Three
-  // stages, so that other loads can be issued between them and no arithmetic
-  // on a loaded value forces an early wait: entry loads (raw), then the
-  // dependent posting-range loads (raw), then the range arithmetic.
-  int32_t b_s[2], b_L[2], b_row[2];
-  float b_qv[2];
-  int32_t r_d[2], r_lo[2], r_hi[2];
-  uint32_t r_qv[2], r_row[2];
-  bool r_ok[2];
-  auto fetch_entries = [&](int32_t eb, int32_t ee) {
+  // Batch descriptors (see the sparse part): entries eb + t and eb + t + NT
+  // of a batch [eb, ee). Three stages, so that other loads can be issued
+  // between them and no arithmetic on a loaded value forces an early wait:
+  // the dims; then the dependent posting ranges, with the value and row;
+  // then the range arithmetic. The first batch of each group is fetched at
+  // the start, so both groups' lookups overlap the dense part.
+  struct Raw {
+    int32_t d[2], lo[2], hi[2];
+    uint32_t qv[2], row[2];
+    bool ok[2];
+  };
+  struct Desc {
+    int32_t s[2], L[2], row[2];
+    float qv[2];
+  };
+  // a readable entry (the light arrays hold at least one) when e is past the end
+  auto entry = [&](int32_t eb, int32_t ee, int i) {
+    const int32_t e = eb + t + i * NT;
+    return e < ee ? e : (ee > 0 ? ee - 1 : 0);
+  };
+  auto fetch_dims = [&](Raw &r, int32_t eb, int32_t ee) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int32_t e = eb + t + i * NT;
-      r_ok[i] = e < ee;
-      // a readable entry (the light arrays hold at least one) when e is past the end
-      const int32_t ec = e < ee ? e : (ee > 0 ? ee - 1 : 0);
-      r_d[i] = a.ldim[ec];
-      r_qv[i] = __float_as_uint(a.lval[ec]);
-      r_row[i] = a.lrow[ec];
+      r.ok[i] = eb + t + i * NT < ee;
+      r.d[i] = a.ldim[entry(eb, ee, i)];
     }
   };
-  auto fetch_ranges = [&]() {
+  // (the dim is checked here, so that it is not kept until the arithmetic)
+  auto fetch_ranges = [&](Raw &r, int32_t eb, int32_t ee) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int32_t d = (uint32_t)r_d[i] < (uint64_t)a.dim ? r_d[i] : 0;
-      r_lo[i] = cps[d];
-      r_hi[i] = cps[d + 1];
+      const bool dok = (uint32_t)r.d[i] < (uint64_t)a.dim;
+      r.ok[i] = r.ok[i] && dok;
+      const int32_t d = dok ? r.d[i] : 0;
+      r.lo[i] = cps[d];
+      r.hi[i] = cps[d + 1];
+      const int32_t ec = entry(eb, ee, i);
+      r.qv[i] = __float_as_uint(a.lval[ec]);
+      r.row[i] = a.lrow[ec];
     }
   };
-  auto finish_ranges = [&]() {
+  auto finish_ranges = [&](const Raw &r, Desc &b) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const bool ok = r_ok[i] && (uint32_t)r_d[i] < (uint64_t)a.dim;
-      b_s[i] = ok ? (int32_t)clamp64(r_lo[i], 0, snnz) : 0;
-      const int32_t L = ok ? (int32_t)clamp64(r_hi[i], b_s[i], snnz) - b_s[i] : 0;
-      b_L[i] = L < kSliceMax ? L : kSliceMax;  // a slice holds a dim once per item
-      b_row[i] = (int32_t)(r_row[i] & (kRows - 1));
-      b_qv[i] = __uint_as_float(r_qv[i]);
+      const bool ok = r.ok[i];
+      b.s[i] = ok ? (int32_t)clamp64(r.lo[i], 0, snnz) : 0;
+      const int32_t L = ok ? (int32_t)clamp64(r.hi[i], b.s[i], snnz) - b.s[i] : 0;
+      b.L[i] = L < kSliceMax ? L : kSliceMax;  // a slice holds a dim once per item
+      b.row[i] = (int32_t)(r.row[i] & (kRows - 1));
+      b.qv[i] = __uint_as_float(r.qv[i]);
     }
   };
-  fetch_entries(ge[0], ge[1]);
+  auto batch_end = [&](int32_t eb, int32_t ee) { return ee - eb < kBatch ? ee : eb + kBatch; };
+  Raw r0, r1;
+  const int32_t f0 = batch_end(ge[0], ge[1]), f1 = batch_end(ge[1], ge[2]);
+  fetch_dims(r0, ge[0], f0);
+  fetch_dims(r1, ge[1], f1);
 
   // ---- dense part: heavy dims on the matrix cores ----
   // Wave w owns items [128 w, 128 w + 128) of the slice as 8 tiles of 16.
@@ -173,19 +192,47 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void sc
   // accumulators' initial value: group 0's is written to LDS at once, group
   // 1's waits in registers. Each slab tile loaded serves both groups.
   const int32_t wcol = wv * 128;
-  // Load order matters: the vector-memory counter drains in issue order, so
-  // the slab loads go out after the entry loads and before the dependent
-  // range loads; the MFMAs then wait for the slab only, and the range
-  // lookups (random, often an L2 miss) overlap the dense work.
-  constexpr int kTiles = 8;
-  h16x8 a_hi[kGroups], a_lo[kGroups], b_hi[kTiles], b_lo[kTiles];
+  constexpr int kTiles = 8, kHalf = 4;  // tiles per wave, loaded in two halves
+  h16x8 a_hi[kGroups], a_lo[kGroups], b_hi[kHalf], b_lo[kHalf];
   int32_t dpend[kTiles][4];  // group 1's initial values, fixed point
   const bool wdense = DENSE && wcol < Sp;
-  if (DENSE) {  // unconditional (a wave past the slice loads tile 0 and drops it), so that
-                // the counter waits below see one path
-    // A: lane l holds row l%16, dims 8(l/16)..+7 (hi, lo); B: item l%16 of
-    // the tile, the same dims. Both are tiles in the MFMA operand order.
-    static_assert(kTileHalves == 2 * 64 * 8, "a tile is one 16-byte load per lane per part");
+  // A: lane l holds row l%16, dims 8(l/16)..+7 (hi, lo); B: item l%16 of the
+  // tile, the same dims. Both are tiles in the MFMA operand order. The loads
+  // are unconditional (a wave past the slice loads tile 0 and drops it), so
+  // that the counter waits below see one path.
+  static_assert(kTileHalves == 2 * 64 * 8, "a tile is one 16-byte load per lane per part");
+  const h16x8 *st = reinterpret_cast<const h16x8 *>(
+      a.slab + (sl * (int64_t)a.pitch + (wdense ? wcol : 0)) * kHeavyRec);
+  auto load_half = [&](int h) {
+#pragma unroll
+    for (int tt = 0; tt < kHalf; ++tt) {
+      b_hi[tt] = st[(h * kHalf + tt) * 128 + lane];
+      b_lo[tt] = st[(h * kHalf + tt) * 128 + 64 + lane];
+    }
+  };
+  // lane l holds rows 4(l/16) + i of item 16 tt + l%16
+  int *const dbase = acc + (4 * (lane >> 4)) * Lp + wcol + (lane & 15);
+  auto mfma_half = [&](int h) {
+    if (!wdense) return;
+#pragma unroll
+    for (int tt = 0; tt < kHalf; ++tt) {
+      const int T = h * kHalf + tt;
+#pragma unroll
+      for (int gi = 0; gi < kGroups; ++gi) {
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        const f32x4 mn = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_hi[gi], b_hi[tt], z, 0, 0, 0);
+        f32x4 cr = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_hi[gi], b_lo[tt], z, 0, 0, 0);
+        cr = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_lo[gi], b_hi[tt], cr, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int v = round_fix((mn[i] + cr[i] * (1.0f / kLoScale)) * kDenseToFix);
+          if (gi == 0) dbase[i * Lp + 16 * T] = v;
+          else dpend[T][i] = v;
+        }
+      }
+    }
+  };
+  if (DENSE) {
 #pragma unroll
     for (int gi = 0; gi < kGroups; ++gi) {
       const h16x8 *qt = reinterpret_cast<const h16x8 *>(
@@ -193,44 +240,30 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void sc
       a_hi[gi] = qt[lane];
       a_lo[gi] = qt[64 + lane];
     }
-    const h16x8 *st = reinterpret_cast<const h16x8 *>(
-        a.slab + (sl * (int64_t)a.pitch + (wdense ? wcol : 0)) * kHeavyRec);
-#pragma unroll
-    for (int tt = 0; tt < kTiles; ++tt) {
-      b_hi[tt] = st[tt * 128 + lane];
-      b_lo[tt] = st[tt * 128 + 64 + lane];
-    }
+    load_half(0);
   }
   __builtin_amdgcn_sched_barrier(0);
-  fetch_ranges();
-  __builtin_amdgcn_sched_barrier(0);
-  // lane l holds rows 4(l/16) + i of item 16 tt + l%16
-  int *const dbase = acc + (4 * (lane >> 4)) * Lp + wcol + (lane & 15);
+  // Load order matters: the vector-memory counter drains in issue order.
+  // The first half's products wait for its slab tiles (and the dims issued
+  // before them); the second half's tiles go out before the dependent range
+  // lookups, so its products wait for the slab only and the lookups (random,
+  // often an L2 miss) overlap them.
   if (DENSE) {
-    if (wdense) {
-#pragma unroll
-      for (int tt = 0; tt < kTiles; ++tt) {
-#pragma unroll
-        for (int gi = 0; gi < kGroups; ++gi) {
-          const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-          const f32x4 mn = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_hi[gi], b_hi[tt], z, 0, 0, 0);
-          f32x4 cr = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_hi[gi], b_lo[tt], z, 0, 0, 0);
-          cr = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_lo[gi], b_hi[tt], cr, 0, 0, 0);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int v = round_fix((mn[i] + cr[i] * (1.0f / kLoScale)) * kDenseToFix);
-            if (gi == 0) dbase[i * Lp + 16 * tt] = v;
-            else dpend[tt][i] = v;
-          }
-        }
-      }
-    }
+    mfma_half(0);
   } else {
     int4 *acc4 = reinterpret_cast<int4 *>(acc);
     for (int k = t; k < kRows * Lp / 4; k += NT) acc4[k] = make_int4(0, 0, 0, 0);
   }
   __builtin_amdgcn_sched_barrier(0);
-  finish_ranges();
+  if (DENSE) load_half(1);
+  fetch_ranges(r0, ge[0], f0);
+  fetch_ranges(r1, ge[1], f1);
+  __builtin_amdgcn_sched_barrier(0);
+  if (DENSE) mfma_half(1);
+  __builtin_amdgcn_sched_barrier(0);
+  Desc cur, nxt;  // first batch of this group and of the next
+  finish_ranges(r0, cur);
+  finish_ranges(r1, nxt);
   __syncthreads();  // accumulators initialised before any sparse update
 
   const uint2 *__restrict__ ppost = a.post + cb0;
@@ -259,33 +292,24 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void sc
     // ---- sparse part: the rows' light entries, batch by batch ----
     const int32_t e1 = ge[gi + 1];
     for (int32_t eb = ge[gi]; eb < e1; eb += kBatch) {
+      // this batch's lists: the group's first batch was fetched at the start
+      Desc c;
+      if (eb == ge[gi]) {
+        c = cur;
+      } else {
+        Raw r;
+        const int32_t ee = batch_end(eb, e1);
+        fetch_dims(r, eb, ee);
+        fetch_ranges(r, eb, ee);
+        finish_ranges(r, c);
+      }
       int32_t nseg[2];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) nseg[i] = (b_L[i] + kSeg - 1) / kSeg;
+      for (int i = 0; i < 2; ++i) nseg[i] = (c.L[i] + kSeg - 1) / kSeg;
       int32_t total;
-      const int32_t pend = block_incl_scan<NT>(nseg[0] + nseg[1], ws, &total);  // barrier inside
+      // (a barrier inside; the previous call is behind the barriers of its round)
+      const int32_t pend = block_incl_scan_1b<NT>(nseg[0] + nseg[1], ws, &total);
       const int32_t sp[2] = {pend - nseg[0] - nseg[1], pend - nseg[1]};
-      // this batch's lists, kept while the next batch's descriptors load
-      int32_t c_s[2], c_L[2], c_off[2];
-      uint32_t c_qv[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        c_s[i] = b_s[i];
-        c_L[i] = b_L[i];
-        c_off[i] = b_row[i] * Lp;
-        c_qv[i] = __float_as_uint(b_qv[i]);
-      }
-      // the next batch's descriptors (this group's, else the next group's
-      // first), in flight during this one
-      if (eb + kBatch < e1) {
-        fetch_entries(eb + kBatch, e1);
-        fetch_ranges();
-        finish_ranges();
-      } else if (gi + 1 < ng) {
-        fetch_entries(ge[gi + 1], ge[gi + 2]);
-        fetch_ranges();
-        finish_ranges();
-      }
       for (int32_t r0 = 0; r0 < total; r0 += kSegMax) {
         // the segments of this round that belong to this thread's lists
 #pragma unroll
@@ -294,10 +318,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void sc
           const int32_t se = sp[i] + nseg[i] < r0 + kSegMax ? sp[i] + nseg[i] : r0 + kSegMax;
           for (int32_t sg = sb0; sg < se; ++sg) {
             const int32_t j0 = (sg - sp[i]) * kSeg;
-            const int32_t n = c_L[i] - j0 < kSeg ? c_L[i] - j0 : kSeg;
-            s_spos[sg - r0] = (uint32_t)(c_s[i] + j0);
-            s_sqv[sg - r0] = c_qv[i];
-            s_smeta[sg - r0] = (uint32_t)n | ((uint32_t)c_off[i] << 7);  // byte offset << 5
+            const int32_t n = c.L[i] - j0 < kSeg ? c.L[i] - j0 : kSeg;
+            s_spos[sg - r0] = (uint32_t)(c.s[i] + j0);
+            s_sqv[sg - r0] = __float_as_uint(c.qv[i]);
+            s_smeta[sg - r0] = (uint32_t)n | ((uint32_t)(c.row[i] * Lp) << 7);  // byte offset << 5
           }
         }
         const int32_t nr = total - r0 < kSegMax ? total - r0 : kSegMax;
@@ -340,6 +364,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void sc
         __syncthreads();
       }
     }
+    cur = nxt;
 
     // ---- epilogue: wave w writes rows w, w + NW, ... of the group ----
 #pragma unroll
