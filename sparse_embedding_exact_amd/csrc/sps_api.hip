@@ -98,7 +98,7 @@ ItemsLayout items_layout(const sps::Geom &g, int64_t dim, int64_t nnz, bool dens
   Layout p;
   L.inv = p.add(g.n_items, 4);
   L.colp = p.add((uint64_t)ns * (uint64_t)sps::cp_pitch(dim), 4);
-  L.post = p.add(nnz, 8);
+  L.post = p.add(nnz + sps::kPostPad, 8);
   L.sbase = p.add(ns + 1, 4);
   L.heavy = p.add(sps::kHeavyMax + 1, 4);
   L.slab = p.add(dense ? (uint64_t)ns * sps::kHeavyRec * (uint64_t)sps::slab_pitch(g.S) : 0, 2);

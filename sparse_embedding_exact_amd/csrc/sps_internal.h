@@ -19,6 +19,9 @@ constexpr int kFlagsInts = 16;
 constexpr int kRows = 16;
 constexpr int kSliceMax = 1024;
 constexpr int kScoreThreads = 512;
+// zeroed postings past the end of the posting array: the score kernel reads
+// postings in pairs, so the pair of a list's last posting stays readable
+constexpr int kPostPad = 2;
 
 // Dense path for heavy dims: at most kHeavyMax dims (a multiple of 4, the
 // MFMA depth) whose item document frequency is at least n_items /
@@ -123,7 +126,7 @@ struct ItemsDev {
   const float *values;
   float *inv_norm;      // persistent, n_items
   int32_t *col_ptr;     // persistent, num_slices * cp_pitch(dim)
-  uint2 *post;          // persistent, nnz: (slice-local item id, value bits)
+  uint2 *post;          // persistent, nnz + kPostPad: (slice-local item id, value bits)
   int32_t *slice_base;  // persistent, num_slices + 1
   int32_t *heavy;       // persistent, kHeavyMax + 1: heavy dims ascending, then their count
   uint16_t *slab;       // persistent, [num_slices][pitch / 16 tiles] split fp16 (dense only)

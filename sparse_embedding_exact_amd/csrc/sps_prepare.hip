@@ -524,6 +524,8 @@ hipError_t launch_prepare_items(const ItemsDev &d, hipStream_t s) {
   if (e != hipSuccess) return e;
   e = launch_fill_i32(d.heavy, kHeavyMax + 1, 0, s);
   if (e != hipSuccess) return e;
+  e = launch_fill_i32(reinterpret_cast<int32_t *>(d.post + d.nnz), 2 * kPostPad, 0, s);
+  if (e != hipSuccess) return e;
   if (g.n_items == 0) return hipSuccess;
   if (d.dense) {
     e = launch_fill_i32(d.gdf, d.dim, 0, s);

@@ -33,11 +33,13 @@
 // row) are taken in batches of 1024, two per thread; each looks up its
 // posting list [col_ptr[d], col_ptr[d+1]) in the slice. Lists are cut into
 // segments of 16 postings, a block scan numbers the segments and an LDS
-// table records each one (first posting, value, row, length), so 16 lanes
-// take one segment with no search: lane i handles posting i of it, loads
-// (item, w) with one 8-byte load and applies acc[row][item] += rn(fl32(qs *
-// w)) (ds_add_u32), with qs = fl32(q_d / |q|) * 2^30, w = fl32(i_d / |i|)
-// and rn rounding to the nearest integer (ties up).
+// table records each one (first posting, value, row, length), so 8 lanes
+// take one segment with no search: lane i handles postings 2i and 2i + 1 of
+// it, loads both (item, w) pairs with one 16-byte load and applies
+// acc[row][item] += rn(fl32(qs * w)) (ds_add_u32) for each, with qs =
+// fl32(q_d / |q|) * 2^30, w = fl32(i_d / |i|) and rn rounding to the nearest
+// integer (ties up). (The vector-memory data path, not the LDS atomics, is
+// what limits this loop, so fewer and wider loads pay.)
 //
 // Epilogue: wave w writes rows w and w + 8: out[q, j] = fl32(acc) * 2^-30,
 // 16-byte nontemporal stores when aligned (the scores are not re-read, so
@@ -66,10 +68,13 @@ __device__ __forceinline__ int round_fix(float x) {
   return r;
 }
 
-// load at a 32-bit byte offset from a uniform base (base + offset addressing)
-template <typename T>
-__device__ __forceinline__ T ld_off(const T *base, uint32_t byte_off) {
-  return *reinterpret_cast<const T *>(reinterpret_cast<const char *>(base) + byte_off);
+// two consecutive 8-byte postings (item, value, item, value) with one
+// 16-byte load from an 8-byte aligned address (global memory accesses need
+// only 4-byte alignment on this target)
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_a8 __attribute__((ext_vector_type(4), aligned(8)));
+__device__ __forceinline__ u32x4 ld_pair(const uint2 *base, uint32_t byte_off) {
+  return *reinterpret_cast<const u32x4_a8 *>(reinterpret_cast<const char *>(base) + byte_off);
 }
 
 constexpr int NT = kScoreThreads;
@@ -83,13 +88,13 @@ static_assert(kRows == 16 && kHeavyMax == 32, "one 16x16x32 MFMA tile covers the
 // 16 lanes, described in an LDS table.
 constexpr int kSeg = 16;
 constexpr int kSegMax = 896;         // segments per round
-constexpr int kSegPad = 4 * NW * 8;  // one step of quads past the end (U <= 8)
+constexpr int kSegPad = 8 * NW * 4;  // one step of octets past the end (U <= 4)
 static_assert(kRows * kSliceMax * 4 < (1 << 27), "row byte offset fits the segment record");
 
 template <bool DENSE, int U>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void score_kernel(
     const ScoreArgs a, int vec4) {
-  static_assert(U <= 8, "the segment table pads one step of at most 8 quads per wave");
+  static_assert(8 * NW * U <= kSegPad, "the segment table pads one step of octets per wave");
   extern __shared__ int acc[];
   // segment table of a round: first posting, query value, and the LDS byte
   // offset of the row << 5 | postings in the segment (1..16; 0 pads the
@@ -327,38 +332,46 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void sc
         const int32_t nr = total - r0 < kSegMax ? total - r0 : kSegMax;
         for (int k = t; k < kSegPad; k += NT) s_smeta[nr + k] = 0u;
         __syncthreads();
-        // Wave w takes segment quads w, w + NW, ...; lanes 16i..16i+15 take
-        // segment i of a quad, U quads per step.
-        const int32_t jl = lane & 15;
-        for (int32_t k0 = wv; 4 * k0 < nr; k0 += NW * U) {
+        // Wave w takes segment octets w, w + NW, ...; lanes 8i..8i+7 take
+        // segment i of an octet, two postings per lane (one 16-byte load),
+        // U octets per step.
+        const int32_t jl = 2 * (lane & 7);
+        for (int32_t k0 = wv; 8 * k0 < nr; k0 += NW * U) {
           uint32_t pos[U];
           uint32_t aoff[U];
           float qv[U];
-          bool ok[U];
+          int32_t nn[U];  // postings of the segment from this lane's first on
 #pragma unroll
           for (int u = 0; u < U; ++u) {
             // entries past nr are padding (no postings)
-            const int32_t sg = 4 * (k0 + NW * u) + (lane >> 4);
+            const int32_t sg = 8 * (k0 + NW * u) + (lane >> 3);
             const uint32_t meta = s_smeta[sg];
             const uint32_t sp0 = s_spos[sg];
-            ok[u] = jl < (int32_t)(meta & 31u);
-            pos[u] = ok[u] ? sp0 + jl : 0u;
+            nn[u] = (int32_t)(meta & 31u) - jl;
+            pos[u] = nn[u] > 0 ? sp0 + jl : 0u;
             aoff[u] = meta >> 5;
             qv[u] = __uint_as_float(s_sqv[sg]);
           }
-          uint2 pe[U];
+          // (the posting array holds kPostPad extra entries, so the second
+          // posting of a lane's pair is readable at the end of the array)
+          u32x4 pe[U];
 #pragma unroll
-          for (int u = 0; u < U; ++u) pe[u] = ld_off(ppost, pos[u] * 8u);
+          for (int u = 0; u < U; ++u) pe[u] = ld_pair(ppost, pos[u] * 8u);
           // all U loads are in flight before the first is waited on (keeps the
           // compiler from sinking a load into the masked update below it)
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int u = 0; u < U; ++u) asm volatile("" ::"v"(pe[u].x), "v"(pe[u].y));
+          for (int u = 0; u < U; ++u)
+            asm volatile("" ::"v"(pe[u].x), "v"(pe[u].y), "v"(pe[u].z), "v"(pe[u].w));
 #pragma unroll
           for (int u = 0; u < U; ++u) {
-            if (ok[u] && pe[u].x < (uint32_t)slen)
-              atomicAdd(reinterpret_cast<int *>(reinterpret_cast<char *>(acc) + aoff[u] + 4 * pe[u].x),
+            char *const rbase = reinterpret_cast<char *>(acc) + aoff[u];
+            if (nn[u] > 0 && pe[u].x < (uint32_t)slen)
+              atomicAdd(reinterpret_cast<int *>(rbase + 4 * pe[u].x),
                         round_fix(qv[u] * __uint_as_float(pe[u].y)));
+            if (nn[u] > 1 && pe[u].z < (uint32_t)slen)
+              atomicAdd(reinterpret_cast<int *>(rbase + 4 * pe[u].z),
+                        round_fix(qv[u] * __uint_as_float(pe[u].w)));
           }
         }
         __syncthreads();
@@ -416,10 +429,10 @@ size_t score_lds_bytes(int32_t S) {
 static int env_unroll() {
   static int v = -1;
   if (v < 0) {
-    v = 4;
+    v = 2;
     if (const char *e = getenv("SPS_SCORE_UNROLL")) {
       const int x = atoi(e);
-      if (x == 2 || x == 4 || x == 8) v = x;
+      if (x == 2 || x == 4) v = x;
     }
   }
   return v;
@@ -448,11 +461,9 @@ hipError_t launch_score(const ScoreArgs &a, hipStream_t s) {
   const int u = env_unroll();
   hipError_t e;
   if (a.dense) {
-    e = u == 8 ? launch_t<true, 8>(a, s)
-               : (u == 2 ? launch_t<true, 2>(a, s) : launch_t<true, 4>(a, s));
+    e = u == 4 ? launch_t<true, 4>(a, s) : launch_t<true, 2>(a, s);
   } else {
-    e = u == 8 ? launch_t<false, 8>(a, s)
-               : (u == 2 ? launch_t<false, 2>(a, s) : launch_t<false, 4>(a, s));
+    e = u == 4 ? launch_t<false, 4>(a, s) : launch_t<false, 2>(a, s);
   }
   if (e != hipSuccess) return e;
   if (a.row_sums != nullptr && a.g.n_sub > 1) {
