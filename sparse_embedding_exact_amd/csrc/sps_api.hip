@@ -118,7 +118,7 @@ ItemsLayout items_layout(const sps::Geom &g, int64_t dim, int64_t nnz, bool dens
 }
 
 struct QueriesLayout {
-  size_t flags, inv, norm64, lptr, ldim, lval, lrow, qh, rspart, total;
+  size_t flags, inv, norm64, lptr, lrec, qh, rspart, total;
   bool overflow;
 };
 
@@ -132,9 +132,7 @@ QueriesLayout queries_layout(int64_t n, int64_t nnz, int32_t n_sub, bool dense) 
   L.lptr = p.add(n + 1, 4);
   // at least one light entry each: the score kernel may read entry 0 of an
   // empty batch (and ignores it)
-  L.ldim = p.add(nnz > 0 ? nnz : 1, 4);
-  L.lval = p.add(nnz > 0 ? nnz : 1, 4);
-  L.lrow = p.add(nnz > 0 ? nnz : 1, 1);
+  L.lrec = p.add(nnz > 0 ? nnz : 1, 16);
   L.qh = p.add(dense ? (uint64_t)ng * sps::kHeavyRec * sps::kRows : 0, 2);
   L.rspart = p.add(n_sub > 1 ? (uint64_t)n_sub * (uint64_t)n : 0, 8);
   L.total = p.off;
@@ -165,9 +163,8 @@ struct sps_queries {
   bool dense;
   const sps_items *items;  // the corpus the queries were prepared for
   float *inv_norm;
-  int32_t *lptr, *ldim;
-  float *lval;
-  uint8_t *lrow;
+  int32_t *lptr;
+  uint4 *lrec;
   uint16_t *qh;
   double *rs_part;
 };
@@ -389,9 +386,7 @@ sps_status sps_prepare_queries(const sps_csr *queries, const sps_items *items, v
   d.inv_norm = at<float>(workspace, L.inv);
   d.norm64 = at<double>(workspace, L.norm64);
   d.lptr = at<int32_t>(workspace, L.lptr);
-  d.ldim = at<int32_t>(workspace, L.ldim);
-  d.lval = at<float>(workspace, L.lval);
-  d.lrow = at<uint8_t>(workspace, L.lrow);
+  d.lrec = at<uint4>(workspace, L.lrec);
   d.qh = dense ? at<uint16_t>(workspace, L.qh) : nullptr;
   sps_queries *h = new (std::nothrow) sps_queries;
   if (!h) return fail(SPS_ERR_INVALID_ARGUMENT, "out of host memory");
@@ -409,9 +404,7 @@ sps_status sps_prepare_queries(const sps_csr *queries, const sps_items *items, v
   h->items = items;
   h->inv_norm = d.inv_norm;
   h->lptr = d.lptr;
-  h->ldim = d.ldim;
-  h->lval = d.lval;
-  h->lrow = d.lrow;
+  h->lrec = d.lrec;
   h->qh = d.qh;
   h->rs_part = items->g.n_sub > 1 ? at<double>(workspace, L.rspart) : nullptr;
   *out = h;
@@ -455,9 +448,7 @@ static sps_status score_one(const sps_queries *q, const sps_items *items, int32_
   a.chunk = chunk;
   a.dense = q->dense && items->dense;
   a.lptr = q->lptr;
-  a.ldim = q->ldim;
-  a.lval = q->lval;
-  a.lrow = q->lrow;
+  a.lrec = q->lrec;
   a.qh = q->qh;
   a.col_ptr = items->col_ptr;
   a.post = items->post;

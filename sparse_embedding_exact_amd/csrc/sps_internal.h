@@ -153,9 +153,7 @@ struct QueriesDev {
   float *inv_norm;       // n_rows
   double *norm64;        // n_rows
   int32_t *lptr;         // n_rows + 1: light (non-heavy) entries per row, prefix
-  int32_t *ldim;         // nnz
-  float *lval;           // nnz: fl32(q / |q|) * 2^30
-  uint8_t *lrow;         // nnz: row within its group of kRows
+  uint4 *lrec;           // nnz: (dim, bits of fl32(q / |q|) * 2^30, row within its group, 0)
   uint16_t *qh;          // [n_groups] tiles of split fp16: fl32(q / |q|) on heavy dims
 };
 hipError_t launch_prepare_queries(const QueriesDev &d, hipStream_t s);
@@ -167,9 +165,8 @@ struct ScoreArgs {
   int32_t n_groups;
   int32_t chunk;
   bool dense;
-  const int32_t *lptr, *ldim;
-  const float *lval;
-  const uint8_t *lrow;
+  const int32_t *lptr;
+  const uint4 *lrec;          // light entries: (dim, value bits, row in group, 0)
   const uint16_t *qh;         // [row groups] tiles of split fp16 (dense only)
   const int32_t *col_ptr;     // all slices
   const uint2 *post;          // all slices: (slice-local item id, value bits)

@@ -569,10 +569,10 @@ hipError_t launch_prepare_items(const ItemsDev &d, hipStream_t s) {
 // Queries. Each row is normalised by its float64 norm (§5.2) and rounded
 // once to fp32: qn = fl32(q_d / |q|). Heavy dims (dense path) go to the
 // row's split-fp16 record in qh (rows padded to a multiple of kRows); the
-// other entries form the
-// "light" CSR (same row order) with values qn * 2^30 (exact: a power of two),
-// the scale of the fixed-point accumulators, and the row's position in its
-// group.
+// other entries form the "light" CSR (same row order) of 16-byte records
+// (dim, value, row's position in its group, 0), one load each in the score
+// kernel, with values qn * 2^30 (exact: a power of two), the scale of the
+// fixed-point accumulators.
 // ---------------------------------------------------------------------------
 
 template <bool FILL>
@@ -580,8 +580,7 @@ __global__ __launch_bounds__(256) void light_split_kernel(
     int64_t n_rows, const int32_t *__restrict__ indptr, const int32_t *__restrict__ indices,
     const float *__restrict__ values, const double *__restrict__ norm64,
     const int32_t *__restrict__ flags, const int32_t *__restrict__ heavy,
-    int32_t *__restrict__ lptr, int32_t *__restrict__ ldim, float *__restrict__ lval,
-    uint8_t *__restrict__ lrow, uint16_t *__restrict__ qh) {
+    int32_t *__restrict__ lptr, uint4 *__restrict__ lrec, uint16_t *__restrict__ qh) {
   const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (q >= n_rows) return;
   const int m = heavy != nullptr ? heavy[kHeavyMax] : 0;
@@ -606,9 +605,7 @@ __global__ __launch_bounds__(256) void light_split_kernel(
         tile[heavy_tile_index((int)(q % kRows), hs, 0)] = hi;
         tile[heavy_tile_index((int)(q % kRows), hs, 1)] = lo;
       } else {
-        ldim[out] = d;
-        lval[out] = v * kFixScale;
-        lrow[out] = (uint8_t)rq;
+        lrec[out] = make_uint4((uint32_t)d, __float_as_uint(v * kFixScale), (uint32_t)rq, 0u);
       }
     }
     if (hs < 0) {
@@ -636,15 +633,15 @@ hipError_t launch_prepare_queries(const QueriesDev &d, hipStream_t s) {
   const int32_t *heavy = d.dense ? d.heavy : nullptr;
   const unsigned blocks = (unsigned)((d.n_rows + 255) / 256);
   hipLaunchKernelGGL(light_split_kernel<false>, dim3(blocks), dim3(256), 0, s, d.n_rows,
-                     d.indptr, d.indices, d.values, d.norm64, d.flags, heavy, d.lptr, d.ldim,
-                     d.lval, d.lrow, d.qh);
+                     d.indptr, d.indices, d.values, d.norm64, d.flags, heavy, d.lptr, d.lrec,
+                     d.qh);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(scan_inplace_kernel<1024>, dim3(1), dim3(1024), 0, s, d.lptr,
                      d.n_rows + 1);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(light_split_kernel<true>, dim3(blocks), dim3(256), 0, s, d.n_rows,
-                     d.indptr, d.indices, d.values, d.norm64, d.flags, heavy, d.lptr, d.ldim,
-                     d.lval, d.lrow, d.qh);
+                     d.indptr, d.indices, d.values, d.norm64, d.flags, heavy, d.lptr, d.lrec,
+                     d.qh);
   return hipGetLastError();
 }
 

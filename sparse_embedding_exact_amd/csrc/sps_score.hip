@@ -133,42 +133,36 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void sc
   // Batch descriptors (see the sparse part): entries eb + t and eb + t + NT
   // of a batch [eb, ee). Three stages, so that other loads can be issued
   // between them and no arithmetic on a loaded value forces an early wait:
-  // the dims; then the dependent posting ranges, with the value and row;
+  // the entry records (dim, value, row); then the dependent posting ranges;
   // then the range arithmetic. The first batch of each group is fetched at
   // the start, so both groups' lookups overlap the dense part.
   struct Raw {
-    int32_t d[2], lo[2], hi[2];
-    uint32_t qv[2], row[2];
+    uint4 rec[2];  // (dim, value bits, row in group, 0)
+    int32_t lo[2], hi[2];
     bool ok[2];
   };
   struct Desc {
     int32_t s[2], L[2], row[2];
     float qv[2];
   };
-  // a readable entry (the light arrays hold at least one) when e is past the end
-  auto entry = [&](int32_t eb, int32_t ee, int i) {
-    const int32_t e = eb + t + i * NT;
-    return e < ee ? e : (ee > 0 ? ee - 1 : 0);
-  };
-  auto fetch_dims = [&](Raw &r, int32_t eb, int32_t ee) {
+  auto fetch_entries = [&](Raw &r, int32_t eb, int32_t ee) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      r.ok[i] = eb + t + i * NT < ee;
-      r.d[i] = a.ldim[entry(eb, ee, i)];
+      const int32_t e = eb + t + i * NT;
+      r.ok[i] = e < ee;
+      // a readable entry (the light arrays hold at least one) when e is past the end
+      r.rec[i] = a.lrec[e < ee ? e : (ee > 0 ? ee - 1 : 0)];
     }
   };
   // (the dim is checked here, so that it is not kept until the arithmetic)
-  auto fetch_ranges = [&](Raw &r, int32_t eb, int32_t ee) {
+  auto fetch_ranges = [&](Raw &r) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const bool dok = (uint32_t)r.d[i] < (uint64_t)a.dim;
+      const bool dok = r.rec[i].x < (uint64_t)a.dim;
       r.ok[i] = r.ok[i] && dok;
-      const int32_t d = dok ? r.d[i] : 0;
+      const int32_t d = dok ? (int32_t)r.rec[i].x : 0;
       r.lo[i] = cps[d];
       r.hi[i] = cps[d + 1];
-      const int32_t ec = entry(eb, ee, i);
-      r.qv[i] = __float_as_uint(a.lval[ec]);
-      r.row[i] = a.lrow[ec];
     }
   };
   auto finish_ranges = [&](const Raw &r, Desc &b) {
@@ -178,15 +172,15 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void sc
       b.s[i] = ok ? (int32_t)clamp64(r.lo[i], 0, snnz) : 0;
       const int32_t L = ok ? (int32_t)clamp64(r.hi[i], b.s[i], snnz) - b.s[i] : 0;
       b.L[i] = L < kSliceMax ? L : kSliceMax;  // a slice holds a dim once per item
-      b.row[i] = (int32_t)(r.row[i] & (kRows - 1));
-      b.qv[i] = __uint_as_float(r.qv[i]);
+      b.row[i] = (int32_t)(r.rec[i].z & (kRows - 1));
+      b.qv[i] = __uint_as_float(r.rec[i].y);
     }
   };
   auto batch_end = [&](int32_t eb, int32_t ee) { return ee - eb < kBatch ? ee : eb + kBatch; };
   Raw r0, r1;
   const int32_t f0 = batch_end(ge[0], ge[1]), f1 = batch_end(ge[1], ge[2]);
-  fetch_dims(r0, ge[0], f0);
-  fetch_dims(r1, ge[1], f1);
+  fetch_entries(r0, ge[0], f0);
+  fetch_entries(r1, ge[1], f1);
 
   // ---- dense part: heavy dims on the matrix cores ----
   // Wave w owns items [128 w, 128 w + 128) of the slice as 8 tiles of 16.
@@ -237,22 +231,33 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void sc
       }
     }
   };
+  // The A tiles of both groups (4 KiB) are loaded once per workgroup by the
+  // first 256 threads and shared through LDS (the segment table's space,
+  // unused until the sparse part), not loaded by every wave.
+  static_assert(kGroups * kTileHalves * 2 <= (kSegMax + kSegPad) * 4, "A tiles fit the staging");
+  h16x8 *const astage = reinterpret_cast<h16x8 *>(s_spos);
+  h16x8 aq;
+  if (DENSE && t < kGroups * 128) {
+    const int gi = t >> 7;
+    aq = reinterpret_cast<const h16x8 *>(
+        a.qh + (grp0 + (gi < ng ? gi : 0)) * (int64_t)kTileHalves)[t & 127];
+  }
+  if (DENSE) load_half(0);
+  __builtin_amdgcn_sched_barrier(0);
   if (DENSE) {
+    if (t < kGroups * 128) astage[t] = aq;
+    __syncthreads();
 #pragma unroll
     for (int gi = 0; gi < kGroups; ++gi) {
-      const h16x8 *qt = reinterpret_cast<const h16x8 *>(
-          a.qh + (grp0 + (gi < ng ? gi : 0)) * (int64_t)kTileHalves);
-      a_hi[gi] = qt[lane];
-      a_lo[gi] = qt[64 + lane];
+      a_hi[gi] = astage[gi * 128 + lane];
+      a_lo[gi] = astage[gi * 128 + 64 + lane];
     }
-    load_half(0);
   }
-  __builtin_amdgcn_sched_barrier(0);
   // Load order matters: the vector-memory counter drains in issue order.
-  // The first half's products wait for its slab tiles (and the dims issued
-  // before them); the second half's tiles go out before the dependent range
-  // lookups, so its products wait for the slab only and the lookups (random,
-  // often an L2 miss) overlap them.
+  // The first half's products wait for its slab tiles (and the entries
+  // issued before them); the second half's tiles go out before the dependent
+  // range lookups, so its products wait for the slab only and the lookups
+  // (random, often an L2 miss) overlap them.
   if (DENSE) {
     mfma_half(0);
   } else {
@@ -261,8 +266,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void sc
   }
   __builtin_amdgcn_sched_barrier(0);
   if (DENSE) load_half(1);
-  fetch_ranges(r0, ge[0], f0);
-  fetch_ranges(r1, ge[1], f1);
+  fetch_ranges(r0);
+  fetch_ranges(r1);
   __builtin_amdgcn_sched_barrier(0);
   if (DENSE) mfma_half(1);
   __builtin_amdgcn_sched_barrier(0);
@@ -304,8 +309,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void sc
       } else {
         Raw r;
         const int32_t ee = batch_end(eb, e1);
-        fetch_dims(r, eb, ee);
-        fetch_ranges(r, eb, ee);
+        fetch_entries(r, eb, ee);
+        fetch_ranges(r);
         finish_ranges(r, c);
       }
       int32_t nseg[2];
