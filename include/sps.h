@@ -32,7 +32,8 @@
  *    On an error no work has been enqueued, and sps_last_error_message()
  *    (thread-local) holds a detail string.
  *  - Sizes are 64-bit on the interface; row counts, nnz and dims must be
- *    below 2^31 (SPS_ERR_OVERFLOW otherwise).
+ *    below 2^31, and the item nnz below 2^29 - 64 (postings are addressed
+ *    with 32-bit byte offsets) (SPS_ERR_OVERFLOW otherwise).
  *  - Input CSR must be canonical: indptr[0] = 0, non-decreasing,
  *    indptr[n_rows] = nnz, column indices strictly ascending within a row
  *    and inside [0, n_cols), values finite (§3.1 note: the merge needs

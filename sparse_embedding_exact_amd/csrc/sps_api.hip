@@ -199,8 +199,8 @@ sps_status sps_items_workspace_size(int64_t n_items, int64_t dim, int64_t nnz,
     return fail(SPS_ERR_INVALID_ARGUMENT, "chunk_size must be in [1, %d]", kMaxChunk);
   if (n_items >= kI32Max || dim >= kI32Max || nnz >= kI32Max)
     return fail(SPS_ERR_OVERFLOW, "sizes must be below 2^31");
-  if (nnz >= (1ll << 30))
-    return fail(SPS_ERR_OVERFLOW, "item nnz must be below 2^30 (32-bit byte offsets)");
+  if (nnz >= (1ll << 29) - 64)
+    return fail(SPS_ERR_OVERFLOW, "item nnz must be below 2^29 - 64 (32-bit posting byte offsets)");
   const sps::Geom g = sps::make_geom(n_items, chunk_size);
   const ItemsLayout L = items_layout(g, dim, nnz, dense_wanted(g));
   if (L.overflow) return fail(SPS_ERR_OVERFLOW, "workspace byte count overflows");
