@@ -88,7 +88,7 @@ T *at(void *base, size_t off) {
 
 struct ItemsLayout {
   size_t inv, colp, post, sbase, heavy, slab, persistent;
-  size_t flags, norm64, ticket, trow, tval, mlist, mcount, gdf, scratch;
+  size_t flags, norm64, ticket, trow, tval, mlist, mcount, gdf, hsel, scratch;
   bool overflow;
 };
 
@@ -112,6 +112,7 @@ ItemsLayout items_layout(const sps::Geom &g, int64_t dim, int64_t nnz, bool dens
   L.mlist = s.add(nnz / 2 + ns + 1, 4);
   L.mcount = s.add(ns, 4);
   L.gdf = s.add(dense ? (uint64_t)dim : 0, 4);
+  L.hsel = s.add(dense ? sps::kHeavySelInts : 0, 4);
   L.scratch = s.off;
   L.overflow = p.overflow || s.overflow;
   return L;
@@ -256,6 +257,7 @@ sps_status sps_prepare(const sps_csr *items, int32_t chunk_size, void *persisten
   d.mlist = at<int32_t>(scratch, L.mlist);
   d.mcount = at<int32_t>(scratch, L.mcount);
   d.gdf = dense ? at<int32_t>(scratch, L.gdf) : nullptr;
+  d.hsel = dense ? at<int32_t>(scratch, L.hsel) : nullptr;
 
   sps_items *h = new (std::nothrow) sps_items;
   if (!h) return fail(SPS_ERR_INVALID_ARGUMENT, "out of host memory");

@@ -138,7 +138,9 @@ struct ItemsDev {
   int32_t *mlist;       // scratch, nnz/2 + num_slices + 1
   int32_t *mcount;      // scratch, num_slices
   int32_t *gdf;         // scratch, dim (dense only)
+  int32_t *hsel;        // scratch, kHeavySelInts (dense only): heavy-dim candidates
 };
+constexpr int kHeavySelInts = 33 + 2 * 2048;
 hipError_t launch_prepare_items(const ItemsDev &d, hipStream_t s);
 
 // ---- queries ----

@@ -69,35 +69,67 @@ __device__ __forceinline__ void report(int32_t *flags, int64_t row, int bit, int
   atomicMin(reinterpret_cast<unsigned long long *>(flags + 2), key);
 }
 
+// Rows are checked as in a plain loop over each row; a workgroup whose 256
+// row pointers are all in order and in range stages the rows' indices (and
+// values, for the full check) through LDS in windows, with coalesced loads.
+constexpr int kCheckWin = 4096;
+
 __global__ __launch_bounds__(256) void csr_check_kernel(int64_t n_rows, int64_t n_cols,
                                                         int64_t nnz,
                                                         const int32_t *__restrict__ indptr,
                                                         const int32_t *__restrict__ indices,
                                                         const float *__restrict__ values,
                                                         int full, int32_t *flags) {
-  const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  __shared__ int32_t s_d[kCheckWin];
+  __shared__ float s_x[kCheckWin];
+  const int64_t r0 = (int64_t)blockIdx.x * 256;
+  const int64_t r = r0 + threadIdx.x;
   if (r == 0) {
     if (indptr[0] != 0) report(flags, 0, 1, 1);
     if ((int64_t)indptr[n_rows] != nnz) report(flags, n_rows > 0 ? n_rows - 1 : 0, 1, 1);
   }
-  if (r >= n_rows) return;
-  const int64_t b = indptr[r], e = indptr[r + 1];
-  if (b < 0 || e < b || e > nnz) {
-    report(flags, r, 1, 1);
-    return;
+  int64_t b = 0, e = 0;
+  bool ok = true;
+  if (r < n_rows) {
+    b = indptr[r];
+    e = indptr[r + 1];
+    ok = 0 <= b && b <= e && e <= nnz;
+    if (!ok) {
+      report(flags, r, 1, 1);
+      b = e = 0;
+    }
   }
   int32_t prev = -1;
-  for (int64_t k = b; k < e; ++k) {
-    const int32_t d = indices[k];
+  bool live = true;  // no index out of range found yet in this row
+  auto check = [&](int64_t r_, int32_t d, float x) {
+    if (!live) return;
     if (d < 0 || (int64_t)d >= n_cols) {
-      report(flags, r, 4, 3);
+      report(flags, r_, 4, 3);
+      live = false;
       return;
     }
     if (full) {
-      if (d <= prev) report(flags, r, 2, 2);
-      if (!isfinite(values[k])) report(flags, r, 8, 4);
+      if (d <= prev) report(flags, r_, 2, 2);
+      if (!isfinite(x)) report(flags, r_, 8, 4);
     }
     prev = d;
+  };
+  if (__syncthreads_and(ok)) {
+    const int64_t r1 = r0 + 256 < n_rows ? r0 + 256 : n_rows;
+    const int64_t vb = r0 < n_rows ? indptr[r0] : 0, ve = r0 < n_rows ? indptr[r1] : 0;
+    for (int64_t w0 = vb; w0 < ve; w0 += kCheckWin) {
+      const int64_t w1 = w0 + kCheckWin < ve ? w0 + kCheckWin : ve;
+      __syncthreads();  // the previous window has been read
+      for (int64_t k = w0 + threadIdx.x; k < w1; k += 256) {
+        s_d[k - w0] = indices[k];
+        if (full) s_x[k - w0] = values[k];
+      }
+      __syncthreads();
+      const int64_t kb = b > w0 ? b : w0, ke = e < w1 ? e : w1;
+      for (int64_t k = kb; k < ke; ++k) check(r, s_d[k - w0], full ? s_x[k - w0] : 0.0f);
+    }
+  } else {
+    for (int64_t k = b; k < e; ++k) check(r, indices[k], full ? values[k] : 0.0f);
   }
 }
 
@@ -119,25 +151,58 @@ hipError_t launch_csr_check(int64_t n_rows, int64_t n_cols, int64_t nnz, const i
 // v*v is exact in float64 for a float32 v, so the sum only rounds at the adds.
 // ---------------------------------------------------------------------------
 
+// A workgroup takes 256 consecutive rows. When their row pointers are in
+// order and in range, their values are one contiguous range of the CSR; it
+// is staged through LDS in windows of kNormWin values with coalesced loads,
+// and each thread adds its row's squares from LDS in index order, so the sum
+// is the same sequence of float64 adds as a plain loop over the row (which
+// is what a workgroup with a malformed row pointer does, over the clamped
+// row).
+constexpr int kNormWin = 4096;
+
 __global__ __launch_bounds__(256) void row_norm_kernel(int64_t n_rows, int64_t nnz,
                                                        const int32_t *__restrict__ indptr,
                                                        const float *__restrict__ values,
                                                        const int32_t *__restrict__ flags,
                                                        float *__restrict__ inv32,
                                                        double *__restrict__ norm64) {
-  const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (r >= n_rows) return;
-  const bool bad = flags != nullptr && flags[0] != 0;
-  double s = 0.0;
+  __shared__ float s_v[kNormWin];
+  const int64_t r0 = (int64_t)blockIdx.x * 256;
+  const int64_t r = r0 + threadIdx.x;
+  const int64_t r1 = r0 + 256 < n_rows ? r0 + 256 : n_rows;
+  const bool bad = flags != nullptr && flags[0] != 0;  // uniform
+  double sum = 0.0;
   if (!bad) {
-    const int64_t b = clamp64(indptr[r], 0, nnz);
-    const int64_t e = clamp64(indptr[r + 1], b, nnz);
-    for (int64_t k = b; k < e; ++k) {
-      const double v = (double)values[k];
-      s += v * v;
+    int64_t b = 0, e = 0;
+    bool ok = true;
+    if (r < n_rows) {
+      const int64_t pb = indptr[r], pe = indptr[r + 1];
+      ok = 0 <= pb && pb <= pe && pe <= nnz;
+      b = clamp64(pb, 0, nnz);
+      e = clamp64(pe, b, nnz);
+    }
+    if (__syncthreads_and(ok)) {
+      const int64_t vb = indptr[r0], ve = indptr[r1];
+      for (int64_t w0 = vb; w0 < ve; w0 += kNormWin) {
+        const int64_t w1 = w0 + kNormWin < ve ? w0 + kNormWin : ve;
+        __syncthreads();  // the previous window has been read
+        for (int64_t k = w0 + threadIdx.x; k < w1; k += 256) s_v[k - w0] = values[k];
+        __syncthreads();
+        const int64_t kb = b > w0 ? b : w0, ke = e < w1 ? e : w1;
+        for (int64_t k = kb; k < ke; ++k) {
+          const double v = (double)s_v[k - w0];
+          sum += v * v;
+        }
+      }
+    } else {
+      for (int64_t k = b; k < e; ++k) {
+        const double v = (double)values[k];
+        sum += v * v;
+      }
     }
   }
-  const double n = sqrt(s);
+  if (r >= n_rows) return;
+  const double n = sqrt(sum);
   if (norm64) norm64[r] = n;
   inv32[r] = (n > 0.0) ? (float)(1.0 / n) : 0.0f;
 }
@@ -414,56 +479,82 @@ __global__ __launch_bounds__(NT) void csc_fixup_kernel(
 // ---------------------------------------------------------------------------
 
 constexpr int kCandCap = 2048;
+static_assert(kHeavySelInts == 33 + 2 * kCandCap, "heavy-dim selection scratch layout");
 
-__global__ __launch_bounds__(1024) void heavy_select_kernel(const int32_t *__restrict__ gdf,
-                                                            int64_t dim, int32_t tglob, int32_t cap,
-                                                            const int32_t *__restrict__ flags,
-                                                            int32_t *__restrict__ heavy) {
-  constexpr int NT = 1024;
+// Heavy-dim choice in three launches over gdf (hsel: 32 level counts, the
+// candidate count, kCandCap candidate dims, kCandCap their frequencies; the
+// first 33 zeroed). Level k counts the dims with gdf in [tglob * 2^k,
+// tglob * 2^(k+1)); the candidates are the dims at or above the lowest level
+// whose tail still fits kCandCap, and the heavy dims are the `cap` most
+// frequent candidates (ties to the lower dim), stored ascending.
+__global__ __launch_bounds__(256) void heavy_level_kernel(const int32_t *__restrict__ gdf,
+                                                         int64_t dim, int32_t tglob,
+                                                         const int32_t *__restrict__ flags,
+                                                         int32_t *__restrict__ hsel) {
   __shared__ int32_t s_lvl[32];
-  __shared__ int32_t s_cd[kCandCap], s_cv[kCandCap];
-  __shared__ uint8_t s_sel[kCandCap];
-  __shared__ int32_t s_n, s_level;
   const int t = threadIdx.x;
-  if (flags[0] != 0 || tglob <= 0 || cap <= 0) {
-    if (t == 0) heavy[kHeavyMax] = 0;
-    return;
-  }
+  if (flags[0] != 0 || tglob <= 0) return;
   if (t < 32) s_lvl[t] = 0;
-  if (t == 0) s_n = 0;
   __syncthreads();
-  // level k counts dims with gdf in [tglob * 2^k, tglob * 2^(k+1))
-  for (int64_t d = t; d < dim; d += NT) {
+  for (int64_t d = (int64_t)blockIdx.x * 256 + t; d < dim; d += (int64_t)gridDim.x * 256) {
     const int32_t v = gdf[d];
-    if (v >= tglob) {
-      const int k = 31 - __clz((unsigned)(v / tglob));
-      atomicAdd(&s_lvl[k], 1);
-    }
+    if (v >= tglob) atomicAdd(&s_lvl[31 - __clz((unsigned)(v / tglob))], 1);
   }
   __syncthreads();
-  if (t == 0) {
-    int above = 0, level = 31;
-    for (int k = 31; k >= 0; --k) {  // lowest level whose tail still fits the candidate cap
-      if (above + s_lvl[k] > kCandCap) break;
-      above += s_lvl[k];
-      level = k;
-    }
-    s_level = level;
+  if (t < 32 && s_lvl[t] != 0) atomicAdd(&hsel[t], s_lvl[t]);
+}
+
+__device__ __forceinline__ int heavy_level(const int32_t *hsel) {
+  int above = 0, level = 31;
+  for (int k = 31; k >= 0; --k) {  // lowest level whose tail still fits the candidate cap
+    if (above + hsel[k] > kCandCap) break;
+    above += hsel[k];
+    level = k;
   }
+  return level;
+}
+
+__global__ __launch_bounds__(256) void heavy_collect_kernel(const int32_t *__restrict__ gdf,
+                                                           int64_t dim, int32_t tglob,
+                                                           const int32_t *__restrict__ flags,
+                                                           int32_t *__restrict__ hsel) {
+  __shared__ int32_t s_level;
+  const int t = threadIdx.x;
+  if (flags[0] != 0 || tglob <= 0) return;
+  if (t == 0) s_level = heavy_level(hsel);
   __syncthreads();
   const int64_t thr = (int64_t)tglob << s_level;
-  for (int64_t d = t; d < dim; d += NT) {
+  int32_t *cd = hsel + 33, *cv = hsel + 33 + kCandCap;
+  for (int64_t d = (int64_t)blockIdx.x * 256 + t; d < dim; d += (int64_t)gridDim.x * 256) {
     const int32_t v = gdf[d];
     if ((int64_t)v >= thr) {
-      const int i = atomicAdd(&s_n, 1);
+      const int i = atomicAdd(&hsel[32], 1);
       if (i < kCandCap) {
-        s_cd[i] = (int32_t)d;
-        s_cv[i] = v;
+        cd[i] = (int32_t)d;
+        cv[i] = v;
       }
     }
   }
+}
+
+__global__ __launch_bounds__(1024) void heavy_rank_kernel(int32_t cap,
+                                                         const int32_t *__restrict__ flags,
+                                                         const int32_t *__restrict__ hsel,
+                                                         int32_t *__restrict__ heavy) {
+  constexpr int NT = 1024;
+  __shared__ int32_t s_cd[kCandCap], s_cv[kCandCap];
+  __shared__ uint8_t s_sel[kCandCap];
+  const int t = threadIdx.x;
+  if (flags[0] != 0 || cap <= 0) {
+    if (t == 0) heavy[kHeavyMax] = 0;
+    return;
+  }
+  const int n = hsel[32] < kCandCap ? hsel[32] : kCandCap;
+  for (int i = t; i < n; i += NT) {
+    s_cd[i] = hsel[33 + i];
+    s_cv[i] = hsel[33 + kCandCap + i];
+  }
   __syncthreads();
-  const int n = s_n < kCandCap ? s_n : kCandCap;
   for (int i = t; i < n; i += NT) {
     int rank = 0;
     const int32_t vi = s_cv[i], di = s_cd[i];
@@ -554,8 +645,18 @@ hipError_t launch_prepare_items(const ItemsDev &d, hipStream_t s) {
   if (!d.dense) return hipSuccess;
   const int64_t tg64 = (g.n_items + kHeavyFracInv - 1) / kHeavyFracInv;
   const int32_t tglob = (int32_t)(tg64 > 2 ? tg64 : 2);
-  hipLaunchKernelGGL(heavy_select_kernel, dim3(1), dim3(1024), 0, s, d.gdf, d.dim, tglob, d.heavy_cap,
-                     d.flags, d.heavy);
+  e = launch_fill_i32(d.hsel, 33, 0, s);
+  if (e != hipSuccess) return e;
+  int64_t hblocks = (d.dim + 255) / 256;
+  if (hblocks > 1024) hblocks = 1024;
+  hipLaunchKernelGGL(heavy_level_kernel, dim3((unsigned)hblocks), dim3(256), 0, s, d.gdf, d.dim,
+                     tglob, d.flags, d.hsel);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(heavy_collect_kernel, dim3((unsigned)hblocks), dim3(256), 0, s, d.gdf, d.dim,
+                     tglob, d.flags, d.hsel);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(heavy_rank_kernel, dim3(1), dim3(1024), 0, s, d.heavy_cap, d.flags, d.hsel,
+                     d.heavy);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int32_t pitch = slab_pitch(g.S);
   e = launch_fill_i32(reinterpret_cast<int32_t *>(d.slab), ns * (int64_t)pitch * kHeavyRec / 2, 0, s);
