@@ -133,7 +133,7 @@ QueriesLayout queries_layout(int64_t n, int64_t nnz, int32_t n_sub, bool dense) 
   L.lptr = p.add(n + 1, 4);
   // at least one light entry each: the score kernel may read entry 0 of an
   // empty batch (and ignores it)
-  L.lrec = p.add(nnz > 0 ? nnz : 1, 16);
+  L.lrec = p.add(nnz > 0 ? nnz : 1, 12);
   L.qh = p.add(dense ? (uint64_t)ng * sps::kHeavyRec * sps::kRows : 0, 2);
   L.rspart = p.add(n_sub > 1 ? (uint64_t)n_sub * (uint64_t)n : 0, 8);
   L.total = p.off;
@@ -165,7 +165,7 @@ struct sps_queries {
   const sps_items *items;  // the corpus the queries were prepared for
   float *inv_norm;
   int32_t *lptr;
-  uint4 *lrec;
+  uint3 *lrec;
   uint16_t *qh;
   double *rs_part;
 };
@@ -388,7 +388,7 @@ sps_status sps_prepare_queries(const sps_csr *queries, const sps_items *items, v
   d.inv_norm = at<float>(workspace, L.inv);
   d.norm64 = at<double>(workspace, L.norm64);
   d.lptr = at<int32_t>(workspace, L.lptr);
-  d.lrec = at<uint4>(workspace, L.lrec);
+  d.lrec = at<uint3>(workspace, L.lrec);
   d.qh = dense ? at<uint16_t>(workspace, L.qh) : nullptr;
   sps_queries *h = new (std::nothrow) sps_queries;
   if (!h) return fail(SPS_ERR_INVALID_ARGUMENT, "out of host memory");

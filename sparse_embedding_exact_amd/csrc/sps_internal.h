@@ -155,7 +155,7 @@ struct QueriesDev {
   float *inv_norm;       // n_rows
   double *norm64;        // n_rows
   int32_t *lptr;         // n_rows + 1: light (non-heavy) entries per row, prefix
-  uint4 *lrec;           // nnz: (dim, bits of fl32(q / |q|) * 2^30, row within its group, 0)
+  uint3 *lrec;           // nnz: (dim, bits of fl32(q / |q|) * 2^30, row within its group)
   uint16_t *qh;          // [n_groups] tiles of split fp16: fl32(q / |q|) on heavy dims
 };
 hipError_t launch_prepare_queries(const QueriesDev &d, hipStream_t s);
@@ -168,7 +168,7 @@ struct ScoreArgs {
   int32_t chunk;
   bool dense;
   const int32_t *lptr;
-  const uint4 *lrec;          // light entries: (dim, value bits, row in group, 0)
+  const uint3 *lrec;          // light entries: (dim, value bits, row in group)
   const uint16_t *qh;         // [row groups] tiles of split fp16 (dense only)
   const int32_t *col_ptr;     // all slices
   const uint2 *post;          // all slices: (slice-local item id, value bits)

@@ -670,8 +670,8 @@ hipError_t launch_prepare_items(const ItemsDev &d, hipStream_t s) {
 // Queries. Each row is normalised by its float64 norm (§5.2) and rounded
 // once to fp32: qn = fl32(q_d / |q|). Heavy dims (dense path) go to the
 // row's split-fp16 record in qh (rows padded to a multiple of kRows); the
-// other entries form the "light" CSR (same row order) of 16-byte records
-// (dim, value, row's position in its group, 0), one load each in the score
+// other entries form the "light" CSR (same row order) of 12-byte records
+// (dim, value, row's position in its group), one load each in the score
 // kernel, with values qn * 2^30 (exact: a power of two), the scale of the
 // fixed-point accumulators.
 // ---------------------------------------------------------------------------
@@ -681,7 +681,7 @@ __global__ __launch_bounds__(256) void light_split_kernel(
     int64_t n_rows, const int32_t *__restrict__ indptr, const int32_t *__restrict__ indices,
     const float *__restrict__ values, const double *__restrict__ norm64,
     const int32_t *__restrict__ flags, const int32_t *__restrict__ heavy,
-    int32_t *__restrict__ lptr, uint4 *__restrict__ lrec, uint16_t *__restrict__ qh) {
+    int32_t *__restrict__ lptr, uint3 *__restrict__ lrec, uint16_t *__restrict__ qh) {
   const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (q >= n_rows) return;
   const int m = heavy != nullptr ? heavy[kHeavyMax] : 0;
@@ -706,7 +706,7 @@ __global__ __launch_bounds__(256) void light_split_kernel(
         tile[heavy_tile_index((int)(q % kRows), hs, 0)] = hi;
         tile[heavy_tile_index((int)(q % kRows), hs, 1)] = lo;
       } else {
-        lrec[out] = make_uint4((uint32_t)d, __float_as_uint(v * kFixScale), (uint32_t)rq, 0u);
+        lrec[out] = make_uint3((uint32_t)d, __float_as_uint(v * kFixScale), (uint32_t)rq);
       }
     }
     if (hs < 0) {

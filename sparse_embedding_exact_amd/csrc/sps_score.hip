@@ -137,7 +137,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void sc
   // then the range arithmetic. The first batch of each group is fetched at
   // the start, so both groups' lookups overlap the dense part.
   struct Raw {
-    uint4 rec[2];  // (dim, value bits, row in group, 0)
+    uint3 rec[2];  // (dim, value bits, row in group)
     int32_t lo[2], hi[2];
     bool ok[2];
   };
