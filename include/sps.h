@@ -213,6 +213,37 @@ sps_status sps_cosine_stream(const sps_queries *q, const sps_items *items, int32
                              void *stream);
 
 /* ------------------------------------------------------------------ */
+/* Reduced-precision variant (fp16)                                    */
+/* ------------------------------------------------------------------ */
+
+/* The page allows fp16 value data where a loss below 1e-3 is acceptable,
+ * with the norms kept in float32 (§5.3). This variant stores each item value
+ * as fp16(256 * fl32(v / ||item||)) (a 4-byte posting with the slice-local
+ * item id) and writes fp16 scores; query values and all norms stay float32
+ * and the accumulation is the same as in sps_cosine_chunk. Error: the item
+ * values contribute at most 2^-11 * sum_d |q_d i_d| <= 2^-11 (Cauchy-Schwarz
+ * on unit rows) and the fp16 output rounding at most 2^-11 for |S| <= 1 +
+ * 2^-11, so |S_half - S| < 1e-3 for every score. */
+
+/* Bytes of the workspace for sps_items_enable_half: (nnz + 4) * 4. Pure host. */
+sps_status sps_items_half_workspace_size(const sps_items *h, size_t *bytes);
+
+/* Build the 4-byte postings of a prepared corpus (asynchronous, after the
+ * sps_prepare work on the same stream). workspace: DEVICE, 16-byte aligned,
+ * caller-owned, kept alive while the handle is used for sps_cosine_chunk_half;
+ * errors: SPS_ERR_WORKSPACE_TOO_SMALL, SPS_ERR_INVALID_ARGUMENT. */
+sps_status sps_items_enable_half(sps_items *h, void *workspace, size_t workspace_bytes,
+                                 void *stream);
+
+/* sps_cosine_chunk with fp16 scores (IEEE binary16 bit patterns in `out`,
+ * DEVICE uint16[n_rows * ld_out]) computed from the fp16 item values above;
+ * row_sums (nullable) = the float64 sum of the fp16 scores written. Requires
+ * sps_items_enable_half (SPS_ERR_INVALID_ARGUMENT otherwise). Bitwise
+ * reproducible. */
+sps_status sps_cosine_chunk_half(const sps_queries *q, const sps_items *items, int32_t chunk,
+                                 uint16_t *out, int64_t ld_out, double *row_sums, void *stream);
+
+/* ------------------------------------------------------------------ */
 /* Stand-alone pieces                                                  */
 /* ------------------------------------------------------------------ */
 

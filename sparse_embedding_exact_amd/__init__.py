@@ -79,6 +79,9 @@ SIGNATURES = {
     "sps_queries_destroy": (None, [_P]),
     "sps_cosine_chunk": (_I32, [_P, _P, _I32, _P, _I64, _P, _P]),
     "sps_cosine_stream": (_I32, [_P, _P, _I32, _I32, _P, _I64, _P, _P]),
+    "sps_items_half_workspace_size": (_I32, [_P, ctypes.POINTER(_SZ)]),
+    "sps_items_enable_half": (_I32, [_P, _P, _SZ, _P]),
+    "sps_cosine_chunk_half": (_I32, [_P, _P, _I32, _P, _I64, _P, _P]),
     "sps_row_inv_norms": (_I32, [ctypes.POINTER(_Csr), _P, _P]),
     "sps_validate_csr": (_I32, [ctypes.POINTER(_Csr), _P, _P, ctypes.POINTER(_I64),
                                 ctypes.POINTER(_I32)]),
@@ -187,6 +190,17 @@ class Items:
         b = c * self.chunk_size
         return min(b + self.chunk_size, self.n_items) - b
 
+    def enable_half(self, stream=None) -> None:
+        """Build the fp16 postings used by cosine_chunk_half (once; needs the prepare work
+        to have been enqueued on the same stream)."""
+        if getattr(self, "_half", None) is not None:
+            return
+        n = _SZ()
+        _check(_lib.sps_items_half_workspace_size(self._h, ctypes.byref(n)))
+        buf, ptr = _workspace(n.value, self._persistent.device)
+        _check(_lib.sps_items_enable_half(self._h, ptr, n.value, _stream_ptr(stream)))
+        self._half = buf
+
     def release_inputs(self):
         """Drop the item CSR and prepare scratch (after the prepare work completed)."""
         torch.cuda.current_stream().synchronize()
@@ -288,8 +302,8 @@ def prepare_queries(queries: CSR, items: Items, stream=None) -> Queries:
     return q
 
 
-def _out_args(q: Queries, out: torch.Tensor, row_sums):
-    assert out.is_cuda and out.dtype == torch.float32 and out.dim() == 2
+def _out_args(q: Queries, out: torch.Tensor, row_sums, dtype=torch.float32):
+    assert out.is_cuda and out.dtype == dtype and out.dim() == 2
     assert out.stride(1) == 1 and out.shape[0] == q.n_rows
     ld = out.stride(0) if q.n_rows > 1 else out.shape[1]
     rs = None
@@ -308,6 +322,19 @@ def cosine_chunk(q: Queries, items: Items, chunk: int, out: torch.Tensor,
         assert row_sums.numel() >= q.n_rows
     _check(_lib.sps_cosine_chunk(q._h, items._h, chunk, out.data_ptr(), ld, rs,
                                  _stream_ptr(stream)))
+
+
+def cosine_chunk_half(q: Queries, items: Items, chunk: int, out: torch.Tensor,
+                      row_sums: torch.Tensor | None = None, stream=None) -> None:
+    """The reduced-precision variant: out[:, :chunk_len] = fp16 scores from fp16 item
+    values (|error| < 1e-3); out is (n_query, >= chunk_len) float16, row-major. Needs
+    items.enable_half()."""
+    ld, rs = _out_args(q, out, row_sums, torch.float16)
+    assert out.shape[1] >= items.chunk_len(chunk)
+    if row_sums is not None:
+        assert row_sums.numel() >= q.n_rows
+    _check(_lib.sps_cosine_chunk_half(q._h, items._h, chunk, out.data_ptr(), ld, rs,
+                                      _stream_ptr(stream)))
 
 
 def cosine_stream(q: Queries, items: Items, chunk_begin: int, chunk_end: int,

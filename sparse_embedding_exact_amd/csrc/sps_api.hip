@@ -155,6 +155,7 @@ struct sps_items {
   int32_t *slice_base;
   int32_t *heavy;
   uint16_t *slab;
+  uint32_t *post4;  // reduced-precision postings (null until sps_items_enable_half)
 };
 
 struct sps_queries {
@@ -278,6 +279,7 @@ sps_status sps_prepare(const sps_csr *items, int32_t chunk_size, void *persisten
   h->slice_base = d.slice_base;
   h->heavy = d.heavy;
   h->slab = d.slab;
+  h->post4 = nullptr;
   *out = h;
   return SPS_OK;
 }
@@ -421,7 +423,7 @@ sps_status sps_queries_inv_norms(const sps_queries *q, const float **inv_norm) {
 
 void sps_queries_destroy(sps_queries *q) { delete q; }
 
-static sps_status check_score_args(const sps_queries *q, const sps_items *items, float *out,
+static sps_status check_score_args(const sps_queries *q, const sps_items *items, const void *out,
                                    int64_t ld_out) {
   if (!q || !items) return fail(SPS_ERR_INVALID_ARGUMENT, "NULL handle");
   if (q->items != items)
@@ -441,7 +443,8 @@ static sps_status check_score_args(const sps_queries *q, const sps_items *items,
 }
 
 static sps_status score_one(const sps_queries *q, const sps_items *items, int32_t chunk,
-                            float *out, int64_t ld_out, double *row_sums, hipStream_t s) {
+                            float *out, uint16_t *out16, int64_t ld_out, double *row_sums,
+                            hipStream_t s) {
   sps::ScoreArgs a{};
   a.g = items->g;
   a.dim = items->dim;
@@ -454,11 +457,13 @@ static sps_status score_one(const sps_queries *q, const sps_items *items, int32_
   a.qh = q->qh;
   a.col_ptr = items->col_ptr;
   a.post = items->post;
+  a.post4 = items->post4;
   a.slice_base = items->slice_base;
   a.heavy = items->heavy;
   a.slab = items->slab;
   a.pitch = items->pitch;
   a.out = out;
+  a.out16 = out16;
   a.ld = ld_out;
   a.rs_part = q->rs_part;
   a.row_sums = row_sums;
@@ -473,7 +478,42 @@ sps_status sps_cosine_chunk(const sps_queries *q, const sps_items *items, int32_
   if (st != SPS_OK) return st;
   if (chunk < 0 || chunk >= items->g.num_chunks)
     return fail(SPS_ERR_CHUNK_RANGE, "chunk %d outside [0, %d)", chunk, items->g.num_chunks);
-  return score_one(q, items, chunk, out, ld_out, row_sums, reinterpret_cast<hipStream_t>(stream));
+  return score_one(q, items, chunk, out, nullptr, ld_out, row_sums,
+                   reinterpret_cast<hipStream_t>(stream));
+}
+
+sps_status sps_items_half_workspace_size(const sps_items *h, size_t *bytes) {
+  if (!h || !bytes) return fail(SPS_ERR_INVALID_ARGUMENT, "NULL argument");
+  *bytes = (size_t)(h->nnz + sps::kPostPad4) * sizeof(uint32_t);
+  return SPS_OK;
+}
+
+sps_status sps_items_enable_half(sps_items *h, void *workspace, size_t workspace_bytes,
+                                 void *stream) {
+  if (!h) return fail(SPS_ERR_INVALID_ARGUMENT, "NULL handle");
+  size_t need = 0;
+  sps_items_half_workspace_size(h, &need);
+  if (!workspace || workspace_bytes < need)
+    return fail(SPS_ERR_WORKSPACE_TOO_SMALL, "half workspace: %zu bytes needed", need);
+  if (reinterpret_cast<uintptr_t>(workspace) & 15)
+    return fail(SPS_ERR_INVALID_ARGUMENT, "half workspace must be 16-byte aligned");
+  const hipError_t e = sps::launch_pack_half(h->post, h->nnz, static_cast<uint32_t *>(workspace),
+                                             reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "sps_items_enable_half");
+  h->post4 = static_cast<uint32_t *>(workspace);
+  return SPS_OK;
+}
+
+sps_status sps_cosine_chunk_half(const sps_queries *q, const sps_items *items, int32_t chunk,
+                                 uint16_t *out, int64_t ld_out, double *row_sums, void *stream) {
+  sps_status st = check_score_args(q, items, out, ld_out);
+  if (st != SPS_OK) return st;
+  if (!items->post4)
+    return fail(SPS_ERR_INVALID_ARGUMENT, "sps_items_enable_half has not been called");
+  if (chunk < 0 || chunk >= items->g.num_chunks)
+    return fail(SPS_ERR_CHUNK_RANGE, "chunk %d outside [0, %d)", chunk, items->g.num_chunks);
+  return score_one(q, items, chunk, nullptr, out, ld_out, row_sums,
+                   reinterpret_cast<hipStream_t>(stream));
 }
 
 sps_status sps_cosine_stream(const sps_queries *q, const sps_items *items, int32_t chunk_begin,
@@ -486,7 +526,7 @@ sps_status sps_cosine_stream(const sps_queries *q, const sps_items *items, int32
                 chunk_end, items->g.num_chunks);
   for (int32_t c = chunk_begin; c < chunk_end; ++c) {
     double *rs = row_sums ? row_sums + (int64_t)(c - chunk_begin) * q->n_rows : nullptr;
-    st = score_one(q, items, c, out, ld_out, rs, reinterpret_cast<hipStream_t>(stream));
+    st = score_one(q, items, c, out, nullptr, ld_out, rs, reinterpret_cast<hipStream_t>(stream));
     if (st != SPS_OK) return st;
   }
   return SPS_OK;

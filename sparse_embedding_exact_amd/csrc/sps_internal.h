@@ -22,6 +22,9 @@ constexpr int kScoreThreads = 512;
 // zeroed postings past the end of the posting array: the score kernel reads
 // postings in pairs, so the pair of a list's last posting stays readable
 constexpr int kPostPad = 2;
+// the same for the 4-byte postings of the reduced-precision variant, read
+// four at a time
+constexpr int kPostPad4 = 4;
 
 // Dense path for heavy dims: at most kHeavyMax dims (a multiple of 4, the
 // MFMA depth) whose item document frequency is at least n_items /
@@ -142,6 +145,9 @@ struct ItemsDev {
 };
 constexpr int kHeavySelInts = 33 + 2 * 2048;
 hipError_t launch_prepare_items(const ItemsDev &d, hipStream_t s);
+// 4-byte postings (item | fp16(256 value) << 16) from the prepared 8-byte
+// ones, plus kPostPad4 zero entries
+hipError_t launch_pack_half(const uint2 *post, int64_t nnz, uint32_t *post4, hipStream_t s);
 
 // ---- queries ----
 struct QueriesDev {
@@ -172,11 +178,13 @@ struct ScoreArgs {
   const uint16_t *qh;         // [row groups] tiles of split fp16 (dense only)
   const int32_t *col_ptr;     // all slices
   const uint2 *post;          // all slices: (slice-local item id, value bits)
+  const uint32_t *post4;      // reduced-precision variant: item | fp16(256 value) << 16
   const int32_t *slice_base;
   const int32_t *heavy;
   const uint16_t *slab;       // [slices][pitch / 16] tiles of split fp16 (dense only)
   int32_t pitch;
   float *out;
+  uint16_t *out16;            // fp16 output of the reduced-precision variant (else null)
   int64_t ld;
   double *rs_part;            // n_sub * n_q partial row sums (nullable)
   double *row_sums;           // n_q (nullable)

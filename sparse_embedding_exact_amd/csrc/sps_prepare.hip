@@ -667,6 +667,31 @@ hipError_t launch_prepare_items(const ItemsDev &d, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------
+// Reduced-precision variant: 4-byte postings, the slice-local item id (< 2^16)
+// in the low half and fp16(256 w) in the high half (256 w is exact in fp32;
+// the scale keeps normalised values down to 2^-22 in fp16's normal range).
+// ---------------------------------------------------------------------------
+
+__global__ void pack_half_kernel(const uint2 *__restrict__ post, int64_t nnz,
+                                 uint32_t *__restrict__ post4) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < nnz) {
+    const uint2 p = post[i];
+    const _Float16 h = (_Float16)(__uint_as_float(p.y) * kHeavyScale);
+    post4[i] = (p.x & 0xFFFFu) | ((uint32_t)__builtin_bit_cast(uint16_t, h) << 16);
+  } else if (i < nnz + kPostPad4) {
+    post4[i] = 0u;
+  }
+}
+
+hipError_t launch_pack_half(const uint2 *post, int64_t nnz, uint32_t *post4, hipStream_t s) {
+  const int64_t n = nnz + kPostPad4;
+  hipLaunchKernelGGL(pack_half_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, post,
+                     nnz, post4);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Queries. Each row is normalised by its float64 norm (§5.2) and rounded
 // once to fp32: qn = fl32(q_d / |q|). Heavy dims (dense path) go to the
 // row's split-fp16 record in qh (rows padded to a multiple of kRows); the

@@ -47,7 +47,6 @@
 // what it wrote (a per-chunk checksum; slices are folded in a fixed order).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
-#include <stdlib.h>
 
 #include "sps_device.h"
 #include "sps_internal.h"
@@ -72,9 +71,16 @@ __device__ __forceinline__ int round_fix(float x) {
 // 16-byte load from an 8-byte aligned address (global memory accesses need
 // only 4-byte alignment on this target)
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_a8 __attribute__((ext_vector_type(4), aligned(8)));
 __device__ __forceinline__ u32x4 ld_pair(const uint2 *base, uint32_t byte_off) {
   return *reinterpret_cast<const u32x4_a8 *>(reinterpret_cast<const char *>(base) + byte_off);
+}
+
+// four consecutive 4-byte postings with one 16-byte load (4-byte aligned)
+typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+__device__ __forceinline__ u32x4 ld_quad4(const uint32_t *base, uint32_t byte_off) {
+  return *reinterpret_cast<const u32x4_a4 *>(reinterpret_cast<const char *>(base) + byte_off);
 }
 
 constexpr int NT = kScoreThreads;
@@ -88,13 +94,20 @@ static_assert(kRows == 16 && kHeavyMax == 32, "one 16x16x32 MFMA tile covers the
 // 16 lanes, described in an LDS table.
 constexpr int kSeg = 16;
 constexpr int kSegMax = 896;         // segments per round
-constexpr int kSegPad = 8 * NW * 4;  // one step of octets past the end (U <= 4)
+constexpr int kSegPad = 16 * NW * 2;  // one walk step past the end (16 segments, 2 per wave)
 static_assert(kRows * kSliceMax * 4 < (1 << 27), "row byte offset fits the segment record");
 
-template <bool DENSE, int U>
+// HALF: the reduced-precision variant (item values as fp16, scores written
+// as fp16; see sps_cosine_chunk_half): 4-byte postings, four per lane and
+// load, the slab's hi halves only, fp16 output.
+template <bool DENSE, bool HALF>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void score_kernel(
     const ScoreArgs a, int vec4) {
-  static_assert(8 * NW * U <= kSegPad, "the segment table pads one step of octets per wave");
+  constexpr int U = 2;                      // segment groups per wave per walk step
+  constexpr int PPL = HALF ? 4 : 2;         // postings per lane (one 16-byte load)
+  constexpr int LPS = kSeg / PPL;           // lanes per segment
+  constexpr int SPI = 64 / LPS;             // segments per wave per load
+  static_assert(SPI * NW * U <= kSegPad, "the segment table pads one walk step per wave");
   extern __shared__ int acc[];
   // segment table of a round: first posting, query value, and the LDS byte
   // offset of the row << 5 | postings in the segment (1..16; 0 pads the
@@ -206,7 +219,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void sc
 #pragma unroll
     for (int tt = 0; tt < kHalf; ++tt) {
       b_hi[tt] = st[(h * kHalf + tt) * 128 + lane];
-      b_lo[tt] = st[(h * kHalf + tt) * 128 + 64 + lane];
+      if (!HALF) b_lo[tt] = st[(h * kHalf + tt) * 128 + 64 + lane];
     }
   };
   // lane l holds rows 4(l/16) + i of item 16 tt + l%16
@@ -220,8 +233,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void sc
       for (int gi = 0; gi < kGroups; ++gi) {
         const f32x4 z = {0.f, 0.f, 0.f, 0.f};
         const f32x4 mn = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_hi[gi], b_hi[tt], z, 0, 0, 0);
-        f32x4 cr = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_hi[gi], b_lo[tt], z, 0, 0, 0);
-        cr = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_lo[gi], b_hi[tt], cr, 0, 0, 0);
+        f32x4 cr;
+        if (HALF) {  // item values in one fp16 (hi) each: query hi and lo times it
+          cr = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_lo[gi], b_hi[tt], z, 0, 0, 0);
+        } else {
+          cr = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_hi[gi], b_lo[tt], z, 0, 0, 0);
+          cr = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_lo[gi], b_hi[tt], cr, 0, 0, 0);
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int v = round_fix((mn[i] + cr[i] * (1.0f / kLoScale)) * kDenseToFix);
@@ -277,6 +295,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void sc
   __syncthreads();  // accumulators initialised before any sparse update
 
   const uint2 *__restrict__ ppost = a.post + cb0;
+  const uint32_t *__restrict__ ppost4 = HALF ? a.post4 + cb0 : nullptr;
   const int64_t col0 = ib - g.chunk_begin(a.chunk);
   const bool v4 = vec4 && (col0 % 4 == 0);
   double *rsum = g.n_sub == 1 ? a.row_sums : a.rs_part;
@@ -337,11 +356,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void sc
         const int32_t nr = total - r0 < kSegMax ? total - r0 : kSegMax;
         for (int k = t; k < kSegPad; k += NT) s_smeta[nr + k] = 0u;
         __syncthreads();
-        // Wave w takes segment octets w, w + NW, ...; lanes 8i..8i+7 take
-        // segment i of an octet, two postings per lane (one 16-byte load),
-        // U octets per step.
-        const int32_t jl = 2 * (lane & 7);
-        for (int32_t k0 = wv; 8 * k0 < nr; k0 += NW * U) {
+        // Wave w takes segment groups w, w + NW, ...; lanes LPS i .. LPS i + LPS - 1
+        // take segment i of a group (SPI segments), PPL postings per lane with
+        // one 16-byte load, U groups per step.
+        const int32_t jl = PPL * (lane % LPS);
+        for (int32_t k0 = wv; SPI * k0 < nr; k0 += NW * U) {
           uint32_t pos[U];
           uint32_t aoff[U];
           float qv[U];
@@ -349,7 +368,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void sc
 #pragma unroll
           for (int u = 0; u < U; ++u) {
             // entries past nr are padding (no postings)
-            const int32_t sg = 8 * (k0 + NW * u) + (lane >> 3);
+            const int32_t sg = SPI * (k0 + NW * u) + lane / LPS;
             const uint32_t meta = s_smeta[sg];
             const uint32_t sp0 = s_spos[sg];
             nn[u] = (int32_t)(meta & 31u) - jl;
@@ -357,11 +376,12 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void sc
             aoff[u] = meta >> 5;
             qv[u] = __uint_as_float(s_sqv[sg]);
           }
-          // (the posting array holds kPostPad extra entries, so the second
-          // posting of a lane's pair is readable at the end of the array)
+          // (the posting arrays hold padding entries past their ends, so a
+          // lane's last postings stay readable at the end of an array)
           u32x4 pe[U];
 #pragma unroll
-          for (int u = 0; u < U; ++u) pe[u] = ld_pair(ppost, pos[u] * 8u);
+          for (int u = 0; u < U; ++u)
+            pe[u] = HALF ? ld_quad4(ppost4, pos[u] * 4u) : ld_pair(ppost, pos[u] * 8u);
           // all U loads are in flight before the first is waited on (keeps the
           // compiler from sinking a load into the masked update below it)
           __builtin_amdgcn_sched_barrier(0);
@@ -371,12 +391,25 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void sc
 #pragma unroll
           for (int u = 0; u < U; ++u) {
             char *const rbase = reinterpret_cast<char *>(acc) + aoff[u];
-            if (nn[u] > 0 && pe[u].x < (uint32_t)slen)
-              atomicAdd(reinterpret_cast<int *>(rbase + 4 * pe[u].x),
-                        round_fix(qv[u] * __uint_as_float(pe[u].y)));
-            if (nn[u] > 1 && pe[u].z < (uint32_t)slen)
-              atomicAdd(reinterpret_cast<int *>(rbase + 4 * pe[u].z),
-                        round_fix(qv[u] * __uint_as_float(pe[u].w)));
+            if (HALF) {
+              // (item | fp16(256 w) << 16) per posting
+#pragma unroll
+              for (int k = 0; k < 4; ++k) {
+                const uint32_t x = pe[u][k];
+                const uint32_t it = x & 0xFFFFu;
+                const float w = (float)__builtin_bit_cast(_Float16, (uint16_t)(x >> 16)) *
+                                (1.0f / kHeavyScale);
+                if (nn[u] > k && it < (uint32_t)slen)
+                  atomicAdd(reinterpret_cast<int *>(rbase + 4 * it), round_fix(qv[u] * w));
+              }
+            } else {
+              if (nn[u] > 0 && pe[u].x < (uint32_t)slen)
+                atomicAdd(reinterpret_cast<int *>(rbase + 4 * pe[u].x),
+                          round_fix(qv[u] * __uint_as_float(pe[u].y)));
+              if (nn[u] > 1 && pe[u].z < (uint32_t)slen)
+                atomicAdd(reinterpret_cast<int *>(rbase + 4 * pe[u].z),
+                          round_fix(qv[u] * __uint_as_float(pe[u].w)));
+            }
           }
         }
         __syncthreads();
@@ -390,9 +423,40 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void sc
       const int r = wv + NW * rr;
       const int64_t q = q0 + r;
       if (q >= a.n_q) break;
-      float *orow = a.out + q * a.ld + col0;
       const int4 *arow = reinterpret_cast<const int4 *>(acc + r * Lp);
       double rs = 0.0;
+      if (HALF) {
+        // fp16(fl32(acc) * 2^-30), 8-byte stores when aligned; the row sum is
+        // of the fp16 values written
+        uint16_t *hrow = a.out16 + q * a.ld + col0;
+        for (int j0 = 4 * lane; j0 < slen; j0 += 256) {
+          const int4 x = arow[j0 >> 2];
+          const _Float16 h[4] = {(_Float16)((float)x.x * kFixInv), (_Float16)((float)x.y * kFixInv),
+                                 (_Float16)((float)x.z * kFixInv), (_Float16)((float)x.w * kFixInv)};
+          if (v4 && j0 + 3 < slen) {
+            const u32x2 pk = {(uint32_t)__builtin_bit_cast(uint16_t, h[0]) |
+                                  ((uint32_t)__builtin_bit_cast(uint16_t, h[1]) << 16),
+                              (uint32_t)__builtin_bit_cast(uint16_t, h[2]) |
+                                  ((uint32_t)__builtin_bit_cast(uint16_t, h[3]) << 16)};
+            __builtin_nontemporal_store(pk, reinterpret_cast<u32x2 *>(hrow + j0));
+            rs += ((double)(float)h[0] + (double)(float)h[1]) +
+                  ((double)(float)h[2] + (double)(float)h[3]);
+          } else {
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+              if (j0 + u < slen) {
+                hrow[j0 + u] = __builtin_bit_cast(uint16_t, h[u]);
+                rs += (double)(float)h[u];
+              }
+          }
+        }
+        if (rsum != nullptr) {
+          rs = wave_sum(rs);
+          if (lane == 0) rsum[(g.n_sub == 1 ? 0 : (int64_t)ks * a.n_q) + q] = rs;
+        }
+        continue;
+      }
+      float *orow = a.out + q * a.ld + col0;
       for (int j0 = 4 * lane; j0 < slen; j0 += 256) {
         const int4 x = arow[j0 >> 2];
         const f32x4 v = {(float)x.x * kFixInv, (float)x.y * kFixInv, (float)x.z * kFixInv,
@@ -431,22 +495,10 @@ size_t score_lds_bytes(int32_t S) {
   return (size_t)kRows * acc_pitch(S) * sizeof(int) + (kSegMax + kSegPad) * 12 + NW * 4;
 }
 
-static int env_unroll() {
-  static int v = -1;
-  if (v < 0) {
-    v = 2;
-    if (const char *e = getenv("SPS_SCORE_UNROLL")) {
-      const int x = atoi(e);
-      if (x == 2 || x == 4) v = x;
-    }
-  }
-  return v;
-}
-
-template <bool DENSE, int U>
+template <bool DENSE, bool HALF>
 static hipError_t launch_t(const ScoreArgs &a, hipStream_t s) {
   const size_t dyn = (size_t)kRows * acc_pitch(a.g.S) * sizeof(int);
-  auto kern = score_kernel<DENSE, U>;
+  auto kern = score_kernel<DENSE, HALF>;
   // dynamic LDS above 64 KiB needs an explicit opt-in per kernel
   static size_t opted = 65536;
   if (dyn > opted) {
@@ -455,7 +507,10 @@ static hipError_t launch_t(const ScoreArgs &a, hipStream_t s) {
     if (e != hipSuccess) return e;
     opted = dyn;
   }
-  const int vec4 = (a.ld % 4 == 0) && ((reinterpret_cast<uintptr_t>(a.out) & 15) == 0);
+  // wide stores need the row pitch and base aligned: 16 bytes (fp32), 8 (fp16)
+  const uintptr_t base = HALF ? reinterpret_cast<uintptr_t>(a.out16)
+                              : reinterpret_cast<uintptr_t>(a.out);
+  const int vec4 = (a.ld % 4 == 0) && ((base & (HALF ? 7 : 15)) == 0);
   const int64_t pairs = (a.n_groups + kGroups - 1) / kGroups;
   hipLaunchKernelGGL(kern, dim3((unsigned)(pairs * a.g.n_sub)), dim3(NT), dyn, s, a, vec4);
   return hipGetLastError();
@@ -463,12 +518,12 @@ static hipError_t launch_t(const ScoreArgs &a, hipStream_t s) {
 
 hipError_t launch_score(const ScoreArgs &a, hipStream_t s) {
   if (a.n_groups == 0) return hipSuccess;
-  const int u = env_unroll();
+  const bool half = a.out16 != nullptr;
   hipError_t e;
   if (a.dense) {
-    e = u == 4 ? launch_t<true, 4>(a, s) : launch_t<true, 2>(a, s);
+    e = half ? launch_t<true, true>(a, s) : launch_t<true, false>(a, s);
   } else {
-    e = u == 4 ? launch_t<false, 4>(a, s) : launch_t<false, 2>(a, s);
+    e = half ? launch_t<false, true>(a, s) : launch_t<false, false>(a, s);
   }
   if (e != hipSuccess) return e;
   if (a.row_sums != nullptr && a.g.n_sub > 1) {
