@@ -212,6 +212,31 @@ sps_status sps_cosine_stream(const sps_queries *q, const sps_items *items, int32
                              int32_t chunk_end, float *out, int64_t ld_out, double *row_sums,
                              void *stream);
 
+/* One score kept by sps_cosine_chunk_threshold: query row, global item
+ * index, and the float32 score. */
+typedef struct {
+  int32_t row;
+  int32_t item;
+  float score;
+} sps_hit;
+
+/* Threshold-filtered output (asynchronous), for the threshold filtering the
+ * page's downstream logic applies to the full matrix (§2.3): the scores of
+ * chunk `chunk` are computed as in sps_cosine_chunk and every one with
+ * S[q, j] >= threshold (compared in float32) is appended as a hit (q,
+ * item_begin + j, S) to hits[*count ...]: *count (DEVICE uint64, zeroed by the
+ * caller once) is advanced atomically by the number of hits, so successive
+ * calls append; hits past `capacity` are counted but not written (the caller
+ * compares *count with capacity). The order of hits is unspecified; the set
+ * and each score are bitwise reproducible and equal to sps_cosine_chunk's.
+ * hits: DEVICE sps_hit[capacity]; row_sums (nullable): DEVICE double[n_rows],
+ * the float64 sum of all the chunk's scores of the row, kept or not.
+ * Errors: SPS_ERR_INVALID_ARGUMENT (NULL count, negative capacity, NaN
+ * threshold), SPS_ERR_CHUNK_RANGE. */
+sps_status sps_cosine_chunk_threshold(const sps_queries *q, const sps_items *items, int32_t chunk,
+                                      float threshold, sps_hit *hits, int64_t capacity,
+                                      uint64_t *count, double *row_sums, void *stream);
+
 /* ------------------------------------------------------------------ */
 /* Reduced-precision variant (fp16)                                    */
 /* ------------------------------------------------------------------ */

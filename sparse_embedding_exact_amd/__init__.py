@@ -23,6 +23,7 @@ import ctypes
 import os
 from dataclasses import dataclass
 
+import numpy as np
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -79,6 +80,7 @@ SIGNATURES = {
     "sps_queries_destroy": (None, [_P]),
     "sps_cosine_chunk": (_I32, [_P, _P, _I32, _P, _I64, _P, _P]),
     "sps_cosine_stream": (_I32, [_P, _P, _I32, _I32, _P, _I64, _P, _P]),
+    "sps_cosine_chunk_threshold": (_I32, [_P, _P, _I32, ctypes.c_float, _P, _I64, _P, _P, _P]),
     "sps_items_half_workspace_size": (_I32, [_P, ctypes.POINTER(_SZ)]),
     "sps_items_enable_half": (_I32, [_P, _P, _SZ, _P]),
     "sps_cosine_chunk_half": (_I32, [_P, _P, _I32, _P, _I64, _P, _P]),
@@ -335,6 +337,32 @@ def cosine_chunk_half(q: Queries, items: Items, chunk: int, out: torch.Tensor,
         assert row_sums.numel() >= q.n_rows
     _check(_lib.sps_cosine_chunk_half(q._h, items._h, chunk, out.data_ptr(), ld, rs,
                                       _stream_ptr(stream)))
+
+
+def cosine_chunk_threshold(q: Queries, items: Items, chunk: int, threshold: float,
+                           hits: torch.Tensor, count: torch.Tensor,
+                           row_sums: torch.Tensor | None = None, stream=None) -> None:
+    """Append every score >= threshold of the chunk to hits as (row, item, score bits) int32
+    triples; count (one int64/uint64 device value, zeroed once by the caller) advances by the
+    number of hits, including those past hits' capacity, which are dropped."""
+    assert hits.is_cuda and hits.dtype == torch.int32 and hits.dim() == 2
+    assert hits.shape[1] == 3 and hits.is_contiguous()
+    assert count.is_cuda and count.dtype == torch.int64 and count.numel() >= 1
+    rs = None
+    if row_sums is not None:
+        assert row_sums.is_cuda and row_sums.dtype == torch.float64 and row_sums.is_contiguous()
+        assert row_sums.numel() >= q.n_rows
+        rs = row_sums.data_ptr()
+    _check(_lib.sps_cosine_chunk_threshold(q._h, items._h, chunk, float(threshold),
+                                           hits.data_ptr() if hits.numel() else None,
+                                           hits.shape[0], count.data_ptr(), rs,
+                                           _stream_ptr(stream)))
+
+
+def hits_to_numpy(hits: torch.Tensor, count: int):
+    """(rows, items, scores) numpy arrays of the first min(count, capacity) hits."""
+    h = hits[:min(int(count), hits.shape[0])].cpu().numpy()
+    return h[:, 0].copy(), h[:, 1].copy(), h[:, 2].copy().view(np.float32)
 
 
 def cosine_stream(q: Queries, items: Items, chunk_begin: int, chunk_end: int,

@@ -443,9 +443,11 @@ static sps_status check_score_args(const sps_queries *q, const sps_items *items,
 }
 
 static sps_status score_one(const sps_queries *q, const sps_items *items, int32_t chunk,
-                            float *out, uint16_t *out16, int64_t ld_out, double *row_sums,
-                            hipStream_t s) {
+                            sps::ScoreMode mode, float *out, uint16_t *out16, int64_t ld_out,
+                            double *row_sums, hipStream_t s, const sps::ScoreArgs *extra = nullptr) {
   sps::ScoreArgs a{};
+  if (extra) a = *extra;
+  a.mode = mode;
   a.g = items->g;
   a.dim = items->dim;
   a.n_q = q->n_rows;
@@ -478,8 +480,30 @@ sps_status sps_cosine_chunk(const sps_queries *q, const sps_items *items, int32_
   if (st != SPS_OK) return st;
   if (chunk < 0 || chunk >= items->g.num_chunks)
     return fail(SPS_ERR_CHUNK_RANGE, "chunk %d outside [0, %d)", chunk, items->g.num_chunks);
-  return score_one(q, items, chunk, out, nullptr, ld_out, row_sums,
+  return score_one(q, items, chunk, sps::kModeExact, out, nullptr, ld_out, row_sums,
                    reinterpret_cast<hipStream_t>(stream));
+}
+
+sps_status sps_cosine_chunk_threshold(const sps_queries *q, const sps_items *items, int32_t chunk,
+                                      float threshold, sps_hit *hits, int64_t capacity,
+                                      uint64_t *count, double *row_sums, void *stream) {
+  if (!q || !items || !count) return fail(SPS_ERR_INVALID_ARGUMENT, "NULL argument");
+  if (capacity < 0 || (capacity > 0 && !hits))
+    return fail(SPS_ERR_INVALID_ARGUMENT, "negative capacity or NULL hits");
+  if (threshold != threshold) return fail(SPS_ERR_INVALID_ARGUMENT, "threshold is NaN");
+  const int64_t width = items->g.C < items->g.n_items ? items->g.C : items->g.n_items;
+  sps_status st = check_score_args(q, items, count, width);
+  if (st != SPS_OK) return st;
+  if (chunk < 0 || chunk >= items->g.num_chunks)
+    return fail(SPS_ERR_CHUNK_RANGE, "chunk %d outside [0, %d)", chunk, items->g.num_chunks);
+  static_assert(sizeof(sps_hit) == 12, "sps_hit is (int32, int32, float)");
+  sps::ScoreArgs x{};
+  x.hits = reinterpret_cast<int3 *>(hits);
+  x.hit_cap = capacity;
+  x.hit_count = reinterpret_cast<unsigned long long *>(count);
+  x.threshold = threshold;
+  return score_one(q, items, chunk, sps::kModeThreshold, nullptr, nullptr, width, row_sums,
+                   reinterpret_cast<hipStream_t>(stream), &x);
 }
 
 sps_status sps_items_half_workspace_size(const sps_items *h, size_t *bytes) {
@@ -512,7 +536,7 @@ sps_status sps_cosine_chunk_half(const sps_queries *q, const sps_items *items, i
     return fail(SPS_ERR_INVALID_ARGUMENT, "sps_items_enable_half has not been called");
   if (chunk < 0 || chunk >= items->g.num_chunks)
     return fail(SPS_ERR_CHUNK_RANGE, "chunk %d outside [0, %d)", chunk, items->g.num_chunks);
-  return score_one(q, items, chunk, nullptr, out, ld_out, row_sums,
+  return score_one(q, items, chunk, sps::kModeHalf, nullptr, out, ld_out, row_sums,
                    reinterpret_cast<hipStream_t>(stream));
 }
 
@@ -526,7 +550,8 @@ sps_status sps_cosine_stream(const sps_queries *q, const sps_items *items, int32
                 chunk_end, items->g.num_chunks);
   for (int32_t c = chunk_begin; c < chunk_end; ++c) {
     double *rs = row_sums ? row_sums + (int64_t)(c - chunk_begin) * q->n_rows : nullptr;
-    st = score_one(q, items, c, out, nullptr, ld_out, rs, reinterpret_cast<hipStream_t>(stream));
+    st = score_one(q, items, c, sps::kModeExact, out, nullptr, ld_out, rs,
+                   reinterpret_cast<hipStream_t>(stream));
     if (st != SPS_OK) return st;
   }
   return SPS_OK;

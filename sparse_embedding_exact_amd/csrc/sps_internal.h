@@ -167,7 +167,11 @@ struct QueriesDev {
 hipError_t launch_prepare_queries(const QueriesDev &d, hipStream_t s);
 
 // ---- scoring ----
+// output modes of the score kernel: fp32 scores, fp16 scores (reduced-precision
+// variant), or only the scores >= a threshold as (row, item, score) hits
+enum ScoreMode : int32_t { kModeExact = 0, kModeHalf = 1, kModeThreshold = 2 };
 struct ScoreArgs {
+  ScoreMode mode;
   Geom g;
   int64_t dim, n_q;
   int32_t n_groups;
@@ -185,6 +189,10 @@ struct ScoreArgs {
   int32_t pitch;
   float *out;
   uint16_t *out16;            // fp16 output of the reduced-precision variant (else null)
+  int3 *hits;                 // threshold output (row, item, score bits) (else null)
+  int64_t hit_cap;
+  unsigned long long *hit_count;
+  float threshold;
   int64_t ld;
   double *rs_part;            // n_sub * n_q partial row sums (nullable)
   double *row_sums;           // n_q (nullable)

@@ -83,6 +83,8 @@ __device__ __forceinline__ u32x4 ld_quad4(const uint32_t *base, uint32_t byte_of
   return *reinterpret_cast<const u32x4_a4 *>(reinterpret_cast<const char *>(base) + byte_off);
 }
 
+constexpr int kOutExact = kModeExact, kOutHalf = kModeHalf, kOutThreshold = kModeThreshold;
+
 constexpr int NT = kScoreThreads;
 constexpr int NW = NT / 64;
 constexpr int kBatch = 2 * NT;  // light entries per batch, two per thread
@@ -97,12 +99,15 @@ constexpr int kSegMax = 896;         // segments per round
 constexpr int kSegPad = 16 * NW * 2;  // one walk step past the end (16 segments, 2 per wave)
 static_assert(kRows * kSliceMax * 4 < (1 << 27), "row byte offset fits the segment record");
 
-// HALF: the reduced-precision variant (item values as fp16, scores written
-// as fp16; see sps_cosine_chunk_half): 4-byte postings, four per lane and
-// load, the slab's hi halves only, fp16 output.
-template <bool DENSE, bool HALF>
+// MODE kOutExact: fp32 scores. kOutHalf: the reduced-precision variant (item
+// values as fp16, scores written as fp16; see sps_cosine_chunk_half): 4-byte
+// postings, four per lane and load, the slab's hi halves only, fp16 output.
+// kOutThreshold: the exact scores, of which only those >= a.threshold are
+// written, as (row, item, score) hits (see sps_cosine_chunk_threshold).
+template <bool DENSE, int MODE>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void score_kernel(
     const ScoreArgs a, int vec4) {
+  constexpr bool HALF = MODE == kOutHalf;
   constexpr int U = 2;                      // segment groups per wave per walk step
   constexpr int PPL = HALF ? 4 : 2;         // postings per lane (one 16-byte load)
   constexpr int LPS = kSeg / PPL;           // lanes per segment
@@ -425,6 +430,49 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void sc
       if (q >= a.n_q) break;
       const int4 *arow = reinterpret_cast<const int4 *>(acc + r * Lp);
       double rs = 0.0;
+      if (MODE == kOutThreshold) {
+        // the row's scores >= threshold as hits: count this lane's, reserve
+        // the wave's range with one atomic, then write them (re-read from LDS);
+        // the row sum is of all the row's fp32 scores
+        int cnt = 0;
+        for (int j0 = 4 * lane; j0 < slen; j0 += 256) {
+          const int4 x = arow[j0 >> 2];
+          const int xs[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            if (j0 + u < slen) {
+              const float v = (float)xs[u] * kFixInv;
+              cnt += v >= a.threshold ? 1 : 0;
+              rs += (double)v;
+            }
+        }
+        const int incl = wave_incl_scan_dpp(cnt);
+        const int total = __builtin_amdgcn_readlane(incl, 63);
+        if (total > 0) {
+          unsigned long long base = 0;
+          if (lane == 0) base = atomicAdd(a.hit_count, (unsigned long long)total);
+          base = (unsigned long long)__shfl(base, 0, 64);
+          unsigned long long k = base + (unsigned long long)(incl - cnt);
+          for (int j0 = 4 * lane; j0 < slen; j0 += 256) {
+            const int4 x = arow[j0 >> 2];
+            const int xs[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const float v = (float)xs[u] * kFixInv;
+              if (j0 + u < slen && v >= a.threshold) {
+                if (k < (unsigned long long)a.hit_cap)
+                  a.hits[k] = make_int3((int32_t)q, (int32_t)(ib + j0 + u), __float_as_int(v));
+                ++k;
+              }
+            }
+          }
+        }
+        if (rsum != nullptr) {
+          rs = wave_sum(rs);
+          if (lane == 0) rsum[(g.n_sub == 1 ? 0 : (int64_t)ks * a.n_q) + q] = rs;
+        }
+        continue;
+      }
       if (HALF) {
         // fp16(fl32(acc) * 2^-30), 8-byte stores when aligned; the row sum is
         // of the fp16 values written
@@ -495,10 +543,11 @@ size_t score_lds_bytes(int32_t S) {
   return (size_t)kRows * acc_pitch(S) * sizeof(int) + (kSegMax + kSegPad) * 12 + NW * 4;
 }
 
-template <bool DENSE, bool HALF>
+template <bool DENSE, int MODE>
 static hipError_t launch_t(const ScoreArgs &a, hipStream_t s) {
+  constexpr bool HALF = MODE == kOutHalf;
   const size_t dyn = (size_t)kRows * acc_pitch(a.g.S) * sizeof(int);
-  auto kern = score_kernel<DENSE, HALF>;
+  auto kern = score_kernel<DENSE, MODE>;
   // dynamic LDS above 64 KiB needs an explicit opt-in per kernel
   static size_t opted = 65536;
   if (dyn > opted) {
@@ -518,12 +567,25 @@ static hipError_t launch_t(const ScoreArgs &a, hipStream_t s) {
 
 hipError_t launch_score(const ScoreArgs &a, hipStream_t s) {
   if (a.n_groups == 0) return hipSuccess;
-  const bool half = a.out16 != nullptr;
   hipError_t e;
-  if (a.dense) {
-    e = half ? launch_t<true, true>(a, s) : launch_t<true, false>(a, s);
-  } else {
-    e = half ? launch_t<false, true>(a, s) : launch_t<false, false>(a, s);
+  // the mode is explicit: a threshold pass may count without a hit buffer
+  // (capacity 0, hits null), which must not select a scoring mode
+  switch (a.mode) {
+    case kModeThreshold:
+      if (a.hit_count == nullptr || (a.hit_cap > 0 && a.hits == nullptr))
+        return hipErrorInvalidValue;
+      e = a.dense ? launch_t<true, kOutThreshold>(a, s) : launch_t<false, kOutThreshold>(a, s);
+      break;
+    case kModeHalf:
+      if (a.out16 == nullptr || a.post4 == nullptr) return hipErrorInvalidValue;
+      e = a.dense ? launch_t<true, kOutHalf>(a, s) : launch_t<false, kOutHalf>(a, s);
+      break;
+    case kModeExact:
+      if (a.out == nullptr) return hipErrorInvalidValue;
+      e = a.dense ? launch_t<true, kOutExact>(a, s) : launch_t<false, kOutExact>(a, s);
+      break;
+    default:
+      return hipErrorInvalidValue;
   }
   if (e != hipSuccess) return e;
   if (a.row_sums != nullptr && a.g.n_sub > 1) {
