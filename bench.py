@@ -14,7 +14,9 @@ around every score launch, on the stream the kernels run on), and the
 float64 CPU oracle timed on a bounded sample of the same workload. The
 reduced-precision variant (fp16 item values and scores, |error| < 1e-3, as
 §5.3 of the page allows) is timed the same way and reported under
-"variants"; it never stands in for the exact path's value.
+"variants", and so is the threshold-filtered output (the exact scores >= t,
+t = 0.5 unless --threshold says otherwise, appended as (row, item, score)
+hits); neither ever stands in for the exact path's value.
 """
 from __future__ import annotations
 
@@ -41,6 +43,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-half", action="store_true",
                     help="skip the fp16 reduced-precision variant's timing")
+    ap.add_argument("--threshold", type=float, default=0.5,
+                    help="score threshold of the threshold-filtered variant's timing")
+    ap.add_argument("--no-threshold", dest="threshold", action="store_const", const=None,
+                    help="skip the threshold-filtered variant's timing")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles",
                                                       "score_kernel_pages_traffic.txt"),
                     help="measured HBM bytes per score launch (rocprofv3 FETCH_SIZE / "
@@ -138,39 +144,50 @@ def main():
           for _ in range(n_chunks)]
     ev_prep = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
 
-    def step(record):
-        if record:
-            ev_prep[0].record(stream)
-        it = sps.prepare(items, chunk_size=C)
-        qq = sps.prepare_queries(queries, it)
-        if record:
-            ev_prep[1].record(stream)
-        for c in range(n_chunks):
+    def make_step(score_chunk, half=False, before=None):
+        """One pass of the path: prepare items and queries, then score every chunk."""
+        def step(record):
+            if before is not None:
+                before()
             if record:
-                ev[c][0].record(stream)
-            sps.cosine_chunk(qq, it, c, out, sums[c])
+                ev_prep[0].record(stream)
+            it = sps.prepare(items, chunk_size=C)
+            if half:
+                it.enable_half()
+            qq = sps.prepare_queries(queries, it)
             if record:
-                ev[c][1].record(stream)
-        return it, qq
+                ev_prep[1].record(stream)
+            for c in range(n_chunks):
+                if record:
+                    ev[c][0].record(stream)
+                score_chunk(qq, it, c)
+                if record:
+                    ev[c][1].record(stream)
+            return it, qq
+        return step
 
-    for _ in range(args.warmup):
-        step(False)
-    torch.cuda.synchronize()
-    kern_ms = np.zeros(n_chunks)
-    prep_ms = 0.0
-    keep = []
-    t_start = time.perf_counter()
-    for s in range(args.steps):
-        keep.append(step(True))
-        torch.cuda.synchronize()  # events of this step are read before the next records them
-        kern_ms += np.array([a.elapsed_time(b) for a, b in ev])
-        prep_ms += ev_prep[0].elapsed_time(ev_prep[1])
-        keep.clear()
-    torch.cuda.synchronize()
-    t_total = time.perf_counter() - t_start
+    def run_timed(step):
+        """Warmup, then exactly args.steps timed steps: (seconds, per-chunk launch ms,
+        prepare ms), the last two averaged over the steps."""
+        for _ in range(args.warmup):
+            step(False)
+        torch.cuda.synchronize()
+        kern = np.zeros(n_chunks)
+        prep = 0.0
+        keep = []
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            keep.append(step(True))
+            torch.cuda.synchronize()  # events of this step are read before the next records them
+            kern += np.array([a.elapsed_time(b) for a, b in ev])
+            prep += ev_prep[0].elapsed_time(ev_prep[1])
+            keep.clear()
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0, kern / args.steps, prep / args.steps
+
+    t_total, kern_ms, prep_ms = run_timed(
+        make_step(lambda qq, it, c: sps.cosine_chunk(qq, it, c, out, sums[c])))
     ms_per_step = 1e3 * t_total / args.steps
-    kern_ms /= args.steps
-    prep_ms /= args.steps
     scores = float(n_q) * float(n_i)
     value = scores * args.steps / t_total
 
@@ -187,53 +204,55 @@ def main():
     log("step %.2f ms: prepare %.2f ms, %d score launches %.2f ms (avg %.3f ms)" %
         (ms_per_step, prep_ms, n_chunks, loop_ms, avg_launch_ms))
 
+    def variant(total, kern, prep, nbytes, **extra):
+        avg = float(kern.mean())
+        ach = float(nbytes.mean()) / (avg * 1e-3) / 1e9
+        d = {"value": scores * args.steps / total, "unit": "scores/s",
+             "ms_per_step": 1e3 * total / args.steps}
+        d.update(extra)
+        d["breakdown_ms"] = {"prepare": prep, "score_loop": float(kern.sum()),
+                             "score_launch_avg": avg}
+        d["roofline"] = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBPS,
+                         "unit": "GB/s", "frac": ach / HBM_PEAK_GBPS}
+        return d
+
     # the reduced-precision variant (fp16 item values and scores, |error| < 1e-3),
     # timed the same way; reported beside the exact path, never as `value`
     half = None
     if not args.no_half:
         out16 = torch.empty(n_q, min(C, n_i), dtype=torch.float16, device=dev)
+        h_total, h_kern, h_prep = run_timed(make_step(
+            lambda qq, it, c: sps.cosine_chunk_half(qq, it, c, out16, sums[c]), half=True))
+        half = variant(h_total, h_kern, h_prep,
+                       2.0 * n_q * chunk_len + 4.0 * chunk_nnz + 8.0 * n_q,
+                       dtype="f16", max_abs_error_bound=1e-3)
+        log("fp16 variant: step %.2f ms, avg launch %.3f ms" %
+            (half["ms_per_step"], half["breakdown_ms"]["score_launch_avg"]))
 
-        def step_half(record):
-            if record:
-                ev_prep[0].record(stream)
-            it = sps.prepare(items, chunk_size=C)
-            it.enable_half()
-            qq = sps.prepare_queries(queries, it)
-            if record:
-                ev_prep[1].record(stream)
-            for c in range(n_chunks):
-                if record:
-                    ev[c][0].record(stream)
-                sps.cosine_chunk_half(qq, it, c, out16, sums[c])
-                if record:
-                    ev[c][1].record(stream)
-            return it, qq
-
-        for _ in range(args.warmup):
-            step_half(False)
+    # threshold-filtered output: the exact scores >= t appended as 12-byte hits;
+    # an untimed counting pass (capacity 0) sizes the hit buffer, so no hit of a
+    # timed step is dropped
+    thr = None
+    if args.threshold is not None:
+        t_ = float(args.threshold)
+        count = torch.zeros(1, dtype=torch.int64, device=dev)
+        no_hits = torch.empty(0, 3, dtype=torch.int32, device=dev)
+        count_step = make_step(
+            lambda qq, it, c: sps.cosine_chunk_threshold(qq, it, c, t_, no_hits, count, sums[c]),
+            before=count.zero_)
+        count_step(False)
         torch.cuda.synchronize()
-        h_kern = np.zeros(n_chunks)
-        h_prep = 0.0
-        t0 = time.perf_counter()
-        for s_ in range(args.steps):
-            keep.append(step_half(True))
-            torch.cuda.synchronize()
-            h_kern += np.array([a.elapsed_time(b) for a, b in ev])
-            h_prep += ev_prep[0].elapsed_time(ev_prep[1])
-            keep.clear()
-        h_total = time.perf_counter() - t0
-        h_kern /= args.steps
-        h_bytes = 2.0 * n_q * chunk_len + 4.0 * chunk_nnz + 8.0 * n_q
-        h_avg = float(h_kern.mean())
-        h_ach = float(h_bytes.mean()) / (h_avg * 1e-3) / 1e9
-        half = {"value": scores * args.steps / h_total, "unit": "scores/s",
-                "ms_per_step": 1e3 * h_total / args.steps, "dtype": "f16",
-                "max_abs_error_bound": 1e-3,
-                "breakdown_ms": {"prepare": h_prep / args.steps, "score_loop": float(h_kern.sum()),
-                                 "score_launch_avg": h_avg},
-                "roofline": {"bound": "hbm", "achieved": h_ach, "peak": HBM_PEAK_GBPS,
-                             "unit": "GB/s", "frac": h_ach / HBM_PEAK_GBPS}}
-        log("fp16 variant: step %.2f ms, avg launch %.3f ms" % (half["ms_per_step"], h_avg))
+        n_hits = int(count.item())
+        hits = torch.empty(n_hits, 3, dtype=torch.int32, device=dev)
+        t_total_, t_kern, t_prep = run_timed(make_step(
+            lambda qq, it, c: sps.cosine_chunk_threshold(qq, it, c, t_, hits, count, sums[c]),
+            before=count.zero_))
+        assert int(count.item()) == n_hits
+        thr = variant(t_total_, t_kern, t_prep,
+                      8.0 * chunk_nnz + 8.0 * n_q + 12.0 * n_hits / n_chunks,
+                      dtype="f32", threshold=t_, hits=n_hits)
+        log("threshold %.2f variant: %d hits, step %.2f ms, avg launch %.3f ms" %
+            (t_, n_hits, thr["ms_per_step"], thr["breakdown_ms"]["score_launch_avg"]))
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -274,7 +293,7 @@ def main():
         "breakdown_ms": {"prepare": prep_ms, "score_loop": loop_ms,
                          "score_launch_avg": avg_launch_ms},
         "step_hbm_gbps_algorithmic": float(alg_bytes.sum()) / (ms_per_step * 1e-3) / 1e9,
-        "variants": {"fp16": half},
+        "variants": {"fp16": half, "threshold": thr},
     }
     print(json.dumps(res), flush=True)
 

@@ -120,6 +120,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void sc
   __shared__ uint32_t s_spos[kSegMax + kSegPad], s_sqv[kSegMax + kSegPad],
       s_smeta[kSegMax + kSegPad];
   __shared__ int32_t ws[NW];
+  // threshold epilogue: hits per wave of the current group, and the group's
+  // first position in the hit buffer
+  __shared__ int32_t s_wtot[NW];
+  __shared__ unsigned long long s_hbase;
 
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const Geom &g = a.g;
@@ -422,37 +426,62 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void sc
     }
     cur = nxt;
 
-    // ---- epilogue: wave w writes rows w, w + NW, ... of the group ----
+    if (MODE == kOutThreshold) {
+      // ---- epilogue: the group's scores >= threshold as hits ----
+      // Wave w counts rows w, w + NW, ... (and sums all their scores for the
+      // row sums); one atomic per group reserves the group's range of the
+      // hit buffer, laid out wave by wave, row by row, lane by lane; then
+      // each wave re-reads its rows from LDS and writes its hits.
+      constexpr int RW = kRows / NW;
+      int cnt[RW], incl[RW], tot[RW];
+      int wtot = 0;
 #pragma unroll
-    for (int rr = 0; rr < kRows / NW; ++rr) {
-      const int r = wv + NW * rr;
-      const int64_t q = q0 + r;
-      if (q >= a.n_q) break;
-      const int4 *arow = reinterpret_cast<const int4 *>(acc + r * Lp);
-      double rs = 0.0;
-      if (MODE == kOutThreshold) {
-        // the row's scores >= threshold as hits: count this lane's, reserve
-        // the wave's range with one atomic, then write them (re-read from LDS);
-        // the row sum is of all the row's fp32 scores
-        int cnt = 0;
-        for (int j0 = 4 * lane; j0 < slen; j0 += 256) {
-          const int4 x = arow[j0 >> 2];
-          const int xs[4] = {x.x, x.y, x.z, x.w};
+      for (int rr = 0; rr < RW; ++rr) {
+        const int r = wv + NW * rr;
+        const int64_t q = q0 + r;
+        const int4 *arow = reinterpret_cast<const int4 *>(acc + r * Lp);
+        double rs = 0.0;
+        int c = 0;
+        if (q < a.n_q) {
+          for (int j0 = 4 * lane; j0 < slen; j0 += 256) {
+            const int4 x = arow[j0 >> 2];
+            const int xs[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
-          for (int u = 0; u < 4; ++u)
-            if (j0 + u < slen) {
-              const float v = (float)xs[u] * kFixInv;
-              cnt += v >= a.threshold ? 1 : 0;
-              rs += (double)v;
-            }
+            for (int u = 0; u < 4; ++u)
+              if (j0 + u < slen) {
+                const float v = (float)xs[u] * kFixInv;
+                c += v >= a.threshold ? 1 : 0;
+                rs += (double)v;
+              }
+          }
         }
-        const int incl = wave_incl_scan_dpp(cnt);
-        const int total = __builtin_amdgcn_readlane(incl, 63);
-        if (total > 0) {
-          unsigned long long base = 0;
-          if (lane == 0) base = atomicAdd(a.hit_count, (unsigned long long)total);
-          base = (unsigned long long)__shfl(base, 0, 64);
-          unsigned long long k = base + (unsigned long long)(incl - cnt);
+        cnt[rr] = c;
+        incl[rr] = wave_incl_scan_dpp(c);
+        tot[rr] = __builtin_amdgcn_readlane(incl[rr], 63);
+        wtot += tot[rr];
+        if (rsum != nullptr && q < a.n_q) {
+          rs = wave_sum(rs);
+          if (lane == 0) rsum[(g.n_sub == 1 ? 0 : (int64_t)ks * a.n_q) + q] = rs;
+        }
+      }
+      if (lane == 0) s_wtot[wv] = wtot;
+      __syncthreads();
+      if (t == 0) {
+        int sum = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) sum += s_wtot[w];
+        s_hbase = sum > 0 ? atomicAdd(a.hit_count, (unsigned long long)sum) : 0ull;
+      }
+      __syncthreads();
+      unsigned long long k0 = s_hbase;
+      for (int w = 0; w < wv; ++w) k0 += (unsigned long long)s_wtot[w];
+#pragma unroll
+      for (int rr = 0; rr < RW; ++rr) {
+        if (tot[rr] > 0) {
+          const int r = wv + NW * rr;
+          const int64_t q = q0 + r;
+          const int4 *arow = reinterpret_cast<const int4 *>(acc + r * Lp);
+          unsigned long long k = k0 + (unsigned long long)(incl[rr] - cnt[rr]);
           for (int j0 = 4 * lane; j0 < slen; j0 += 256) {
             const int4 x = arow[j0 >> 2];
             const int xs[4] = {x.x, x.y, x.z, x.w};
@@ -466,13 +495,20 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void sc
               }
             }
           }
+          k0 += (unsigned long long)tot[rr];
         }
-        if (rsum != nullptr) {
-          rs = wave_sum(rs);
-          if (lane == 0) rsum[(g.n_sub == 1 ? 0 : (int64_t)ks * a.n_q) + q] = rs;
-        }
-        continue;
       }
+      continue;
+    }
+
+    // ---- epilogue: wave w writes rows w, w + NW, ... of the group ----
+#pragma unroll
+    for (int rr = 0; rr < kRows / NW; ++rr) {
+      const int r = wv + NW * rr;
+      const int64_t q = q0 + r;
+      if (q >= a.n_q) break;
+      const int4 *arow = reinterpret_cast<const int4 *>(acc + r * Lp);
+      double rs = 0.0;
       if (HALF) {
         // fp16(fl32(acc) * 2^-30), 8-byte stores when aligned; the row sum is
         // of the fp16 values written
@@ -540,7 +576,7 @@ __global__ void fold_row_sums_kernel(int64_t n_q, int32_t n_sub, const double *_
 }
 
 size_t score_lds_bytes(int32_t S) {
-  return (size_t)kRows * acc_pitch(S) * sizeof(int) + (kSegMax + kSegPad) * 12 + NW * 4;
+  return (size_t)kRows * acc_pitch(S) * sizeof(int) + (kSegMax + kSegPad) * 12 + 2 * NW * 4 + 8;
 }
 
 template <bool DENSE, int MODE>
