@@ -16,7 +16,9 @@ reduced-precision variant (fp16 item values and scores, |error| < 1e-3, as
 §5.3 of the page allows) is timed the same way and reported under
 "variants", and so is the threshold-filtered output (the exact scores >= t,
 t = 0.5 unless --threshold says otherwise, appended as (row, item, score)
-hits); neither ever stands in for the exact path's value.
+hits), and so is the output streamed into pinned host memory (the first
+--host-chunks chunks, against a plain device-to-host copy's rate); none of
+them ever stands in for the exact path's value.
 """
 from __future__ import annotations
 
@@ -47,6 +49,9 @@ def parse():
                     help="score threshold of the threshold-filtered variant's timing")
     ap.add_argument("--no-threshold", dest="threshold", action="store_const", const=None,
                     help="skip the threshold-filtered variant's timing")
+    ap.add_argument("--host-chunks", type=int, default=4,
+                    help="chunks streamed into pinned host memory for the host-output "
+                         "variant's timing (0 skips it)")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles",
                                                       "score_kernel_pages_traffic.txt"),
                     help="measured HBM bytes per score launch (rocprofv3 FETCH_SIZE / "
@@ -254,6 +259,43 @@ def main():
         log("threshold %.2f variant: %d hits, step %.2f ms, avg launch %.3f ms" %
             (t_, n_hits, thr["ms_per_step"], thr["breakdown_ms"]["score_launch_avg"]))
 
+    # the output streamed to pinned host memory (double-buffered, the copy
+    # engine on a side stream): `host_chunks` chunks after one prepare, against a
+    # plain device-to-host copy of one chunk's bytes, the link's own rate
+    host = None
+    if args.host_chunks > 0:
+        K = min(args.host_chunks, n_chunks)
+        span = min(K * C, n_i)
+        hout = torch.empty(n_q, span, dtype=torch.float32, pin_memory=True)
+        it_h = sps.prepare(items, chunk_size=C)
+        qq_h = sps.prepare_queries(queries, it_h)
+        sps.cosine_stream_host(qq_h, it_h, 0, K, hout)  # warm-up
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            sps.cosine_stream_host(qq_h, it_h, 0, K, hout)
+        torch.cuda.synchronize()
+        hs = (time.perf_counter() - t0) / args.steps
+        probe = torch.empty(n_q, min(C, n_i), dtype=torch.float32, device=dev)
+        probe_h = torch.empty(n_q, min(C, n_i), dtype=torch.float32, pin_memory=True)
+        probe_h.copy_(probe, non_blocking=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            probe_h.copy_(probe, non_blocking=True)
+        torch.cuda.synchronize()
+        cs = (time.perf_counter() - t0) / args.steps
+        link = 4.0 * probe.numel() / cs / 1e9
+        rate = 4.0 * n_q * span / hs / 1e9
+        host = {"value": float(n_q) * span / hs, "unit": "scores/s", "dtype": "f32",
+                "chunks": K, "ms_per_range": 1e3 * hs, "ms_per_chunk": 1e3 * hs / K,
+                "d2h_gbps": rate, "plain_d2h_copy_gbps": link, "frac_of_plain_copy": rate / link,
+                "note": "prepare excluded; the full %d-chunk matrix (%.0f GB) would take %.1f s "
+                        "at this rate" % (n_chunks, 4.0 * n_q * n_i / 1e9, 4.0 * n_q * n_i / 1e9 / rate)}
+        del hout, probe, probe_h, it_h, qq_h
+        log("host stream: %d chunks in %.1f ms (%.1f GB/s; plain D2H copy %.1f GB/s)" %
+            (K, 1e3 * hs, rate, link))
+
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
@@ -293,7 +335,7 @@ def main():
         "breakdown_ms": {"prepare": prep_ms, "score_loop": loop_ms,
                          "score_launch_avg": avg_launch_ms},
         "step_hbm_gbps_algorithmic": float(alg_bytes.sum()) / (ms_per_step * 1e-3) / 1e9,
-        "variants": {"fp16": half, "threshold": thr},
+        "variants": {"fp16": half, "threshold": thr, "host_stream": host},
     }
     print(json.dumps(res), flush=True)
 

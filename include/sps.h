@@ -212,6 +212,33 @@ sps_status sps_cosine_stream(const sps_queries *q, const sps_items *items, int32
                              int32_t chunk_end, float *out, int64_t ld_out, double *row_sums,
                              void *stream);
 
+/* The streaming loop with the output on the host (§2.2, §4.4: each chunk's
+ * scores are accumulated into a host output buffer). Chunks [chunk_begin,
+ * chunk_end) are scored in turn into the two DEVICE buffers dev_buf0 and
+ * dev_buf1 (n_rows * ld_dev floats each, ld_dev >= min(chunk_size, n_items),
+ * distinct), alternately, on `stream`; the copy engine moves each chunk into
+ * its column block of the host matrix on `copy_stream`, so that the copy of
+ * one chunk overlaps the scoring of the next:
+ *     host_out[q * ld_host + (item - item_begin)] = S[q, item]
+ * for every item of the range, item_begin = chunk_begin * chunk_size.
+ * host_out: page-locked HOST memory (hipHostMalloc, or a pinned torch
+ * tensor), n_rows * ld_host floats, ld_host >= the number of items in the
+ * range; columns past them are not touched. row_sums (nullable): DEVICE
+ * double[(chunk_end-chunk_begin) * n_rows], chunk-major, as in
+ * sps_cosine_stream. The work completes in `stream` order (the stream waits
+ * for the last copy): synchronise `stream` before reading host_out. Both
+ * buffers and host_out must stay untouched until then. copy_stream should
+ * be a stream other than `stream` (the same one is correct but serialises
+ * the copies with the scoring). Errors: SPS_ERR_INVALID_ARGUMENT (NULL or
+ * equal buffers, host_out not page-locked, ld too small),
+ * SPS_ERR_CHUNK_RANGE, SPS_ERR_OVERFLOW; SPS_ERR_HIP if a runtime call fails
+ * (then part of the range may have been enqueued). */
+sps_status sps_cosine_stream_host(const sps_queries *q, const sps_items *items,
+                                  int32_t chunk_begin, int32_t chunk_end, float *host_out,
+                                  int64_t ld_host, float *dev_buf0, float *dev_buf1,
+                                  int64_t ld_dev, double *row_sums, void *stream,
+                                  void *copy_stream);
+
 /* One score kept by sps_cosine_chunk_threshold: query row, global item
  * index, and the float32 score. */
 typedef struct {

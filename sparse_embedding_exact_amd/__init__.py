@@ -80,6 +80,7 @@ SIGNATURES = {
     "sps_queries_destroy": (None, [_P]),
     "sps_cosine_chunk": (_I32, [_P, _P, _I32, _P, _I64, _P, _P]),
     "sps_cosine_stream": (_I32, [_P, _P, _I32, _I32, _P, _I64, _P, _P]),
+    "sps_cosine_stream_host": (_I32, [_P, _P, _I32, _I32, _P, _I64, _P, _P, _I64, _P, _P, _P]),
     "sps_cosine_chunk_threshold": (_I32, [_P, _P, _I32, ctypes.c_float, _P, _I64, _P, _P, _P]),
     "sps_items_half_workspace_size": (_I32, [_P, ctypes.POINTER(_SZ)]),
     "sps_items_enable_half": (_I32, [_P, _P, _SZ, _P]),
@@ -376,6 +377,58 @@ def cosine_stream(q: Queries, items: Items, chunk_begin: int, chunk_end: int,
                                   _stream_ptr(stream)))
 
 
+_copy_streams: dict = {}
+
+
+def _copy_stream(device) -> "torch.cuda.Stream":
+    """One side stream per device for device-to-host copies (default priority)."""
+    idx = torch.device(device).index
+    idx = torch.cuda.current_device() if idx is None else idx
+    if idx not in _copy_streams:
+        _copy_streams[idx] = torch.cuda.Stream(device=idx)
+    return _copy_streams[idx]
+
+
+def cosine_stream_host(q: Queries, items: Items, chunk_begin: int, chunk_end: int,
+                       host_out: torch.Tensor, bufs=None, row_sums: torch.Tensor | None = None,
+                       stream=None, copy_stream=None) -> None:
+    """Chunks [chunk_begin, chunk_end) into the pinned host matrix host_out
+    (n_query x >= the range's items, float32, row-major), column 0 being item
+    chunk_begin * chunk_size: scored into two alternating device buffers, each
+    copied out by the copy engine on a side stream while the next is scored.
+    Asynchronous in `stream` order: synchronise before reading host_out."""
+    assert not host_out.is_cuda and host_out.is_pinned(), "host_out must be a pinned CPU tensor"
+    assert host_out.dtype == torch.float32 and host_out.dim() == 2
+    assert host_out.stride(1) == 1 and host_out.shape[0] == q.n_rows
+    ld_host = host_out.stride(0) if q.n_rows > 1 else host_out.shape[1]
+    if chunk_end > chunk_begin:
+        span = min(chunk_end * items.chunk_size, items.n_items) - chunk_begin * items.chunk_size
+        assert host_out.shape[1] >= span, "host_out narrower than the chunk range"
+    s = stream if stream is not None else torch.cuda.current_stream()
+    dev = s.device
+    if bufs is None:
+        width = max(min(items.chunk_size, items.n_items), 1)
+        bufs = tuple(torch.empty(q.n_rows, width, dtype=torch.float32, device=dev)
+                     for _ in range(2))
+        for b in bufs:  # freed by the caller's stream order only after the copies
+            b.record_stream(s)
+    b0, b1 = bufs
+    assert b0.is_cuda and b0.dtype == torch.float32 and b0.stride(1) == 1
+    assert b1.shape == b0.shape and b1.stride() == b0.stride() and b1.dtype == b0.dtype
+    assert b0.shape[0] == q.n_rows and b0.shape[1] >= min(items.chunk_size, items.n_items)
+    ld_dev = b0.stride(0) if q.n_rows > 1 else b0.shape[1]
+    rs = None
+    if row_sums is not None:
+        assert row_sums.is_cuda and row_sums.dtype == torch.float64 and row_sums.is_contiguous()
+        assert row_sums.numel() >= (chunk_end - chunk_begin) * q.n_rows
+        rs = row_sums.data_ptr()
+    cs = copy_stream if copy_stream is not None else _copy_stream(dev)
+    _check(_lib.sps_cosine_stream_host(q._h, items._h, chunk_begin, chunk_end,
+                                       host_out.data_ptr(), ld_host, b0.data_ptr(),
+                                       b1.data_ptr(), ld_dev, rs, int(s.cuda_stream),
+                                       int(cs.cuda_stream)))
+
+
 def row_inv_norms(m: CSR, stream=None) -> torch.Tensor:
     load_library()
     out = torch.empty(m.n_rows, dtype=torch.float32, device=m.indptr.device)
@@ -411,13 +464,17 @@ def bulk_similarity(queries: CSR, items: CSR, chunk_size: int = 8192, out=None,
     """
     it = prepare(items, chunk_size)
     q = prepare_queries(queries, it)
+    dev = queries.indptr.device
+    if out is not None and on_chunk is None and not out.is_cuda and out.is_pinned():
+        # pinned host output: double-buffered, the copies overlapping the scoring
+        cosine_stream_host(q, it, 0, it.num_chunks, out)
+        torch.cuda.current_stream().synchronize()
+        return out
     width = min(chunk_size, it.n_items)
-    buf = torch.empty(queries.n_rows, max(width, 1), dtype=torch.float32,
-                      device=queries.indptr.device)
-    sums = torch.empty(queries.n_rows, dtype=torch.float64, device=buf.device) \
-        if row_sums else None
+    buf = torch.empty(queries.n_rows, max(width, 1), dtype=torch.float32, device=dev)
+    sums = torch.empty(queries.n_rows, dtype=torch.float64, device=dev) if row_sums else None
     if out is None and on_chunk is None:
-        out = torch.empty(queries.n_rows, it.n_items, dtype=torch.float32, device=buf.device)
+        out = torch.empty(queries.n_rows, it.n_items, dtype=torch.float32, device=dev)
     for c in range(it.num_chunks):
         cosine_chunk(q, it, c, buf, sums)
         n = it.chunk_len(c)

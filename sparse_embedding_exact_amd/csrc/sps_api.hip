@@ -557,6 +557,74 @@ sps_status sps_cosine_stream(const sps_queries *q, const sps_items *items, int32
   return SPS_OK;
 }
 
+sps_status sps_cosine_stream_host(const sps_queries *q, const sps_items *items,
+                                  int32_t chunk_begin, int32_t chunk_end, float *host_out,
+                                  int64_t ld_host, float *dev_buf0, float *dev_buf1,
+                                  int64_t ld_dev, double *row_sums, void *stream,
+                                  void *copy_stream) {
+  sps_status st = check_score_args(q, items, dev_buf0, ld_dev);
+  if (st != SPS_OK) return st;
+  if (chunk_begin < 0 || chunk_end > items->g.num_chunks || chunk_begin > chunk_end)
+    return fail(SPS_ERR_CHUNK_RANGE, "chunk range [%d, %d) outside [0, %d)", chunk_begin,
+                chunk_end, items->g.num_chunks);
+  if (chunk_begin == chunk_end || q->n_rows == 0) return SPS_OK;
+  if (!dev_buf1 || dev_buf1 == dev_buf0)
+    return fail(SPS_ERR_INVALID_ARGUMENT, "two distinct device buffers are needed");
+  if (!host_out) return fail(SPS_ERR_INVALID_ARGUMENT, "NULL host output");
+  const int64_t item0 = items->g.chunk_begin(chunk_begin);
+  const int64_t span = items->g.chunk_end(chunk_end - 1) - item0;
+  if (ld_host < span)
+    return fail(SPS_ERR_INVALID_ARGUMENT, "ld_host %lld below the range's %lld items",
+                (long long)ld_host, (long long)span);
+  if ((uint64_t)ld_host > (uint64_t)INT64_MAX / 4 / (uint64_t)q->n_rows)
+    return fail(SPS_ERR_OVERFLOW, "n_rows * ld_host overflows");
+  // the copy engine overlaps only with page-locked host memory
+  hipPointerAttribute_t attr;
+  const hipError_t pe = hipPointerGetAttributes(&attr, host_out);
+  if (pe != hipSuccess || attr.type != hipMemoryTypeHost) {
+    (void)hipGetLastError();  // an unregistered pointer leaves an error behind
+    return fail(SPS_ERR_INVALID_ARGUMENT,
+                "host_out must be page-locked host memory (hipHostMalloc)");
+  }
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const hipStream_t cs = reinterpret_cast<hipStream_t>(copy_stream);
+  float *buf[2] = {dev_buf0, dev_buf1};
+  hipEvent_t scored[2] = {nullptr, nullptr}, copied[2] = {nullptr, nullptr};
+  hipError_t e = hipSuccess;
+  for (int k = 0; k < 2 && e == hipSuccess; ++k) {
+    e = hipEventCreateWithFlags(&scored[k], hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&copied[k], hipEventDisableTiming);
+  }
+  for (int32_t c = chunk_begin; c < chunk_end && e == hipSuccess; ++c) {
+    const int k = (c - chunk_begin) & 1;
+    // buffer k is free once the copy of the chunk before last has left it
+    if (c - chunk_begin >= 2) e = hipStreamWaitEvent(s, copied[k], 0);
+    if (e != hipSuccess) break;
+    double *rs = row_sums ? row_sums + (int64_t)(c - chunk_begin) * q->n_rows : nullptr;
+    st = score_one(q, items, c, sps::kModeExact, buf[k], nullptr, ld_dev, rs, s);
+    if (st != SPS_OK) break;
+    e = hipEventRecord(scored[k], s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(cs, scored[k], 0);
+    const int64_t len = items->g.chunk_end(c) - items->g.chunk_begin(c);
+    if (e == hipSuccess)
+      e = hipMemcpy2DAsync(host_out + (items->g.chunk_begin(c) - item0), (size_t)ld_host * 4,
+                           buf[k], (size_t)ld_dev * 4, (size_t)len * 4, (size_t)q->n_rows,
+                           hipMemcpyDeviceToHost, cs);
+    if (e == hipSuccess) e = hipEventRecord(copied[k], cs);
+  }
+  // the call completes in `stream` order: the stream waits for the last copies
+  const int used = chunk_end - chunk_begin < 2 ? chunk_end - chunk_begin : 2;
+  for (int k = 0; k < used && e == hipSuccess && st == SPS_OK; ++k)
+    e = hipStreamWaitEvent(s, copied[k], 0);
+  for (int k = 0; k < 2; ++k) {
+    if (scored[k]) (void)hipEventDestroy(scored[k]);
+    if (copied[k]) (void)hipEventDestroy(copied[k]);
+  }
+  if (st != SPS_OK) return st;
+  if (e != hipSuccess) return hip_fail(e, "sps_cosine_stream_host");
+  return SPS_OK;
+}
+
 sps_status sps_row_inv_norms(const sps_csr *rows, float *inv_norm, void *stream) {
   sps_status st = check_csr_shape(rows, "rows");
   if (st != SPS_OK) return st;
