@@ -18,6 +18,10 @@ one pair at a time) after the page "ç¨€ç–åµŒå…¥æ‰¹é‡ç›¸ä¼¼åº¦è®¡ç®—çš„å·¥ç¨‹åŒ
 * ``chunk_row_sums`` / ``col_sums`` -- closed forms by linearity of the dot
                         product, used to check chunks too big to merge pair by pair.
 
+``oracle/bsc.py`` holds the Block-Sparse CSR codec of Â§3.2 (block ids
+delta + variable-length coded, 10-bit packed local offsets) in plain Python
+and numpy, pinned in tests/test_oracle_bsc.py.
+
 Pins (tests/test_oracle_pins.py) tie every function to something other than
 itself: brute-force dense dot products, scipy's sparse product, hand-worked
 closed forms, invariants of the cosine, and transposition by scipy.
