@@ -296,6 +296,66 @@ sps_status sps_cosine_chunk_half(const sps_queries *q, const sps_items *items, i
                                  uint16_t *out, int64_t ld_out, double *row_sums, void *stream);
 
 /* ------------------------------------------------------------------ */
+/* Block-Sparse CSR codec                                              */
+/* ------------------------------------------------------------------ */
+
+/* Compressed column indices (§3.2: Block-Sparse CSR). A column d is the pair
+ * (block = d / 1024, offset = d % 1024). Row by row, the block ids (ascending
+ * in a canonical row) are stored as differences from the previous entry's
+ * block id, the first from 0, each as an unsigned base-128 varint (7 value
+ * bits per byte, least significant group first, the high bit set on every
+ * byte of a value but its last: 1 byte below 128, 2 below 16384, 3 for any
+ * int32 column). The 10-bit offsets are packed in entry order over the whole
+ * matrix, least significant bit first: entry k at bits 10k .. 10k + 9 of the
+ * byte stream. Where the page leaves it open: differences restart at each
+ * row, so rows decode independently; the varint bytes of row r start at
+ * bptr[r] (a second row pointer, since they cannot be located by entry).
+ * indptr and values are the CSR's. nnz is limited to (2^31 - 1) / 3. */
+typedef struct {
+  int64_t n_rows;
+  int64_t n_cols;
+  int64_t nnz;
+  const int32_t *indptr;   /* DEVICE int32[n_rows + 1]: entry positions (the CSR's) */
+  const int32_t *bptr;     /* DEVICE int32[n_rows + 1]: byte positions in `blocks` */
+  const uint8_t *blocks;   /* DEVICE uint8[block_bytes]: the block-id varints */
+  int64_t block_bytes;     /* = bptr[n_rows] */
+  const uint8_t *offsets;  /* DEVICE uint8[offsets_bytes]: the packed 10-bit offsets */
+  int64_t offsets_bytes;   /* >= ceil(10 nnz / 8) */
+  const float *values;     /* DEVICE float[nnz] (the CSR's) */
+} sps_bsc;
+
+/* Bytes of the offset stream for nnz entries: ceil(10 nnz / 8) rounded up to
+ * a multiple of 4 (sps_bsc_encode writes whole 32-bit words; the tail bits
+ * are zero). Pure host. */
+sps_status sps_bsc_offsets_bytes(int64_t nnz, size_t *bytes);
+
+/* First half of the encoder (SYNCHRONOUS): checks that m is canonical (as
+ * sps_validate_csr; scratch: DEVICE, >= 64 bytes, 8-byte aligned), writes the
+ * row byte pointers bptr (DEVICE int32[n_rows + 1]) and returns the size of
+ * the varint stream in *block_bytes. Errors: SPS_ERR_BAD_CSR,
+ * SPS_ERR_OVERFLOW (nnz above the limit), SPS_ERR_INVALID_ARGUMENT. */
+sps_status sps_bsc_encode_sizes(const sps_csr *m, int32_t *bptr, void *scratch, void *stream,
+                                int64_t *block_bytes);
+
+/* Second half (asynchronous): the varint stream into blocks (DEVICE
+ * uint8[block_bytes], block_bytes from sps_bsc_encode_sizes for the same m)
+ * and the offset stream into offsets (DEVICE, 4-byte aligned, offsets_bytes
+ * >= sps_bsc_offsets_bytes(nnz)). Nothing is written past either size.
+ * Errors: SPS_ERR_WORKSPACE_TOO_SMALL (offsets), SPS_ERR_INVALID_ARGUMENT. */
+sps_status sps_bsc_encode(const sps_csr *m, const int32_t *bptr, uint8_t *blocks,
+                          int64_t block_bytes, uint8_t *offsets, int64_t offsets_bytes,
+                          void *stream);
+
+/* Decode (asynchronous) the column indices of b into indices (DEVICE
+ * int32[nnz]); with b->indptr and b->values they form the CSR that was
+ * encoded, ready for sps_prepare (which may then drop them). Any contents
+ * are safe to decode: no access leaves the sizes given. If the encoding is
+ * malformed (a row's bytes do not hold exactly its entries, or a value of
+ * more than 3 bytes), *status (DEVICE int32, nullable, zeroed by the caller)
+ * gets bit 1 and the indices are unspecified. */
+sps_status sps_bsc_decode(const sps_bsc *b, int32_t *indices, int32_t *status, void *stream);
+
+/* ------------------------------------------------------------------ */
 /* Stand-alone pieces                                                  */
 /* ------------------------------------------------------------------ */
 

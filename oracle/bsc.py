@@ -158,10 +158,11 @@ def encode(indptr, indices):
     if _MUTANT == 3:
         off = np.array([int("{:010b}".format(int(x))[::-1], 2) for x in off], dtype=np.int64)
     bit = OFFSET_BITS * np.arange(nnz, dtype=np.int64)
-    w = off << (bit % 8)  # up to 17 bits, spread over two bytes
-    np.bitwise_or.at(packed, bit // 8, w & 0xFF)
-    np.bitwise_or.at(packed, bit // 8 + 1, (w >> 8) & 0xFF)
-    np.bitwise_or.at(packed, bit // 8 + 2, (w >> 16) & 0xFF)
+    w = off << (bit % 8)  # up to 17 bits, spread over three bytes from byte bit // 8
+    # bit // 8 = floor(10k / 8) differs for different entries k, so within one
+    # of the three assignments below no byte is named twice
+    for i in range(3):
+        packed[bit // 8 + i] |= (w >> (8 * i)) & 0xFF
     return bptr, out, packed[:offsets_nbytes(nnz)].astype(np.uint8)
 
 

@@ -49,6 +49,14 @@ class _Csr(ctypes.Structure):
                 ("values", ctypes.c_void_p)]
 
 
+class _Bsc(ctypes.Structure):
+    _fields_ = [("n_rows", ctypes.c_int64), ("n_cols", ctypes.c_int64), ("nnz", ctypes.c_int64),
+                ("indptr", ctypes.c_void_p), ("bptr", ctypes.c_void_p),
+                ("blocks", ctypes.c_void_p), ("block_bytes", ctypes.c_int64),
+                ("offsets", ctypes.c_void_p), ("offsets_bytes", ctypes.c_int64),
+                ("values", ctypes.c_void_p)]
+
+
 class _SliceView(ctypes.Structure):
     _fields_ = [("item_begin", ctypes.c_int64), ("slice_len", ctypes.c_int32),
                 ("slice_nnz", ctypes.c_int32), ("col_ptr", ctypes.c_void_p),
@@ -86,6 +94,10 @@ SIGNATURES = {
     "sps_items_enable_half": (_I32, [_P, _P, _SZ, _P]),
     "sps_cosine_chunk_half": (_I32, [_P, _P, _I32, _P, _I64, _P, _P]),
     "sps_row_inv_norms": (_I32, [ctypes.POINTER(_Csr), _P, _P]),
+    "sps_bsc_offsets_bytes": (_I32, [_I64, ctypes.POINTER(_SZ)]),
+    "sps_bsc_encode_sizes": (_I32, [ctypes.POINTER(_Csr), _P, _P, _P, ctypes.POINTER(_I64)]),
+    "sps_bsc_encode": (_I32, [ctypes.POINTER(_Csr), _P, _P, _I64, _P, _I64, _P]),
+    "sps_bsc_decode": (_I32, [ctypes.POINTER(_Bsc), _P, _P, _P]),
     "sps_validate_csr": (_I32, [ctypes.POINTER(_Csr), _P, _P, ctypes.POINTER(_I64),
                                 ctypes.POINTER(_I32)]),
     "sps_status_string": (ctypes.c_char_p, [_I32]),
@@ -169,6 +181,75 @@ class CSR:
         return _Csr(self.n_rows, self.n_cols, self.nnz, self.indptr.data_ptr(),
                     self.indices.data_ptr() if self.nnz else None,
                     self.values.data_ptr() if self.nnz else None)
+
+
+@dataclass
+class BSC:
+    """Device Block-Sparse CSR (§3.2): the CSR's indptr and values, the per-row
+    block-id varint bytes (located by bptr) and the packed 10-bit offsets."""
+    indptr: torch.Tensor   # int32 [n_rows + 1]
+    bptr: torch.Tensor     # int32 [n_rows + 1]
+    blocks: torch.Tensor   # uint8 [bptr[-1]]
+    offsets: torch.Tensor  # uint8, a multiple of 4 bytes
+    values: torch.Tensor   # float32 [nnz]
+    n_rows: int
+    n_cols: int
+
+    @property
+    def nnz(self) -> int:
+        return int(self.values.numel())
+
+    def index_bytes(self) -> int:
+        """Bytes that locate the entries: bptr, varints and offsets (indptr, as in
+        the CSR, left out)."""
+        return 4 * self.bptr.numel() + self.blocks.numel() + (10 * self.nnz + 7) // 8
+
+    def _c(self) -> _Bsc:
+        for t, dt in ((self.indptr, torch.int32), (self.bptr, torch.int32),
+                      (self.blocks, torch.uint8), (self.offsets, torch.uint8),
+                      (self.values, torch.float32)):
+            assert t.is_cuda and t.dtype == dt and t.is_contiguous()
+        return _Bsc(self.n_rows, self.n_cols, self.nnz, self.indptr.data_ptr(),
+                    self.bptr.data_ptr(), self.blocks.data_ptr() if self.blocks.numel() else None,
+                    self.blocks.numel(), self.offsets.data_ptr() if self.offsets.numel() else None,
+                    self.offsets.numel(), self.values.data_ptr() if self.nnz else None)
+
+
+def bsc_encode(m: CSR, stream=None) -> BSC:
+    """Block-Sparse CSR of a canonical CSR (synchronises once, to size the varint
+    stream; raises SpsError for a non-canonical CSR)."""
+    load_library()
+    dev = m.indptr.device
+    c = m._c()
+    bptr = torch.empty(m.n_rows + 1, dtype=torch.int32, device=dev)
+    scratch = torch.empty(16, dtype=torch.int32, device=dev)
+    nbytes = _I64()
+    _check(_lib.sps_bsc_encode_sizes(ctypes.byref(c), bptr.data_ptr(), scratch.data_ptr(),
+                                     _stream_ptr(stream), ctypes.byref(nbytes)))
+    ob = _SZ()
+    _check(_lib.sps_bsc_offsets_bytes(m.nnz, ctypes.byref(ob)))
+    blocks = torch.empty(nbytes.value, dtype=torch.uint8, device=dev)
+    offsets = torch.empty(ob.value, dtype=torch.uint8, device=dev)
+    _check(_lib.sps_bsc_encode(ctypes.byref(c), bptr.data_ptr(),
+                               blocks.data_ptr() if nbytes.value else None, nbytes.value,
+                               offsets.data_ptr() if ob.value else None, ob.value,
+                               _stream_ptr(stream)))
+    return BSC(m.indptr, bptr, blocks, offsets, m.values, m.n_rows, m.n_cols)
+
+
+def bsc_decode(b: BSC, stream=None, check: bool = True) -> CSR:
+    """The CSR of a Block-Sparse CSR (its indptr and values shared). With check,
+    synchronises and raises SpsError for a malformed encoding."""
+    load_library()
+    dev = b.indptr.device
+    indices = torch.empty(b.nnz, dtype=torch.int32, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    c = b._c()
+    _check(_lib.sps_bsc_decode(ctypes.byref(c), indices.data_ptr() if b.nnz else None,
+                               status.data_ptr(), _stream_ptr(stream)))
+    if check and int(status.item()) != 0:
+        raise SpsError(-2, "malformed Block-Sparse CSR (status %d)" % int(status.item()))
+    return CSR(b.indptr, indices, b.values, b.n_rows, b.n_cols)
 
 
 class Items:
@@ -273,9 +354,12 @@ def items_workspace_size(n_items: int, dim: int, nnz: int, chunk_size: int) -> t
     return p.value, s.value
 
 
-def prepare(items: CSR, chunk_size: int = 8192, stream=None) -> Items:
-    """Norms + per-chunk inverted lists of an item corpus (asynchronous)."""
+def prepare(items, chunk_size: int = 8192, stream=None) -> Items:
+    """Norms + per-chunk inverted lists of an item corpus (asynchronous). items is a
+    CSR, or a BSC whose indices are decoded on the device first."""
     load_library()
+    if isinstance(items, BSC):
+        items = bsc_decode(items, stream)
     pb, sb = items_workspace_size(items.n_rows, items.n_cols, items.nnz, chunk_size)
     dev = items.indptr.device
     pbuf, pptr = _workspace(pb, dev)

@@ -8,7 +8,8 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
-SOURCES = [os.path.join(CSRC, f) for f in ("sps_prepare.hip", "sps_score.hip", "sps_api.hip")]
+SOURCES = [os.path.join(CSRC, f) for f in ("sps_prepare.hip", "sps_score.hip", "sps_bsc.hip",
+                                                  "sps_api.hip")]
 HEADERS = [os.path.join(ROOT, "include", "sps.h"), os.path.join(CSRC, "sps_internal.h"),
            os.path.join(CSRC, "sps_device.h")]
 LIB = os.path.join(PKG, "libsps.so")

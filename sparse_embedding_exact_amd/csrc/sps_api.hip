@@ -625,6 +625,84 @@ sps_status sps_cosine_stream_host(const sps_queries *q, const sps_items *items,
   return SPS_OK;
 }
 
+// ---- Block-Sparse CSR codec ----
+
+// at most three varint bytes per entry of an int32 column: the byte
+// positions stay below 2^31
+constexpr int64_t kBscMaxNnz = kI32Max / 3;
+
+static int64_t bsc_offsets_needed(int64_t nnz) { return (10 * nnz + 7) / 8; }
+
+sps_status sps_bsc_offsets_bytes(int64_t nnz, size_t *bytes) {
+  if (!bytes || nnz < 0) return fail(SPS_ERR_INVALID_ARGUMENT, "NULL argument or negative nnz");
+  *bytes = (size_t)((bsc_offsets_needed(nnz) + 3) / 4 * 4);
+  return SPS_OK;
+}
+
+sps_status sps_bsc_encode_sizes(const sps_csr *m, int32_t *bptr, void *scratch, void *stream,
+                                int64_t *block_bytes) {
+  if (block_bytes) *block_bytes = 0;
+  sps_status st = check_csr_shape(m, "csr");
+  if (st != SPS_OK) return st;
+  if (!bptr || !block_bytes) return fail(SPS_ERR_INVALID_ARGUMENT, "NULL bptr or block_bytes");
+  if (m->nnz > kBscMaxNnz)
+    return fail(SPS_ERR_OVERFLOW, "nnz %lld above the codec's %lld", (long long)m->nnz,
+                (long long)kBscMaxNnz);
+  st = sps_validate_csr(m, scratch, stream, nullptr, nullptr);
+  if (st != SPS_OK) return st;
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = sps::launch_bsc_row_bytes(m->n_rows, m->nnz, m->indptr, m->indices, bptr, s);
+  int32_t total = 0;
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(&total, bptr + m->n_rows, sizeof total, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "sps_bsc_encode_sizes");
+  *block_bytes = total;
+  return SPS_OK;
+}
+
+sps_status sps_bsc_encode(const sps_csr *m, const int32_t *bptr, uint8_t *blocks,
+                          int64_t block_bytes, uint8_t *offsets, int64_t offsets_bytes,
+                          void *stream) {
+  sps_status st = check_csr_shape(m, "csr");
+  if (st != SPS_OK) return st;
+  if (m->nnz > kBscMaxNnz) return fail(SPS_ERR_OVERFLOW, "nnz above the codec's limit");
+  if (!bptr || block_bytes < 0 || (block_bytes > 0 && !blocks))
+    return fail(SPS_ERR_INVALID_ARGUMENT, "NULL bptr or blocks, or negative block_bytes");
+  size_t need = 0;
+  sps_bsc_offsets_bytes(m->nnz, &need);
+  if (offsets_bytes < (int64_t)need || (need > 0 && !offsets))
+    return fail(SPS_ERR_WORKSPACE_TOO_SMALL, "offsets: %zu bytes needed", need);
+  if (reinterpret_cast<uintptr_t>(offsets) & 3)
+    return fail(SPS_ERR_INVALID_ARGUMENT, "offsets must be 4-byte aligned");
+  const hipError_t e = sps::launch_bsc_encode(
+      m->n_rows, m->nnz, m->indptr, m->indices, bptr, blocks, block_bytes,
+      reinterpret_cast<uint32_t *>(offsets), (int64_t)need / 4,
+      reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "sps_bsc_encode");
+  return SPS_OK;
+}
+
+sps_status sps_bsc_decode(const sps_bsc *b, int32_t *indices, int32_t *status, void *stream) {
+  if (!b) return fail(SPS_ERR_INVALID_ARGUMENT, "NULL matrix");
+  if (b->n_rows < 0 || b->nnz < 0 || b->block_bytes < 0 || b->offsets_bytes < 0)
+    return fail(SPS_ERR_INVALID_ARGUMENT, "negative size");
+  if (b->n_rows >= kI32Max || b->nnz > kBscMaxNnz || b->block_bytes >= kI32Max)
+    return fail(SPS_ERR_OVERFLOW, "sizes above the codec's limits");
+  if (!b->indptr || !b->bptr || (b->block_bytes > 0 && !b->blocks))
+    return fail(SPS_ERR_INVALID_ARGUMENT, "NULL indptr, bptr or blocks");
+  if (b->nnz > 0 && (!indices || !b->offsets))
+    return fail(SPS_ERR_INVALID_ARGUMENT, "NULL indices or offsets");
+  if (b->offsets_bytes < bsc_offsets_needed(b->nnz))
+    return fail(SPS_ERR_INVALID_ARGUMENT, "offsets: %lld bytes, %lld needed",
+                (long long)b->offsets_bytes, (long long)bsc_offsets_needed(b->nnz));
+  const hipError_t e = sps::launch_bsc_decode(b->n_rows, b->nnz, b->indptr, b->bptr,
+                                              b->block_bytes, b->blocks, b->offsets, indices,
+                                              status, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "sps_bsc_decode");
+  return SPS_OK;
+}
+
 sps_status sps_row_inv_norms(const sps_csr *rows, float *inv_norm, void *stream) {
   sps_status st = check_csr_shape(rows, "rows");
   if (st != SPS_OK) return st;

@@ -112,6 +112,8 @@ __host__ __device__ inline int32_t acc_pitch(int32_t S) { return slab_pitch(S) +
 inline bool dense_slice_ok(int32_t S) { return S >= kDenseMinSlice; }
 
 hipError_t launch_fill_i32(int32_t *p, int64_t n, int32_t v, hipStream_t s);
+// inclusive scan in place over a[0..n) (one workgroup)
+hipError_t launch_scan_inplace(int32_t *a, int64_t n, hipStream_t s);
 hipError_t launch_csr_check(int64_t n_rows, int64_t n_cols, int64_t nnz, const int32_t *indptr,
                             const int32_t *indices, const float *values, int full,
                             int32_t *flags, hipStream_t s);
@@ -197,6 +199,20 @@ struct ScoreArgs {
   double *rs_part;            // n_sub * n_q partial row sums (nullable)
   double *row_sums;           // n_q (nullable)
 };
+// ---- Block-Sparse CSR codec (sps_bsc.hip) ----
+// bptr[0] = 0, bptr[r + 1] = bytes of rows 0..r's block-id varints
+hipError_t launch_bsc_row_bytes(int64_t n_rows, int64_t nnz, const int32_t *indptr,
+                                const int32_t *indices, int32_t *bptr, hipStream_t s);
+hipError_t launch_bsc_encode(int64_t n_rows, int64_t nnz, const int32_t *indptr,
+                             const int32_t *indices, const int32_t *bptr, uint8_t *blocks,
+                             int64_t block_bytes, uint32_t *offset_words, int64_t n_words,
+                             hipStream_t s);
+// status |= 1 for a malformed encoding
+hipError_t launch_bsc_decode(int64_t n_rows, int64_t nnz, const int32_t *indptr,
+                             const int32_t *bptr, int64_t n_bytes, const uint8_t *blocks,
+                             const uint8_t *offsets, int32_t *indices, int32_t *status,
+                             hipStream_t s);
+
 size_t score_lds_bytes(int32_t S);
 hipError_t launch_score(const ScoreArgs &a, hipStream_t s);
 

@@ -55,6 +55,12 @@ __global__ __launch_bounds__(NT) void scan_inplace_kernel(int32_t *__restrict__ 
   }
 }
 
+hipError_t launch_scan_inplace(int32_t *a, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(scan_inplace_kernel<1024>, dim3(1), dim3(1024), 0, s, a, n);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------------------
 // CSR check. flags layout in sps_internal.h.
 // bit: flag bit (1 indptr, 4 index range -> structural; 2 order, 8 non-finite)

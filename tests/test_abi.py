@@ -67,8 +67,24 @@ def test_null_handles_rejected(lib):
     assert lib.sps_queries_workspace_size(None, 10, 10, 10, ctypes.byref(size)) == -1
     assert lib.sps_row_inv_norms(None, None, None) == -1
     assert lib.sps_validate_csr(None, None, None, None, None) == -1
+    assert lib.sps_cosine_stream_host(None, None, 0, 1, None, 8192, None, None, 8192, None,
+                                      None, None) == -1
+    assert lib.sps_cosine_chunk_threshold(None, None, 0, 0.5, None, 0, None, None, None) == -1
+    assert lib.sps_bsc_decode(None, None, None, None) == -1
+    assert lib.sps_bsc_encode_sizes(None, None, None, None, None) == -1
+    assert lib.sps_bsc_encode(None, None, None, 0, None, 0, None) == -1
     lib.sps_items_destroy(None)
     lib.sps_queries_destroy(None)
+
+
+def test_bsc_offset_sizing(lib):
+    """ceil(10 nnz / 8) bytes of 10-bit offsets, rounded up to whole 32-bit words."""
+    n = ctypes.c_size_t()
+    for nnz, want in ((0, 0), (1, 4), (3, 4), (4, 8), (8, 12), (16, 20), (85_991_513, 107_489_392)):
+        assert lib.sps_bsc_offsets_bytes(nnz, ctypes.byref(n)) == 0
+        assert n.value == want, nnz
+    assert lib.sps_bsc_offsets_bytes(-1, ctypes.byref(n)) == -1
+    assert lib.sps_bsc_offsets_bytes(5, None) == -1
 
 
 def test_csr_shape_checks(lib):
