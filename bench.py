@@ -17,8 +17,9 @@ reduced-precision variant (fp16 item values and scores, |error| < 1e-3, as
 "variants", and so is the threshold-filtered output (the exact scores >= t,
 t = 0.5 unless --threshold says otherwise, appended as (row, item, score)
 hits), and so is the output streamed into pinned host memory (the first
---host-chunks chunks, against a plain device-to-host copy's rate); none of
-them ever stands in for the exact path's value.
+--host-chunks chunks, against a plain device-to-host copy's rate) and the
+Block-Sparse CSR form of the item corpus (index bytes, encode and decode
+times); none of them ever stands in for the exact path's value.
 """
 from __future__ import annotations
 
@@ -52,6 +53,8 @@ def parse():
     ap.add_argument("--host-chunks", type=int, default=4,
                     help="chunks streamed into pinned host memory for the host-output "
                          "variant's timing (0 skips it)")
+    ap.add_argument("--no-bsc", action="store_true",
+                    help="skip the Block-Sparse CSR codec's timing")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles",
                                                       "score_kernel_pages_traffic.txt"),
                     help="measured HBM bytes per score launch (rocprofv3 FETCH_SIZE / "
@@ -296,6 +299,36 @@ def main():
         log("host stream: %d chunks in %.1f ms (%.1f GB/s; plain D2H copy %.1f GB/s)" %
             (K, 1e3 * hs, rate, link))
 
+    # Block-Sparse CSR (compressed column indices) of the item corpus: index bytes
+    # against CSR's, the encoder's time, and the device decode that precedes a prepare
+    bscv = None
+    if not args.no_bsc:
+        t0 = time.perf_counter()
+        bz = sps.bsc_encode(items)  # synchronises once to size the varint stream
+        torch.cuda.synchronize()
+        enc_ms = 1e3 * (time.perf_counter() - t0)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        sps.bsc_decode(bz, check=True)  # warm-up, and a well-formed check
+        reps = 10
+        e0.record(stream)
+        for _ in range(reps):
+            sps.bsc_decode(bz, check=False)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        dec_ms = e0.elapsed_time(e1) / reps
+        nnz_i = int(i_host.nnz)
+        dec_bytes = 8.0 * (n_i + 1) + bz.blocks.numel() + (10 * nnz_i + 7) // 8 + 4.0 * nnz_i
+        bscv = {"index_bytes_per_entry": bz.index_bytes() / nnz_i,
+                "csr_index_bytes_per_entry": 4.0,
+                "index_saving": 1.0 - bz.index_bytes() / (4.0 * nnz_i),
+                "encode_ms": enc_ms, "decode_ms": dec_ms,
+                "roofline": {"bound": "hbm", "achieved": dec_bytes / (dec_ms * 1e-3) / 1e9,
+                             "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                             "frac": dec_bytes / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}}
+        del bz
+        log("bsc: %.3f index bytes per entry (CSR 4), encode %.1f ms, decode %.3f ms" %
+            (bscv["index_bytes_per_entry"], enc_ms, dec_ms))
+
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
@@ -335,7 +368,7 @@ def main():
         "breakdown_ms": {"prepare": prep_ms, "score_loop": loop_ms,
                          "score_launch_avg": avg_launch_ms},
         "step_hbm_gbps_algorithmic": float(alg_bytes.sum()) / (ms_per_step * 1e-3) / 1e9,
-        "variants": {"fp16": half, "threshold": thr, "host_stream": host},
+        "variants": {"fp16": half, "threshold": thr, "host_stream": host, "bsc": bscv},
     }
     print(json.dumps(res), flush=True)
 
