@@ -272,7 +272,8 @@ __global__ __launch_bounds__(256) void csc_count_kernel(Geom g, int64_t dim,
 }
 
 // One workgroup per slice: exclusive scan of dim+1 counts in place, each
-// thread owning 16 consecutive counts of a tile (four 16-byte loads); plus
+// thread owning 8 consecutive counts of a tile (two 16-byte loads, issued
+// for the next tile before this one is scanned and stored); plus
 // the compacted list of dims with >= 2 entries. The scan carries (count,
 // multi-flag) packed in one 64-bit value: slice nnz < 2^31 keeps the count
 // half from carrying into the flag half.
@@ -287,7 +288,7 @@ __global__ __launch_bounds__(NT) void csc_scan_kernel(int64_t dim,
                                                       int32_t *__restrict__ mlist,
                                                       int32_t *__restrict__ mcount,
                                                       int32_t *__restrict__ gdf, int32_t hmin) {
-  constexpr int PER = 16;
+  constexpr int PER = 8;
   constexpr int TILE = PER * NT;
   __shared__ int64_t ws[NT / 64];
   const int64_t c = blockIdx.x;
@@ -301,17 +302,27 @@ __global__ __launch_bounds__(NT) void csc_scan_kernel(int64_t dim,
   int32_t *ml = mlist + (slice_base[c] / 2 + c);
   const int64_t n = dim + 1;
   int64_t carry = 0;
+  // the next tile's counts are loaded while this one is scanned and stored
+  int4 x[PER / 4], xn[PER / 4];
+  auto load = [&](int64_t base, int4 (&dst)[PER / 4]) {
+#pragma unroll
+    for (int k = 0; k < PER / 4; ++k) {
+      const int64_t j = base + (int64_t)PER * t + 4 * k;
+      dst[k] = j < pitch ? cp4[j >> 2] : make_int4(0, 0, 0, 0);
+    }
+  };
+  load(0, x);
   for (int64_t base = 0; base < n; base += TILE) {
     const int64_t j0 = base + (int64_t)PER * t;
+    if (base + TILE < n) load(base + TILE, xn);
     int32_t v[PER];
 #pragma unroll
     for (int k = 0; k < PER / 4; ++k) {
       const int64_t j = j0 + 4 * k;
-      const int4 x = j < pitch ? cp4[j >> 2] : make_int4(0, 0, 0, 0);
-      v[4 * k] = j < n ? x.x : 0;
-      v[4 * k + 1] = j + 1 < n ? x.y : 0;
-      v[4 * k + 2] = j + 2 < n ? x.z : 0;
-      v[4 * k + 3] = j + 3 < n ? x.w : 0;
+      v[4 * k] = j < n ? x[k].x : 0;
+      v[4 * k + 1] = j + 1 < n ? x[k].y : 0;
+      v[4 * k + 2] = j + 2 < n ? x[k].z : 0;
+      v[4 * k + 3] = j + 3 < n ? x[k].w : 0;
     }
     int64_t sum = 0;
 #pragma unroll
@@ -342,6 +353,8 @@ __global__ __launch_bounds__(NT) void csc_scan_kernel(int64_t dim,
       }
     }
     carry += tot;
+#pragma unroll
+    for (int k = 0; k < PER / 4; ++k) x[k] = xn[k];
   }
   if (t == 0) mcount[c] = (int32_t)(carry >> 32);
 }
