@@ -78,6 +78,7 @@ __device__ __forceinline__ u32x4 ld_pair(const uint2 *base, uint32_t byte_off) {
 }
 
 // four consecutive 4-byte postings with one 16-byte load (4-byte aligned)
+typedef uint32_t u32x2_a4 __attribute__((ext_vector_type(2), aligned(4)));
 typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
 __device__ __forceinline__ u32x4 ld_quad4(const uint32_t *base, uint32_t byte_off) {
   return *reinterpret_cast<const u32x4_a4 *>(reinterpret_cast<const char *>(base) + byte_off);
@@ -183,8 +184,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void sc
       const bool dok = r.rec[i].x < (uint64_t)a.dim;
       r.ok[i] = r.ok[i] && dok;
       const int32_t d = dok ? (int32_t)r.rec[i].x : 0;
-      r.lo[i] = cps[d];
-      r.hi[i] = cps[d + 1];
+      // cps[d] and cps[d + 1] with one 8-byte load (4-byte aligned)
+      const u32x2 lh = *reinterpret_cast<const u32x2_a4 *>(cps + d);
+      r.lo[i] = (int32_t)lh.x;
+      r.hi[i] = (int32_t)lh.y;
     }
   };
   auto finish_ranges = [&](const Raw &r, Desc &b) {
