@@ -88,7 +88,7 @@ T *at(void *base, size_t off) {
 
 struct ItemsLayout {
   size_t inv, colp, post, sbase, heavy, slab, persistent;
-  size_t flags, norm64, ticket, trow, tval, mlist, mcount, gdf, hsel, scratch;
+  size_t flags, norm64, skey0, skey1, spay, gdf, hsel, scratch;
   bool overflow;
 };
 
@@ -106,11 +106,9 @@ ItemsLayout items_layout(const sps::Geom &g, int64_t dim, int64_t nnz, bool dens
   Layout s;
   L.flags = s.add(sps::kFlagsInts, 4);
   L.norm64 = s.add(g.n_items, 8);
-  L.ticket = s.add(nnz, 4);
-  L.trow = s.add(nnz, 2);
-  L.tval = s.add(nnz, 4);
-  L.mlist = s.add(nnz / 2 + ns + 1, 4);
-  L.mcount = s.add(ns, 4);
+  L.skey0 = s.add(nnz, 4);
+  L.skey1 = s.add(nnz, 4);
+  L.spay = s.add(nnz, 8);
   L.gdf = s.add(dense ? (uint64_t)dim : 0, 4);
   L.hsel = s.add(dense ? sps::kHeavySelInts : 0, 4);
   L.scratch = s.off;
@@ -252,11 +250,9 @@ sps_status sps_prepare(const sps_csr *items, int32_t chunk_size, void *persisten
   d.slab = dense ? at<uint16_t>(persistent, L.slab) : nullptr;
   d.flags = at<int32_t>(scratch, L.flags);
   d.norm64 = at<double>(scratch, L.norm64);
-  d.ticket = at<int32_t>(scratch, L.ticket);
-  d.trow = at<uint16_t>(scratch, L.trow);
-  d.tval = at<float>(scratch, L.tval);
-  d.mlist = at<int32_t>(scratch, L.mlist);
-  d.mcount = at<int32_t>(scratch, L.mcount);
+  d.skey[0] = at<int32_t>(scratch, L.skey0);
+  d.skey[1] = at<int32_t>(scratch, L.skey1);
+  d.spay = at<uint2>(scratch, L.spay);
   d.gdf = dense ? at<int32_t>(scratch, L.gdf) : nullptr;
   d.hsel = dense ? at<int32_t>(scratch, L.hsel) : nullptr;
 

@@ -137,11 +137,8 @@ struct ItemsDev {
   uint16_t *slab;       // persistent, [num_slices][pitch / 16 tiles] split fp16 (dense only)
   int32_t *flags;       // scratch
   double *norm64;       // scratch, n_items
-  int32_t *ticket;      // scratch, nnz
-  uint16_t *trow;       // scratch, nnz
-  float *tval;          // scratch, nnz
-  int32_t *mlist;       // scratch, nnz/2 + num_slices + 1
-  int32_t *mcount;      // scratch, num_slices
+  int32_t *skey[2];     // scratch, nnz each: columns during the radix sort (sorted: skey[0])
+  uint2 *spay;          // scratch, nnz: (item, value) during the radix sort
   int32_t *gdf;         // scratch, dim (dense only)
   int32_t *hsel;        // scratch, kHeavySelInts (dense only): heavy-dim candidates
 };

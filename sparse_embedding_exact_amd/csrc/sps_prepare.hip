@@ -253,236 +253,201 @@ __global__ void slice_base_kernel(Geom g, int64_t nnz, const int32_t *__restrict
   slice_base[s] = (int32_t)clamp64(indptr[i], 0, nnz);
 }
 
-// 16 lanes per item, so that a row's indices are read coalesced.
-constexpr int kLanesPerItem = 16;
+// Per-slice inverted lists in two kernels, one workgroup per slice each:
+//  csc_sort_pass_kernel   a stable LSD radix sort of the slice's entries by
+//                         column (8-bit digits, one launch per digit). The
+//                         first pass reads the CSR in item order and carries
+//                         (slice-local item, fl32(v / |item|)); stability keeps
+//                         the items ascending within each column, and the last
+//                         pass writes the postings in place.
+//  csc_colptr_kernel      col_ptr of the slice from its sorted columns: tiles
+//                         of 8192 columns, each a histogram in LDS of the
+//                         keys that fall in it (a contiguous run of the sorted
+//                         keys), scanned and written once.
+constexpr int kSortNT = 1024;
+constexpr int kSortWaves = kSortNT / 64;
 
-__global__ __launch_bounds__(256) void csc_count_kernel(Geom g, int64_t dim,
-                                                        const int32_t *__restrict__ indptr,
-                                                        const int32_t *__restrict__ indices,
-                                                        const int32_t *__restrict__ flags,
-                                                        int32_t *__restrict__ col_ptr,
-                                                        int32_t *__restrict__ ticket) {
-  const int64_t gt = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t i = gt / kLanesPerItem;
-  const int sub = (int)(gt % kLanesPerItem);
-  if (i >= g.n_items || flags[0] != 0) return;
-  const int64_t b = indptr[i], e = indptr[i + 1];
-  int32_t *cp = col_ptr + g.slice_of(i) * cp_pitch(dim);
-  for (int64_t k = b + sub; k < e; k += kLanesPerItem) ticket[k] = atomicAdd(&cp[indices[k]], 1);
+// The slice's entries go through in tiles of kSortNT, in order: within a
+// tile each entry's place is its digit's running base, plus the counts of
+// the digit in the waves before its own, plus its rank among the lanes of
+// its wave holding the same digit.
+template <bool FIRST>
+__global__ __launch_bounds__(kSortNT) void csc_sort_pass_kernel(
+    Geom g, const int32_t *__restrict__ flags, const int32_t *__restrict__ indptr,
+    const int32_t *__restrict__ indices, const float *__restrict__ values,
+    const double *__restrict__ norm64, const int32_t *__restrict__ slice_base,
+    const int32_t *__restrict__ src_key, const uint2 *__restrict__ src_pay,
+    int32_t *__restrict__ dst_key, uint2 *__restrict__ dst_pay, int shift) {
+  __shared__ uint32_t s_hist[256];             // digit counts, then running bases
+  __shared__ uint32_t s_cnt[kSortWaves][256];  // per-wave digit counts of a tile
+  __shared__ int32_t s_ptr[kSliceMax + 1];     // first pass: item starts in the slice
+  __shared__ int32_t s_ws[kSortWaves];
+  if (flags[0] != 0) return;
+  const int64_t sl = blockIdx.x;
+  const int64_t b = slice_base[sl];
+  const int64_t n = slice_base[sl + 1] - b;
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int64_t i0 = g.slice_begin(sl);
+  int32_t nitems = 0;
+  if (FIRST) {
+    nitems = (int32_t)(g.slice_end(sl) - i0);
+    for (int k = t; k <= nitems; k += kSortNT) s_ptr[k] = (int32_t)(indptr[i0 + k] - b);
+  }
+  const int32_t *kin = FIRST ? indices + b : src_key + b;
+  if (t < 256) s_hist[t] = 0u;
+  __syncthreads();
+  for (int64_t i = t; i < n; i += kSortNT)
+    atomicAdd(&s_hist[((uint32_t)kin[i] >> shift) & 255u], 1u);
+  __syncthreads();
+  {
+    const int32_t v = t < 256 ? (int32_t)s_hist[t] : 0;
+    int32_t tot;
+    const int32_t incl = block_incl_scan_1b<kSortNT>(v, s_ws, &tot);
+    if (t < 256) s_hist[t] = (uint32_t)(incl - v);
+  }
+  const uint64_t lt = lane ? (~0ull >> (64 - lane)) : 0ull;
+  uint32_t *cflat = &s_cnt[0][0];
+  for (int64_t base = 0; base < n; base += kSortNT) {
+    const int64_t i = base + t;
+    const bool valid = i < n;
+    int32_t key = 0;
+    uint2 pay = make_uint2(0u, 0u);
+    if (valid) {
+      key = kin[i];
+      if (FIRST) {
+        // the item of entry i: the last item starting at or before it
+        int lo = 0, hi = nitems;
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (s_ptr[mid] <= i) lo = mid;
+          else hi = mid;
+        }
+        const double nrm = norm64[i0 + lo];
+        const float w = nrm > 0.0 ? (float)((double)values[b + i] / nrm) : 0.0f;
+        pay = make_uint2((uint32_t)lo, __float_as_uint(w));
+      } else {
+        pay = src_pay[b + i];
+      }
+    }
+    const uint32_t digit = ((uint32_t)key >> shift) & 255u;
+    // the lanes holding the same digit (stable rank = those below this lane)
+    uint64_t m = __ballot(valid);
+#pragma unroll
+    for (int bit = 0; bit < 8; ++bit) {
+      const bool x = (digit >> bit) & 1u;
+      const uint64_t bb = __ballot(x);
+      m &= x ? bb : ~bb;
+    }
+    for (int k = t; k < kSortWaves * 256; k += kSortNT) cflat[k] = 0u;
+    __syncthreads();
+    if (valid && (m & lt) == 0) s_cnt[wv][digit] = (uint32_t)__popcll(m);
+    __syncthreads();
+    if (t < 256) {
+      uint32_t run = s_hist[t];
+      for (int w = 0; w < kSortWaves; ++w) {
+        const uint32_t c = s_cnt[w][t];
+        s_cnt[w][t] = run;
+        run += c;
+      }
+      s_hist[t] = run;
+    }
+    __syncthreads();
+    if (valid) {
+      const int64_t dst = b + s_cnt[wv][digit] + __popcll(m & lt);
+      dst_key[dst] = key;
+      dst_pay[dst] = pay;
+    }
+    __syncthreads();  // this tile's offsets are read before the next tile clears them
+  }
 }
 
-// One workgroup per slice: exclusive scan of dim+1 counts in place, each
-// thread owning 8 consecutive counts of a tile (two 16-byte loads, issued
-// for the next tile before this one is scanned and stored); plus
-// the compacted list of dims with >= 2 entries. The scan carries (count,
-// multi-flag) packed in one 64-bit value: slice nnz < 2^31 keeps the count
-// half from carrying into the flag half.
-// When gdf is given, every dim holding at least `hmin` entries of the slice
-// adds its count to gdf[d] (the document frequency used to pick heavy dims;
-// integer atomics, so the totals do not depend on the order of slices).
-template <int NT>
-__global__ __launch_bounds__(NT) void csc_scan_kernel(int64_t dim,
-                                                      const int32_t *__restrict__ flags,
-                                                      const int32_t *__restrict__ slice_base,
-                                                      int32_t *__restrict__ col_ptr,
-                                                      int32_t *__restrict__ mlist,
-                                                      int32_t *__restrict__ mcount,
-                                                      int32_t *__restrict__ gdf, int32_t hmin) {
-  constexpr int PER = 8;
-  constexpr int TILE = PER * NT;
-  __shared__ int64_t ws[NT / 64];
-  const int64_t c = blockIdx.x;
+// col_ptr[d] of the slice = the number of its entries with column < d, for
+// d = 0 .. dim; a structural fault leaves every list empty. With gdf, every
+// column holding at least hmin entries of the slice adds its count to gdf[d].
+constexpr int kCpNT = 512;
+constexpr int kCpPer = 16;
+constexpr int kCpTile = kCpPer * kCpNT;
+__global__ __launch_bounds__(kCpNT) void csc_colptr_kernel(
+    int64_t dim, const int32_t *__restrict__ flags, const int32_t *__restrict__ slice_base,
+    const int32_t *__restrict__ keys, int32_t *__restrict__ col_ptr, int32_t *__restrict__ gdf,
+    int32_t hmin) {
+  __shared__ int32_t s_h[kCpTile];
+  __shared__ int32_t s_ws[kCpNT / 64];
+  const int64_t sl = blockIdx.x;
+  const bool fault = flags[0] != 0;
+  const int64_t b = fault ? 0 : slice_base[sl];
+  const int64_t n = fault ? 0 : slice_base[sl + 1] - b;
+  const int32_t *ks = keys + b;
+  int32_t *cp = col_ptr + sl * cp_pitch(dim);
   const int t = threadIdx.x;
-  if (flags[0] != 0) {
-    if (t == 0) mcount[c] = 0;
-    return;
-  }
-  const int64_t pitch = cp_pitch(dim);  // a multiple of 4: the int4 accesses stay inside
-  int4 *cp4 = reinterpret_cast<int4 *>(col_ptr + c * pitch);
-  int32_t *ml = mlist + (slice_base[c] / 2 + c);
-  const int64_t n = dim + 1;
-  int64_t carry = 0;
-  // the next tile's counts are loaded while this one is scanned and stored
-  int4 x[PER / 4], xn[PER / 4];
-  auto load = [&](int64_t base, int4 (&dst)[PER / 4]) {
+  const int64_t ncp = dim + 1;
+  int64_t p0 = 0;  // entries with a column below this tile
+  // the first key chunk of the next tile is loaded before this tile's scan
+  int32_t kc = t < n ? ks[t] : 0;
+  for (int64_t D0 = 0; D0 < ncp; D0 += kCpTile) {
+    int4 *h4 = reinterpret_cast<int4 *>(s_h);
 #pragma unroll
-    for (int k = 0; k < PER / 4; ++k) {
-      const int64_t j = base + (int64_t)PER * t + 4 * k;
-      dst[k] = j < pitch ? cp4[j >> 2] : make_int4(0, 0, 0, 0);
+    for (int k = 0; k < kCpPer / 4; ++k) h4[k * kCpNT + t] = make_int4(0, 0, 0, 0);
+    __syncthreads();
+    // the tile's keys are the next run of the sorted keys
+    const int64_t Dend = D0 + kCpTile;
+    int64_t q = p0;
+    int32_t k = kc;
+    for (;;) {
+      const int64_t i = q + t;
+      const bool in = i < n && k < Dend;
+      if (in && k >= D0) atomicAdd(&s_h[k - D0], 1);  // (sorted keys are >= D0 here)
+      const int c = __syncthreads_count(in);
+      q += c;
+      k = q + t < n ? ks[q + t] : 0;
+      if (c < kCpNT) break;
     }
-  };
-  load(0, x);
-  for (int64_t base = 0; base < n; base += TILE) {
-    const int64_t j0 = base + (int64_t)PER * t;
-    if (base + TILE < n) load(base + TILE, xn);
-    int32_t v[PER];
+    kc = k;
+    // thread t: columns D0 + 16 t .. + 15 (four 16-byte LDS reads)
+    int32_t v[kCpPer];
+    int32_t sum = 0;
 #pragma unroll
-    for (int k = 0; k < PER / 4; ++k) {
-      const int64_t j = j0 + 4 * k;
-      v[4 * k] = j < n ? x[k].x : 0;
-      v[4 * k + 1] = j + 1 < n ? x[k].y : 0;
-      v[4 * k + 2] = j + 2 < n ? x[k].z : 0;
-      v[4 * k + 3] = j + 3 < n ? x[k].w : 0;
+    for (int k = 0; k < kCpPer / 4; ++k) {
+      const int4 x = h4[t * (kCpPer / 4) + k];
+      v[4 * k] = x.x;
+      v[4 * k + 1] = x.y;
+      v[4 * k + 2] = x.z;
+      v[4 * k + 3] = x.w;
+      sum += (x.x + x.y) + (x.z + x.w);
     }
-    int64_t sum = 0;
+    int32_t tot;
+    const int32_t incl = block_incl_scan_1b<kCpNT>(sum, s_ws, &tot);
+    int32_t ex = (int32_t)p0 + incl - sum;
+    const int64_t j0 = D0 + (int64_t)kCpPer * t;
+    int32_t o[kCpPer];
 #pragma unroll
-    for (int k = 0; k < PER; ++k) {
-      sum += (int64_t)v[k] + ((int64_t)(v[k] >= 2) << 32);
-      if (gdf != nullptr && v[k] >= hmin) atomicAdd(&gdf[j0 + k], v[k]);
+    for (int k = 0; k < kCpPer; ++k) {
+      o[k] = ex;
+      ex += v[k];
+      if (gdf != nullptr && v[k] >= hmin && j0 + k < dim) atomicAdd(&gdf[j0 + k], v[k]);
     }
-    int64_t tot;
-    const int64_t incl = block_incl_scan<NT>(sum, ws, &tot);
-    int64_t ex = carry + incl - sum;
-    int32_t o[PER];
+    // the tile's values back to LDS in column order (each thread overwrites
+    // only its own counts), then stored with consecutive lanes on
+    // consecutive 16 bytes
 #pragma unroll
-    for (int k = 0; k < PER; ++k) {
-      o[k] = (int32_t)(ex & 0xFFFFFFFFll);
-      if (v[k] >= 2) ml[ex >> 32] = (int32_t)(j0 + k);
-      ex += (int64_t)v[k] + ((int64_t)(v[k] >= 2) << 32);
-    }
+    for (int k = 0; k < kCpPer / 4; ++k)
+      h4[t * (kCpPer / 4) + k] = make_int4(o[4 * k], o[4 * k + 1], o[4 * k + 2], o[4 * k + 3]);
+    __syncthreads();
 #pragma unroll
-    for (int k = 0; k < PER / 4; ++k) {
-      const int64_t j = j0 + 4 * k;
-      if (j + 3 < n) {
-        cp4[j >> 2] = make_int4(o[4 * k], o[4 * k + 1], o[4 * k + 2], o[4 * k + 3]);
+    for (int k = 0; k < kCpPer / 4; ++k) {
+      const int64_t j = D0 + 4 * ((int64_t)k * kCpNT + t);
+      const int4 x = h4[k * kCpNT + t];
+      if (j + 3 < ncp) {
+        reinterpret_cast<int4 *>(cp)[j >> 2] = x;
       } else {
-        int32_t *cp = col_ptr + c * pitch;
+        const int32_t xs[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
         for (int u = 0; u < 4; ++u)
-          if (j + u < n) cp[j + u] = o[4 * k + u];
+          if (j + u < ncp) cp[j + u] = xs[u];
       }
     }
-    carry += tot;
-#pragma unroll
-    for (int k = 0; k < PER / 4; ++k) x[k] = xn[k];
-  }
-  if (t == 0) mcount[c] = (int32_t)(carry >> 32);
-}
-
-__global__ __launch_bounds__(256) void csc_scatter_kernel(
-    Geom g, int64_t dim, const int32_t *__restrict__ indptr, const int32_t *__restrict__ indices,
-    const float *__restrict__ values, const double *__restrict__ norm64,
-    const int32_t *__restrict__ flags, const int32_t *__restrict__ col_ptr,
-    const int32_t *__restrict__ slice_base, const int32_t *__restrict__ ticket,
-    uint2 *__restrict__ post, uint16_t *__restrict__ trow, float *__restrict__ tval) {
-  const int64_t gt = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t i = gt / kLanesPerItem;
-  const int sub = (int)(gt % kLanesPerItem);
-  if (i >= g.n_items || flags[0] != 0) return;
-  const int64_t sl = g.slice_of(i);
-  const int32_t *cp = col_ptr + sl * cp_pitch(dim);
-  const int64_t base = slice_base[sl];
-  const uint16_t local = (uint16_t)(i - g.slice_begin(sl));
-  const double n = norm64[i];
-  const int64_t b = indptr[i], e = indptr[i + 1];
-  for (int64_t k = b + sub; k < e; k += kLanesPerItem) {
-    const int32_t d = indices[k];
-    const int32_t s = cp[d];
-    const int32_t len = cp[d + 1] - s;
-    const int64_t p = base + s + ticket[k];
-    const float w = (n > 0.0) ? (float)((double)values[k] / n) : 0.0f;
-    if (len == 1) {
-      post[p] = make_uint2(local, __float_as_uint(w));
-    } else {
-      trow[p] = local;
-      tval[p] = w;
-    }
-  }
-}
-
-// Workgroup j of slice c handles list entries j, j+G, j+2G, ... in batches of
-// NT. Dynamic LDS: two arrays of ceil(S/32) uint32 (bitmap, prefix).
-template <int NT>
-__global__ __launch_bounds__(NT) void csc_fixup_kernel(
-    int64_t dim, int32_t S, int32_t G, const int32_t *__restrict__ flags,
-    const int32_t *__restrict__ col_ptr, const int32_t *__restrict__ slice_base,
-    const int32_t *__restrict__ mlist, const int32_t *__restrict__ mcount,
-    const uint16_t *__restrict__ trow, const float *__restrict__ tval,
-    uint2 *__restrict__ post) {
-  extern __shared__ uint32_t fx_smem[];
-  const int nwords = (S + 31) >> 5;
-  uint32_t *bm = fx_smem;
-  uint32_t *pre = fx_smem + nwords;
-  __shared__ int32_t s_s[NT], s_L[NT];
-  __shared__ uint32_t ws[NT / 64];
-  if (flags[0] != 0) return;
-  const int64_t c = blockIdx.x / G;
-  const int64_t g = blockIdx.x % G;
-  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
-  const int32_t *cp = col_ptr + c * cp_pitch(dim);
-  const int64_t base = slice_base[c];
-  const int32_t *ml = mlist + (slice_base[c] / 2 + c);
-  const int64_t m = mcount[c];
-  const int wpt = (nwords + NT - 1) / NT;  // bitmap words per thread
-
-  for (int64_t kb = 0; g + (int64_t)G * kb < m; kb += NT) {
-    const int64_t k = g + (int64_t)G * (kb + t);
-    int32_t s = 0, L = 0;
-    if (k < m) {
-      const int32_t d = ml[k];
-      s = cp[d];
-      L = cp[d + 1] - s;
-    }
-    s_s[t] = s;
-    s_L[t] = L;
-    __syncthreads();
-
-    // lists of 2..64 entries: one wave each, rank by direct comparison
-    for (int j = wv; j < NT; j += NT / 64) {
-      const int32_t Lj = s_L[j];
-      if (Lj < 2 || Lj > 64) continue;
-      const int64_t p0 = base + s_s[j];
-      uint32_t r = 0xFFFFFFFFu;
-      float v = 0.0f;
-      if (lane < Lj) {
-        r = trow[p0 + lane];
-        v = tval[p0 + lane];
-      }
-      int rank = 0;
-      for (int i = 0; i < Lj; ++i) {
-        const uint32_t ri = (uint32_t)__builtin_amdgcn_readlane((int)r, i);
-        rank += (ri < r) ? 1 : 0;
-      }
-      if (lane < Lj) post[p0 + rank] = make_uint2(r, __float_as_uint(v));
-    }
-
-    // lists of more than 64 entries: the whole workgroup, one list at a time
-    for (int j = 0; j < NT; ++j) {
-      const int32_t Lj = s_L[j];
-      if (Lj <= 64) continue;
-      const int64_t p0 = base + s_s[j];
-      for (int w = t; w < nwords; w += NT) bm[w] = 0u;
-      __syncthreads();
-      for (int i = t; i < Lj; i += NT) {
-        const uint32_t r = trow[p0 + i];
-        atomicOr(&bm[r >> 5], 1u << (r & 31));
-      }
-      __syncthreads();
-      uint32_t cnt = 0;
-      for (int q = 0; q < wpt; ++q) {
-        const int w = t * wpt + q;
-        if (w < nwords) cnt += __popc(bm[w]);
-      }
-      uint32_t tot;
-      uint32_t ex = block_incl_scan<NT>(cnt, ws, &tot) - cnt;
-      for (int q = 0; q < wpt; ++q) {
-        const int w = t * wpt + q;
-        if (w < nwords) {
-          pre[w] = ex;
-          ex += __popc(bm[w]);
-        }
-      }
-      __syncthreads();
-      for (int i = t; i < Lj; i += NT) {
-        const uint32_t r = trow[p0 + i];
-        const float v = tval[p0 + i];
-        const uint32_t w = r >> 5;
-        const uint32_t rank = pre[w] + __popc(bm[w] & ((1u << (r & 31)) - 1u));
-        post[p0 + rank] = make_uint2(r, __float_as_uint(v));
-      }
-      __syncthreads();
-    }
-    __syncthreads();
+    p0 = q;
+    __syncthreads();  // the tile is read before the next tile clears it
   }
 }
 
@@ -630,8 +595,6 @@ hipError_t launch_prepare_items(const ItemsDev &d, hipStream_t s) {
   hipLaunchKernelGGL(slice_base_kernel, dim3((unsigned)((ns + 1 + 255) / 256)), dim3(256), 0, s,
                      g, d.nnz, d.indptr, d.slice_base);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  e = launch_fill_i32(d.col_ptr, ns * cp_pitch(d.dim), 0, s);
-  if (e != hipSuccess) return e;
   e = launch_fill_i32(d.heavy, kHeavyMax + 1, 0, s);
   if (e != hipSuccess) return e;
   e = launch_fill_i32(reinterpret_cast<int32_t *>(d.post + d.nnz), 2 * kPostPad, 0, s);
@@ -641,25 +604,29 @@ hipError_t launch_prepare_items(const ItemsDev &d, hipStream_t s) {
     e = launch_fill_i32(d.gdf, d.dim, 0, s);
     if (e != hipSuccess) return e;
   }
-  const unsigned item_blocks = (unsigned)((g.n_items * kLanesPerItem + 255) / 256);
-  hipLaunchKernelGGL(csc_count_kernel, dim3(item_blocks), dim3(256), 0, s, g, d.dim, d.indptr,
-                     d.indices, d.flags, d.col_ptr, d.ticket);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // radix passes: 8-bit digits of the largest column, at least one (the
+  // first pass also builds the payload); the last one writes the postings
+  int bits = 0;
+  while (bits < 31 && (d.dim - 1) >> bits > 0) ++bits;
+  const int passes = bits > 8 ? (bits + 7) / 8 : 1;
+  for (int p = 0; p < passes; ++p) {
+    int32_t *kd = ((passes - 1 - p) & 1) ? d.skey[1] : d.skey[0];
+    uint2 *pd = ((passes - 1 - p) & 1) ? d.spay : d.post;
+    const int32_t *ks = ((passes - p) & 1) ? d.skey[1] : d.skey[0];
+    const uint2 *ps = ((passes - p) & 1) ? d.spay : d.post;
+    if (p == 0)
+      hipLaunchKernelGGL(csc_sort_pass_kernel<true>, dim3((unsigned)ns), dim3(kSortNT), 0, s, g,
+                         d.flags, d.indptr, d.indices, d.values, d.norm64, d.slice_base, nullptr,
+                         nullptr, kd, pd, 0);
+    else
+      hipLaunchKernelGGL(csc_sort_pass_kernel<false>, dim3((unsigned)ns), dim3(kSortNT), 0, s, g,
+                         d.flags, d.indptr, d.indices, d.values, d.norm64, d.slice_base, ks, ps,
+                         kd, pd, 8 * p);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   const int32_t hmin = g.S / (2 * kHeavyFracInv) > 2 ? g.S / (2 * kHeavyFracInv) : 2;
-  hipLaunchKernelGGL(csc_scan_kernel<1024>, dim3((unsigned)ns), dim3(1024), 0, s, d.dim, d.flags,
-                     d.slice_base, d.col_ptr, d.mlist, d.mcount, d.dense ? d.gdf : nullptr, hmin);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(csc_scatter_kernel, dim3(item_blocks), dim3(256), 0, s, g, d.dim, d.indptr,
-                     d.indices, d.values, d.norm64, d.flags, d.col_ptr, d.slice_base, d.ticket,
-                     d.post, d.trow, d.tval);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  int64_t G = 2048 / ns;
-  if (G < 4) G = 4;
-  if (G > 256) G = 256;
-  const size_t lds = 2 * sizeof(uint32_t) * (size_t)((g.S + 31) / 32);
-  hipLaunchKernelGGL(csc_fixup_kernel<256>, dim3((unsigned)(G * ns)), dim3(256), lds, s, d.dim,
-                     g.S, (int32_t)G, d.flags, d.col_ptr, d.slice_base, d.mlist, d.mcount, d.trow,
-                     d.tval, d.post);
+  hipLaunchKernelGGL(csc_colptr_kernel, dim3((unsigned)ns), dim3(kCpNT), 0, s, d.dim, d.flags,
+                     d.slice_base, d.skey[0], d.col_ptr, d.dense ? d.gdf : nullptr, hmin);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (!d.dense) return hipSuccess;
   const int64_t tg64 = (g.n_items + kHeavyFracInv - 1) / kHeavyFracInv;

@@ -164,3 +164,28 @@ def test_threshold_arguments(env):
         sps.cosine_chunk_threshold(qq, it, it.num_chunks, 0.5, hits, count)
     with pytest.raises(sps.SpsError):
         sps.cosine_chunk_threshold(qq, it, 0, float("nan"), hits, count)
+
+
+def test_threshold_ragged_groups_and_dense_off(env, orc, monkeypatch):
+    """300 queries (the last 16-row group holds 12), 2048-item chunks (two slices
+    per chunk, partial row sums folded), the heavy-dim part on and off."""
+    torch, sps, dev = env
+    q, items, extra = synth.make_workload("edge", n_item=6000, n_query=300)
+    ref = orc.scores(q, items)
+    for dense_on in ("1", "0"):
+        monkeypatch.setenv("SPS_DENSE", dense_on)
+        it, qq = _prepared(env, q, items, 2048)
+        t = 0.2
+        _, _, need = _dense_and_hits(env, it, qq, q.n_rows, t, 0)
+        dense, hits, count = _dense_and_hits(env, it, qq, q.n_rows, t, need)
+        ek, evs = _as_sorted(*_expected(dense, 2048, t))
+        gr, gi, gv = sps.hits_to_numpy(hits, count)
+        gk, gvs = _as_sorted(gr, gi, gv)
+        assert count == need == len(ek) and np.array_equal(ek, gk)
+        assert np.array_equal(evs.view(np.uint32), gvs.view(np.uint32))
+        assert np.any(gr >= 288)  # the ragged group contributes
+        kept = np.zeros(ref.shape, dtype=bool)
+        kept[gr, gi] = True
+        assert np.all(kept[ref >= t + TOL]) and not np.any(kept[ref < t - TOL])
+        report("threshold %.2f edge 300x6000, chunk 2048, dense=%s: %d hits = dense >= t, "
+               "oracle-consistent" % (t, dense_on, count))
