@@ -364,90 +364,99 @@ __global__ __launch_bounds__(kSortNT) void csc_sort_pass_kernel(
 // col_ptr[d] of the slice = the number of its entries with column < d, for
 // d = 0 .. dim; a structural fault leaves every list empty. With gdf, every
 // column holding at least hmin entries of the slice adds its count to gdf[d].
+// A tile of kCpTile columns is four segments of 4 kCpNT; thread t owns the
+// 4 columns at 4 t of each segment, so LDS reads and global stores are
+// lane-contiguous 16 bytes.
 constexpr int kCpNT = 512;
-constexpr int kCpPer = 16;
-constexpr int kCpTile = kCpPer * kCpNT;
+constexpr int kCpTile = 16 * kCpNT;
 __global__ __launch_bounds__(kCpNT) void csc_colptr_kernel(
     int64_t dim, const int32_t *__restrict__ flags, const int32_t *__restrict__ slice_base,
     const int32_t *__restrict__ keys, int32_t *__restrict__ col_ptr, int32_t *__restrict__ gdf,
     int32_t hmin) {
+  constexpr int NW = kCpNT / 64;
   __shared__ int32_t s_h[kCpTile];
-  __shared__ int32_t s_ws[kCpNT / 64];
+  __shared__ int32_t s_ws[4][NW];
   const int64_t sl = blockIdx.x;
   const bool fault = flags[0] != 0;
   const int64_t b = fault ? 0 : slice_base[sl];
   const int64_t n = fault ? 0 : slice_base[sl + 1] - b;
   const int32_t *ks = keys + b;
   int32_t *cp = col_ptr + sl * cp_pitch(dim);
-  const int t = threadIdx.x;
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const int64_t ncp = dim + 1;
+  int4 *h4 = reinterpret_cast<int4 *>(s_h);
   int64_t p0 = 0;  // entries with a column below this tile
   // the first key chunk of the next tile is loaded before this tile's scan
   int32_t kc = t < n ? ks[t] : 0;
   for (int64_t D0 = 0; D0 < ncp; D0 += kCpTile) {
-    int4 *h4 = reinterpret_cast<int4 *>(s_h);
 #pragma unroll
-    for (int k = 0; k < kCpPer / 4; ++k) h4[k * kCpNT + t] = make_int4(0, 0, 0, 0);
+    for (int k = 0; k < 4; ++k) h4[k * kCpNT + t] = make_int4(0, 0, 0, 0);
     __syncthreads();
-    // the tile's keys are the next run of the sorted keys
+    // the tile's keys are the next run of the sorted keys; equal keys of a
+    // wave are added once, by the first lane of their run
     const int64_t Dend = D0 + kCpTile;
     int64_t q = p0;
     int32_t k = kc;
     for (;;) {
       const int64_t i = q + t;
       const bool in = i < n && k < Dend;
-      if (in && k >= D0) atomicAdd(&s_h[k - D0], 1);  // (sorted keys are >= D0 here)
+      const int32_t kprev = __shfl_up(k, 1, 64);
+      const bool start = in && (lane == 0 || kprev != k);
+      const uint64_t stop = __ballot(!in || lane == 0 || kprev != k);
+      if (start && k >= D0) {  // (sorted keys are >= D0 here)
+        const uint64_t above = stop & (lane == 63 ? 0ull : (~0ull << (lane + 1)));
+        const int next = above ? __ffsll((long long)above) - 1 : 64;
+        atomicAdd(&s_h[k - D0], next - lane);
+      }
       const int c = __syncthreads_count(in);
       q += c;
       k = q + t < n ? ks[q + t] : 0;
       if (c < kCpNT) break;
     }
     kc = k;
-    // thread t: columns D0 + 16 t .. + 15 (four 16-byte LDS reads)
-    int32_t v[kCpPer];
-    int32_t sum = 0;
+    // counts of this thread's four column groups, and their exclusive prefix
+    // in column order (segment-major), from one wave scan per segment
+    int4 v[4];
+    int32_t sg[4], incl[4];
 #pragma unroll
-    for (int k = 0; k < kCpPer / 4; ++k) {
-      const int4 x = h4[t * (kCpPer / 4) + k];
-      v[4 * k] = x.x;
-      v[4 * k + 1] = x.y;
-      v[4 * k + 2] = x.z;
-      v[4 * k + 3] = x.w;
-      sum += (x.x + x.y) + (x.z + x.w);
+    for (int s4 = 0; s4 < 4; ++s4) {
+      v[s4] = h4[s4 * kCpNT + t];
+      sg[s4] = (v[s4].x + v[s4].y) + (v[s4].z + v[s4].w);
+      incl[s4] = wave_incl_scan_dpp(sg[s4]);
+      if (lane == 63) s_ws[s4][wv] = incl[s4];
     }
-    int32_t tot;
-    const int32_t incl = block_incl_scan_1b<kCpNT>(sum, s_ws, &tot);
-    int32_t ex = (int32_t)p0 + incl - sum;
-    const int64_t j0 = D0 + (int64_t)kCpPer * t;
-    int32_t o[kCpPer];
-#pragma unroll
-    for (int k = 0; k < kCpPer; ++k) {
-      o[k] = ex;
-      ex += v[k];
-      if (gdf != nullptr && v[k] >= hmin && j0 + k < dim) atomicAdd(&gdf[j0 + k], v[k]);
-    }
-    // the tile's values back to LDS in column order (each thread overwrites
-    // only its own counts), then stored with consecutive lanes on
-    // consecutive 16 bytes
-#pragma unroll
-    for (int k = 0; k < kCpPer / 4; ++k)
-      h4[t * (kCpPer / 4) + k] = make_int4(o[4 * k], o[4 * k + 1], o[4 * k + 2], o[4 * k + 3]);
     __syncthreads();
+    int32_t base = (int32_t)p0;
 #pragma unroll
-    for (int k = 0; k < kCpPer / 4; ++k) {
-      const int64_t j = D0 + 4 * ((int64_t)k * kCpNT + t);
-      const int4 x = h4[k * kCpNT + t];
+    for (int s4 = 0; s4 < 4; ++s4) {
+      int32_t before = 0, total = 0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const int32_t x = s_ws[s4][w];
+        before += w < wv ? x : 0;
+        total += x;
+      }
+      int32_t ex = base + before + incl[s4] - sg[s4];
+      const int64_t j = D0 + 4 * ((int64_t)s4 * kCpNT + t);
+      const int32_t vs[4] = {v[s4].x, v[s4].y, v[s4].z, v[s4].w};
+      int32_t o[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        o[u] = ex;
+        ex += vs[u];
+        if (gdf != nullptr && vs[u] >= hmin && j + u < dim) atomicAdd(&gdf[j + u], vs[u]);
+      }
       if (j + 3 < ncp) {
-        reinterpret_cast<int4 *>(cp)[j >> 2] = x;
+        reinterpret_cast<int4 *>(cp)[j >> 2] = make_int4(o[0], o[1], o[2], o[3]);
       } else {
-        const int32_t xs[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
         for (int u = 0; u < 4; ++u)
-          if (j + u < ncp) cp[j + u] = xs[u];
+          if (j + u < ncp) cp[j + u] = o[u];
       }
+      base += total;
     }
     p0 = q;
-    __syncthreads();  // the tile is read before the next tile clears it
+    __syncthreads();  // the histogram and the wave totals are read before the next tile
   }
 }
 
