@@ -209,6 +209,17 @@ def main():
 
     # checksum sanity on the last step: row sums finite
     assert torch.isfinite(sums).all().item()
+
+    # a write-only ceiling for the same bytes: the output buffer zero-filled
+    # (torch's fill kernel), timed with events on the same stream
+    w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    out.zero_()
+    w0.record(stream)
+    for _ in range(5):
+        out.zero_()
+    w1.record(stream)
+    torch.cuda.synchronize()
+    write_ceiling = 5 * 4.0 * out.numel() / (w0.elapsed_time(w1) * 1e-3) / 1e9
     log("step %.2f ms: prepare %.2f ms, %d score launches %.2f ms (avg %.3f ms)" %
         (ms_per_step, prep_ms, n_chunks, loop_ms, avg_launch_ms))
 
@@ -368,6 +379,8 @@ def main():
         "breakdown_ms": {"prepare": prep_ms, "score_loop": loop_ms,
                          "score_launch_avg": avg_launch_ms},
         "step_hbm_gbps_algorithmic": float(alg_bytes.sum()) / (ms_per_step * 1e-3) / 1e9,
+        "write_ceiling_gbps": write_ceiling,
+        "frac_of_write_ceiling": achieved / write_ceiling,
         "variants": {"fp16": half, "threshold": thr, "host_stream": host, "bsc": bscv},
     }
     print(json.dumps(res), flush=True)
