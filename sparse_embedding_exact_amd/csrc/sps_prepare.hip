@@ -12,8 +12,8 @@
 //
 // All kernels are wave64. Device-side guards keep every access inside the
 // buffers the host sized, whatever the CSR contents: the prepare calls run
-// csr_check_kernel first and every later kernel exits when it found a
-// structural fault.
+// csr_check_kernel first, and every later kernel exits when it found a
+// structural fault (the col_ptr builder then writes empty lists).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -227,21 +227,10 @@ hipError_t launch_row_norms(int64_t n_rows, int64_t nnz, const int32_t *indptr,
 // Per-slice inverted lists. Chunk c holds items [c*C, min((c+1)*C, n))
 // (§4.4 slicing); it is cut into n_sub slices of S items (Geom). A slice's
 // entries are indptr[first item] .. indptr[last item + 1], and its inverted
-// lists occupy that same entry range of row[] / val[], with item ids local to
-// the slice.
-//
-//  1. count   : tickets t = atomicAdd(&cnt[s][d], 1) (arbitrary order)
-//  2. scan    : col_ptr[s] = exclusive prefix of cnt[s]; list of dims whose
-//               list holds >= 2 entries (compacted, ascending)
-//  3. scatter : entry -> position col_ptr[s][d] + t; single-entry lists are
-//               final, longer lists go to a temporary area
-//  4. fixup   : each longer list is put in ascending item order. Item ids
-//               are distinct inside one list, so the rank of an entry is the
-//               number of smaller ids: a wave compares ids directly for
-//               lists up to 64 entries, a workgroup counts bits of an item
-//               bitmap (prefix popcounts) for longer ones.
-// The result is the unique CSC with ascending item ids per dim, independent
-// of the order the atomics were served in.
+// lists occupy that same entry range of the posting array, with item ids
+// local to the slice, ascending within each column: the unique CSC of the
+// slice (the kernels below build it with a stable sort, so no order of
+// concurrent work can change it).
 // ---------------------------------------------------------------------------
 
 __global__ void slice_base_kernel(Geom g, int64_t nnz, const int32_t *__restrict__ indptr,
