@@ -8,7 +8,8 @@
 //   row_norm_kernel      §5.2 detail one: L2 norm from the stored nonzeros
 //   csc_* kernels        per-slice inverted lists; chunk slicing as in §4.4
 //   heavy_* / slab_*     dense rows of the few dims most items hold
-//   light_* kernels      query rows split into heavy values and the rest
+//   light_* kernels      query rows split into heavy values and the rest,
+//                        each row group's light records sorted by dim
 //
 // All kernels are wave64. Device-side guards keep every access inside the
 // buffers the host sized, whatever the CSR contents: the prepare calls run
@@ -726,6 +727,65 @@ __global__ __launch_bounds__(256) void light_split_kernel(
   if (!FILL) lptr[q + 1] = count;
 }
 
+// Each 16-row group's light records sorted by dim, so that the rows of a
+// group that share a dim walk the same posting list in adjacent segments
+// (one L1 request serves them). The score kernel's sums do not depend on the
+// order of the records; a group of more than kLightSortCap records keeps the
+// row order.
+constexpr int kLightSortNT = 512;
+constexpr int kLightSortCap = 2 * kLightSortNT;
+__global__ __launch_bounds__(kLightSortNT) void light_sort_kernel(int64_t n_rows,
+                                                                  const int32_t *__restrict__ lptr,
+                                                                  uint3 *__restrict__ lrec) {
+  __shared__ uint32_t s_key[kLightSortCap];
+  __shared__ uint16_t s_idx[kLightSortCap];
+  const int64_t g = blockIdx.x;
+  const int64_t r1 = (g + 1) * kRows < n_rows ? (g + 1) * kRows : n_rows;
+  const int64_t b = lptr[g * kRows], e = lptr[r1];
+  const int64_t n = e - b;
+  if (n <= 1 || n > kLightSortCap) return;  // uniform per workgroup
+  int P = 2;
+  while (P < n) P <<= 1;
+  const int t = threadIdx.x;
+  for (int i = t; i < P; i += kLightSortNT) {
+    s_key[i] = i < n ? lrec[b + i].x : 0xFFFFFFFFu;
+    s_idx[i] = (uint16_t)i;
+  }
+  __syncthreads();
+  for (int k = 2; k <= P; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = t; i < P; i += kLightSortNT) {
+        const int l = i ^ j;
+        if (l > i) {
+          const uint32_t ki = s_key[i], kl = s_key[l];
+          const bool up = (i & k) == 0;
+          if (up ? (ki > kl) : (ki < kl)) {
+            s_key[i] = kl;
+            s_key[l] = ki;
+            const uint16_t x = s_idx[i];
+            s_idx[i] = s_idx[l];
+            s_idx[l] = x;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  // every record is read before any is written back
+  uint3 r[kLightSortCap / kLightSortNT];
+#pragma unroll
+  for (int m = 0; m < kLightSortCap / kLightSortNT; ++m) {
+    const int i = t + m * kLightSortNT;
+    if (i < n) r[m] = lrec[b + s_idx[i]];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int m = 0; m < kLightSortCap / kLightSortNT; ++m) {
+    const int i = t + m * kLightSortNT;
+    if (i < n) lrec[b + i] = r[m];
+  }
+}
+
 hipError_t launch_prepare_queries(const QueriesDev &d, hipStream_t s) {
   hipError_t e;
   e = launch_csr_check(d.n_rows, d.dim, d.nnz, d.indptr, d.indices, d.values, 0, d.flags, s);
@@ -752,6 +812,9 @@ hipError_t launch_prepare_queries(const QueriesDev &d, hipStream_t s) {
   hipLaunchKernelGGL(light_split_kernel<true>, dim3(blocks), dim3(256), 0, s, d.n_rows,
                      d.indptr, d.indices, d.values, d.norm64, d.flags, heavy, d.lptr, d.lrec,
                      d.qh);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(light_sort_kernel, dim3((unsigned)d.n_groups), dim3(kLightSortNT), 0, s,
+                     d.n_rows, d.lptr, d.lrec);
   return hipGetLastError();
 }
 
