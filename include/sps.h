@@ -172,8 +172,10 @@ sps_status sps_queries_workspace_size(const sps_items *items, int64_t n_rows, in
 /* Prepare a query batch for the prepared items `items` (asynchronous):
  * inverse norms as for items (§5.2); every row normalised by its float64
  * norm and rounded once to fp32, fl32(q_d / ||q||); values on the items'
- * heavy dims gathered into dense blocks of 16 rows, the rest kept as a CSR of
- * "light" entries. The query CSR may be released once this stream work has
+ * heavy dims gathered into dense blocks of 16 rows, the rest kept as "light"
+ * records (dim, value, row) per group of 16 rows, sorted by dim within the
+ * group (so that rows sharing a dim walk its posting list close together).
+ * The query CSR may be released once this stream work has
  * completed. The batch can only be scored against `items`. Free the handle
  * with sps_queries_destroy. */
 sps_status sps_prepare_queries(const sps_csr *queries, const sps_items *items,
