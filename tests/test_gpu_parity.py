@@ -264,6 +264,26 @@ def test_bitwise_reproducible(env):
     assert all(np.array_equal(runs[0].view(np.uint32), r.view(np.uint32)) for r in runs[1:])
 
 
+def test_row_permutation_invariance(env):
+    """A query's scores do not depend on the rows it is grouped with: the light
+    sums are integers in any order (the query prepare sorts each 16-row group's
+    records by dim) and the heavy part is per row. The batch scored in a
+    shuffled row order, then unshuffled, is bitwise equal to the original."""
+    torch, sps, dev = env
+    from synth import HostCSR
+    q, items, _ = synth.make_workload("mid", n_item=12000, n_query=203)
+    perm = np.random.default_rng(17).permutation(q.n_rows)
+    cnt = np.diff(q.indptr)[perm]
+    ip = np.concatenate([[0], np.cumsum(cnt)]).astype(np.int32)
+    ix = np.concatenate([q.indices[q.indptr[r]:q.indptr[r + 1]] for r in perm])
+    vx = np.concatenate([q.values[q.indptr[r]:q.indptr[r + 1]] for r in perm])
+    qp = HostCSR(ip, ix.astype(np.int32), vx.astype(np.float32), q.n_rows, q.n_cols)
+    a = np.concatenate([g for _, _, g, _ in gpu_chunks(env, q, items, 8192)], axis=1)
+    b = np.concatenate([g for _, _, g, _ in gpu_chunks(env, qp, items, 8192)], axis=1)
+    assert np.array_equal(a[perm].view(np.uint32), b.view(np.uint32))
+    report("mid 203x12000 rows shuffled: bitwise equal", 0.0, a.size)
+
+
 def test_edge_rows_and_ld(env, orc):
     """Empty rows on both sides, explicit zeros, a dim no item has, a chunk
     length that is not a multiple of 4, ld > chunk_len (the tail untouched)."""
