@@ -432,11 +432,15 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void sc
     if (MODE == kOutThreshold) {
       // ---- epilogue: the group's scores >= threshold as hits ----
       // Wave w counts rows w, w + NW, ... (and sums all their scores for the
-      // row sums); one atomic per group reserves the group's range of the
-      // hit buffer, laid out wave by wave, row by row, lane by lane; then
-      // each wave re-reads its rows from LDS and writes its hits.
+      // row sums); each lane marks which of its (at most 16) scores of a row
+      // are hits in a bit mask. One atomic per group reserves the group's
+      // range of the hit buffer, laid out wave by wave, row by row, lane by
+      // lane; then each lane writes its marked hits, reading only their
+      // accumulators back.
       constexpr int RW = kRows / NW;
+      static_assert(kSliceMax / 64 <= 32, "a lane's scores of a row fit a 32-bit mask");
       int cnt[RW], incl[RW], tot[RW];
+      uint32_t hmask[RW];
       int wtot = 0;
 #pragma unroll
       for (int rr = 0; rr < RW; ++rr) {
@@ -444,8 +448,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void sc
         const int64_t q = q0 + r;
         const int4 *arow = reinterpret_cast<const int4 *>(acc + r * Lp);
         double rs = 0.0;
-        int c = 0;
+        uint32_t m = 0;
         if (q < a.n_q) {
+          // score j0 + u of the lane is bit 4 step + u (j0 = 4 lane + 256 step)
           for (int j0 = 4 * lane; j0 < slen; j0 += 256) {
             const int4 x = arow[j0 >> 2];
             const int xs[4] = {x.x, x.y, x.z, x.w};
@@ -453,11 +458,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void sc
             for (int u = 0; u < 4; ++u)
               if (j0 + u < slen) {
                 const float v = (float)xs[u] * kFixInv;
-                c += v >= a.threshold ? 1 : 0;
+                m |= (v >= a.threshold ? 1u : 0u) << (4 * (j0 >> 8) + u);
                 rs += (double)v;
               }
           }
         }
+        hmask[rr] = m;
+        const int c = __builtin_popcount(m);
         cnt[rr] = c;
         incl[rr] = wave_incl_scan_dpp(c);
         tot[rr] = __builtin_amdgcn_readlane(incl[rr], 63);
@@ -482,21 +489,16 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void sc
       for (int rr = 0; rr < RW; ++rr) {
         if (tot[rr] > 0) {
           const int r = wv + NW * rr;
-          const int64_t q = q0 + r;
-          const int4 *arow = reinterpret_cast<const int4 *>(acc + r * Lp);
+          const int32_t q = (int32_t)(q0 + r);
           unsigned long long k = k0 + (unsigned long long)(incl[rr] - cnt[rr]);
-          for (int j0 = 4 * lane; j0 < slen; j0 += 256) {
-            const int4 x = arow[j0 >> 2];
-            const int xs[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-              const float v = (float)xs[u] * kFixInv;
-              if (j0 + u < slen && v >= a.threshold) {
-                if (k < (unsigned long long)a.hit_cap)
-                  a.hits[k] = make_int3((int32_t)q, (int32_t)(ib + j0 + u), __float_as_int(v));
-                ++k;
-              }
-            }
+          // the marked scores in increasing item order
+          for (uint32_t m = hmask[rr]; m != 0u; m &= m - 1u) {
+            const int b = __builtin_ctz(m);
+            const int j = 4 * lane + 256 * (b >> 2) + (b & 3);
+            const float v = (float)acc[r * Lp + j] * kFixInv;
+            if (k < (unsigned long long)a.hit_cap)
+              a.hits[k] = make_int3(q, (int32_t)(ib + j), __float_as_int(v));
+            ++k;
           }
           k0 += (unsigned long long)tot[rr];
         }
