@@ -183,3 +183,47 @@ def test_malformed_and_errors(env):
                                  b.blocks.numel(), b.offsets.data_ptr(), b.offsets.numel() - 4,
                                  None)
     assert ok == -4
+
+
+def _rows_of_lengths(seed, lengths, n_cols):
+    """A canonical CSR whose rows have the given lengths (sorted distinct columns)."""
+    rng = np.random.default_rng(seed)
+    rows = [np.sort(rng.choice(n_cols, int(n), replace=False)) for n in lengths]
+    indptr = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    idx = np.concatenate(rows) if rows else np.zeros(0, np.int64)
+    return indptr, idx.astype(np.int32)
+
+
+def test_decode_paths_and_alignment(env):
+    """The decoder takes a wave's rows one per lane with the indices gathered in LDS when the
+    wave's rows are all short (at most 256 entries) and span at most 3072 entries; one per
+    lane with direct stores when they span more; and rows of more than 256 entries with the
+    whole wave. Each path, on varint and offset buffers that start 0 to 3 bytes past a
+    4-byte boundary (the decoder reads whole aligned words only inside the buffers)."""
+    torch, sps, dev = env
+    n_cols = 1024 * 1000
+    cases = {
+        # every wave staged: 64 rows x 40 entries = 2560 per wave
+        "staged": [40] * 640,
+        # one lane per row, direct stores: 64 x 60 = 3840 entries per wave
+        "direct": [60] * 200,
+        # lengths about the 256-entry boundary: waves with rows for the whole wave
+        "mixed": [0, 1, 5, 43, 100, 255, 256, 257, 300, 3, 2] * 30,
+    }
+    for name, lengths in cases.items():
+        indptr, idx = _rows_of_lengths(11, lengths, n_cols)
+        m = _M(indptr, idx, n_cols)
+        b, bp, bl, of = _gpu_encode(env, m)
+        for shift in (0, 1, 2, 3):
+            # the same bytes at a buffer position that is `shift` past a word boundary
+            big_b = torch.zeros(bl.size + 8, dtype=torch.uint8, device=dev)
+            big_o = torch.zeros(of.size + 8, dtype=torch.uint8, device=dev)
+            big_b[shift:shift + bl.size] = b.blocks
+            big_o[shift:shift + of.size] = b.offsets
+            sb = big_b[shift:shift + bl.size]
+            so = big_o[shift:shift + of.size]
+            assert sb.data_ptr() % 4 == shift % 4 or big_b.data_ptr() % 4 != 0
+            dec = sps.bsc_decode(sps.BSC(b.indptr, b.bptr, sb, so, b.values, b.n_rows, b.n_cols))
+            assert np.array_equal(dec.indices.cpu().numpy(), idx), (name, shift)
+    report("bsc decode paths: staged (64 x 40), direct (64 x 60), rows 0..300 entries about the "
+           "256 boundary; buffers at byte offsets 0..3: exact")
