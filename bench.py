@@ -105,9 +105,9 @@ def measured_traffic(path, workload):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(item chunks would be sharded across GPUs with no collective in the hot "
-              "loop; see the design notes). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path (item chunks "
+              "would be sharded across GPUs, each scoring its own chunks with no collective "
+              "in the hot loop). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
