@@ -378,10 +378,15 @@ __global__ __launch_bounds__(kCpNT) void csc_colptr_kernel(
   int64_t p0 = 0;  // entries with a column below this tile
   // the first key chunk of the next tile is loaded before this tile's scan
   int32_t kc = t < n ? ks[t] : 0;
-  for (int64_t D0 = 0; D0 < ncp; D0 += kCpTile) {
+  // Two barriers per tile: the histogram slots a thread reads after counting
+  // it clears at once, before the barrier that precedes its stores, so the
+  // next tile's counts (after that barrier) start from zero; and the next
+  // tile's counting loop passes at least one barrier before the wave totals
+  // of this tile are overwritten.
 #pragma unroll
-    for (int k = 0; k < 4; ++k) h4[k * kCpNT + t] = make_int4(0, 0, 0, 0);
-    __syncthreads();
+  for (int k = 0; k < 4; ++k) h4[k * kCpNT + t] = make_int4(0, 0, 0, 0);
+  __syncthreads();
+  for (int64_t D0 = 0; D0 < ncp; D0 += kCpTile) {
     // the tile's keys are the next run of the sorted keys; equal keys of a
     // wave are added once, by the first lane of their run
     const int64_t Dend = D0 + kCpTile;
@@ -411,6 +416,7 @@ __global__ __launch_bounds__(kCpNT) void csc_colptr_kernel(
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4) {
       v[s4] = h4[s4 * kCpNT + t];
+      h4[s4 * kCpNT + t] = make_int4(0, 0, 0, 0);
       sg[s4] = (v[s4].x + v[s4].y) + (v[s4].z + v[s4].w);
       incl[s4] = wave_incl_scan_dpp(sg[s4]);
       if (lane == 63) s_ws[s4][wv] = incl[s4];
@@ -446,7 +452,6 @@ __global__ __launch_bounds__(kCpNT) void csc_colptr_kernel(
       base += total;
     }
     p0 = q;
-    __syncthreads();  // the histogram and the wave totals are read before the next tile
   }
 }
 
