@@ -97,8 +97,8 @@ __global__ __launch_bounds__(256) void bsc_pack_offsets_kernel(int64_t nnz,
 // one row: a row of the pages corpus holds about 43 entries in about 100
 // bytes, so a row per lane keeps every lane busy with no cross-lane step, and
 // the thread reads its row's bytes through two 64-bit register windows (the
-// varint bytes and the offset bits), each refilled by one aligned 32-bit
-// load issued a refill ahead. Its indices are stored four at a time. Rows of
+// varint bytes and the offset bits), each refilled word by word from a
+// WordStream of 16-byte loads. Its indices are stored four at a time. Rows of
 // more than kThreadRowMax entries are decoded by the whole wave instead
 // (decode_row_wave), so that one long row does not hold up a lane for its
 // length.
@@ -117,6 +117,45 @@ __device__ __forceinline__ uint32_t ld_word(const uint8_t *__restrict__ buf, int
   return w;
 }
 
+// The little-endian words of buf[0 .. n) from a 4-byte aligned position on,
+// read 16 bytes at a time with the next 16 loaded ahead: a thread that walks
+// its row's bytes word by word then sends one request to the L1 per four
+// words (the L1 cannot hold the lines of every lane of every wave, so each
+// request tends to go on to the L2).
+struct WordStream {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+  const uint8_t *buf;
+  int64_t n;
+  int64_t next;  // position of the next 16-byte load
+  u32x4 q, qn;   // the current 16 bytes and the next
+  int qi;        // words of q already taken
+  __device__ __forceinline__ u32x4 ld16(int64_t a) const {
+    if (a >= 0 && a + 16 <= n) return *reinterpret_cast<const u32x4_a4 *>(buf + a);
+    const u32x4 w = {ld_word(buf, n, a), ld_word(buf, n, a + 4), ld_word(buf, n, a + 8),
+                     ld_word(buf, n, a + 12)};
+    return w;
+  }
+  __device__ __forceinline__ void init(const uint8_t *b, int64_t size, int64_t a) {
+    buf = b;
+    n = size;
+    q = ld16(a);
+    qn = ld16(a + 16);
+    next = a + 32;
+    qi = 0;
+  }
+  __device__ __forceinline__ uint32_t word() {
+    const uint32_t w = qi == 0 ? q.x : (qi == 1 ? q.y : (qi == 2 ? q.z : q.w));
+    if (++qi == 4) {
+      q = qn;
+      qn = ld16(next);
+      next += 16;
+      qi = 0;
+    }
+    return w;
+  }
+};
+
 // Row entries [e0, e1) from its varint bytes [p0, p1), by one thread; entry
 // e goes to out[e - base]. Returns true when the bytes do not hold exactly the row's entries, or a
 // value takes more than 3 bytes (the indices are then unspecified).
@@ -126,23 +165,25 @@ __device__ __forceinline__ bool decode_row_thread(int64_t e0, int64_t e1, int64_
                                                   const uint8_t *__restrict__ offsets,
                                                   int64_t n_off, int32_t *__restrict__ out,
                                                   int64_t base) {
-  // varint bytes: bw holds the words at ba and ba + 4, bn the word at ba + 8;
-  // the next byte is byte bo (0..3) of bw
+  // varint bytes: bw holds the next two words of the row's word stream (from
+  // the word at ba on); the next byte is byte bo (0..3) of bw
   const int64_t mb = (int64_t)(reinterpret_cast<uintptr_t>(blocks) & 3u);
-  int64_t ba = ((p0 + mb) & ~(int64_t)3) - mb;
-  uint64_t bw = (uint64_t)ld_word(blocks, n_bytes, ba) |
-                ((uint64_t)ld_word(blocks, n_bytes, ba + 4) << 32);
-  uint32_t bn = ld_word(blocks, n_bytes, ba + 8);
+  const int64_t ba = ((p0 + mb) & ~(int64_t)3) - mb;
+  WordStream bs;
+  bs.init(blocks, n_bytes, ba);
+  uint64_t bw = (uint64_t)bs.word();
+  bw |= (uint64_t)bs.word() << 32;
   int32_t bo = (int32_t)(p0 - ba);
   int64_t left = p1 - p0;  // the row's bytes not yet taken
-  // offset bits: ow holds the words at oa and oa + 4, on the word at oa + 8;
-  // the next offset starts at bit ob (0..31) of ow
+  // offset bits: ow holds the next two words of the offsets' word stream
+  // (from the word at oa on); the next offset starts at bit ob (0..31) of ow
   const int64_t mo = (int64_t)(reinterpret_cast<uintptr_t>(offsets) & 3u);
   const int64_t bit0 = 10 * e0;
-  int64_t oa = (((bit0 >> 3) + mo) & ~(int64_t)3) - mo;
-  uint64_t ow = (uint64_t)ld_word(offsets, n_off, oa) |
-                ((uint64_t)ld_word(offsets, n_off, oa + 4) << 32);
-  uint32_t on = ld_word(offsets, n_off, oa + 8);
+  const int64_t oa = (((bit0 >> 3) + mo) & ~(int64_t)3) - mo;
+  WordStream os;
+  os.init(offsets, n_off, oa);
+  uint64_t ow = (uint64_t)os.word();
+  ow |= (uint64_t)os.word() << 32;
   int32_t ob = (int32_t)(bit0 - 8 * oa);
   uint32_t blk = 0;
   bool bad = false;
@@ -161,19 +202,15 @@ __device__ __forceinline__ bool decode_row_thread(int64_t e0, int64_t e1, int64_
     left -= len;
     bo += len;
     if (bo >= 4) {  // bo was <= 3, so one word of the window is used up
-      bw = (bw >> 32) | ((uint64_t)bn << 32);
-      ba += 4;
+      bw = (bw >> 32) | ((uint64_t)bs.word() << 32);
       bo -= 4;
-      bn = ld_word(blocks, n_bytes, ba + 8);
     }
     blk += v;
     const uint32_t off = (uint32_t)(ow >> ob) & 1023u;
     ob += 10;
     if (ob >= 32) {
-      ow = (ow >> 32) | ((uint64_t)on << 32);
-      oa += 4;
+      ow = (ow >> 32) | ((uint64_t)os.word() << 32);
       ob -= 32;
-      on = ld_word(offsets, n_off, oa + 8);
     }
     return (int32_t)(blk * 1024u + off);
   };
