@@ -11,10 +11,12 @@
 // offsets are packed in entry order over the whole matrix, least significant
 // bit first (entry k at bits 10k .. 10k + 9). indptr and values are the CSR's.
 //
-// All kernels are wave64 with one wave per row: the lanes of a wave take 64
-// consecutive entries (encode) or bytes (decode) of the row at a time, so
-// every load and store of a row is contiguous. Every access is bounded by
-// the buffer sizes the host passes, whatever the contents.
+// The encoder runs one wave per row: the lanes take 64 consecutive entries
+// of the row at a time, so every load and store of a row is contiguous. The
+// decoder runs one thread per row (a wave per row for rows of more than 256
+// entries) and gathers a wave's indices in LDS to store them contiguously.
+// Every access is bounded by the buffer sizes the host passes, whatever the
+// contents.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
