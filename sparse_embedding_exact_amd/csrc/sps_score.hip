@@ -48,6 +48,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "sps_device.h"
 #include "sps_internal.h"
 
@@ -589,13 +591,24 @@ static hipError_t launch_t(const ScoreArgs &a, hipStream_t s) {
   constexpr bool HALF = MODE == kOutHalf;
   const size_t dyn = (size_t)kRows * acc_pitch(a.g.S) * sizeof(int);
   auto kern = score_kernel<DENSE, MODE>;
-  // dynamic LDS above 64 KiB needs an explicit opt-in per kernel
-  static size_t opted = 65536;
-  if (dyn > opted) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
+  // dynamic LDS above 64 KiB needs an explicit opt-in per kernel, made once
+  // per device (and again if a later corpus needs more); callers on several
+  // threads may race to make it, which is harmless
+  constexpr int kMaxDevices = 64;
+  static std::atomic<size_t> opted[kMaxDevices];
+  if (dyn > 65536) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
-    opted = dyn;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    size_t cur = opted[dev].load(std::memory_order_relaxed);
+    if (dyn > cur) {
+      e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
+      if (e != hipSuccess) return e;
+      while (cur < dyn && !opted[dev].compare_exchange_weak(cur, dyn, std::memory_order_relaxed)) {
+      }
+    }
   }
   // wide stores need the row pitch and base aligned: 16 bytes (fp32), 8 (fp16)
   const uintptr_t base = HALF ? reinterpret_cast<uintptr_t>(a.out16)
