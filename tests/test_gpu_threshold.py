@@ -118,6 +118,16 @@ def test_threshold_keep_all_and_overflow(env):
     ek, evs = _as_sorted(*_expected(dense, 1000, -2.0))
     gk, gvs = _as_sorted(*sps.hits_to_numpy(hits, count))
     assert np.array_equal(ek, gk) and np.array_equal(evs.view(np.uint32), gvs.view(np.uint32))
+    # slices whose length is not a multiple of 4 (1001; 1024 and 1023): a lane's last group of
+    # four scores is partial, and every score of it must still be kept
+    for chunk in (1001, 2047):
+        it2, qq2 = _prepared(env, q, items, chunk)
+        dense, hits, count = _dense_and_hits(env, it2, qq2, q.n_rows, -2.0,
+                                             q.n_rows * items.n_rows)
+        assert count == q.n_rows * items.n_rows, chunk
+        ek, evs = _as_sorted(*_expected(dense, chunk, -2.0))
+        gk, gvs = _as_sorted(*sps.hits_to_numpy(hits, count))
+        assert np.array_equal(ek, gk) and np.array_equal(evs.view(np.uint32), gvs.view(np.uint32))
     # capacity smaller than the hits: all counted, the first `capacity` written and valid
     t = 0.1
     dense, hits, count = _dense_and_hits(env, it, qq, q.n_rows, t, 0)
@@ -131,8 +141,8 @@ def test_threshold_keep_all_and_overflow(env):
     d = np.concatenate([dense[c] for c in sorted(dense)], axis=1)
     assert np.array_equal(d[gr, gi].view(np.uint32), gv.view(np.uint32)) and np.all(gv >= t)
     assert len(set(zip(gr.tolist(), gi.tolist()))) == cap
-    report("threshold tiny: keep-all (%d hits) and capacity %d of %d" % (q.n_rows * items.n_rows,
-                                                                         cap, full))
+    report("threshold tiny: keep-all (%d hits; slices of 1000, 1001, 1024 + 1023 items) and "
+           "capacity %d of %d" % (q.n_rows * items.n_rows, cap, full))
 
 
 def test_threshold_pages_full_size(env):
