@@ -103,11 +103,14 @@ sps_status sps_items_workspace_size(int64_t n_items, int64_t dim, int64_t nnz,
  *     ceil(chunk_size / 1024) slices of slice_size = ceil(chunk_size /
  *     slices_per_chunk) items (the last slice of a chunk may be shorter): a
  *     slice is what one workgroup accumulates on chip;
- *  3. per slice, the inverted lists: col_ptr[dim+1] (slice-relative offsets,
- *     col_ptr[0] = 0, col_ptr[dim] = slice nnz), and for every entry an
- *     sps_posting: the slice-local item id and the value fl32(v / ||item||)
- *     rounded once from float64 (0 if the item norm is 0). Item ids ascend
- *     within each dim;
+ *  3. per slice, the inverted lists (the CSC of the slice's items): for every
+ *     entry an sps_posting, the slice-local item id and the value
+ *     fl32(v / ||item||) rounded once from float64 (0 if the item norm is 0),
+ *     grouped by dim in ascending dim order, item ids ascending within each
+ *     dim. The lists are located through a per-slice hash index of the dims
+ *     the slice holds (dim -> first posting, length), about 32 bytes per
+ *     distinct dim, instead of a col_ptr[dim+1] per slice; the canonical
+ *     col_ptr can be expanded from it (sps_items_slice_col_ptr);
  *  4. when slices hold at least 512 items: the "heavy" dims (at most 32, the
  *     most frequent among those held by at least 1/16 of the items) and, per
  *     slice, their values as dense rows (0 where an item lacks the dim). This
@@ -136,20 +139,31 @@ typedef struct {
 
 /* Device views of one prepared slice (for parity tests and tooling).
  * SYNCHRONOUS: reads the slice's entry range back from the device after
- * synchronising `stream`. col_ptr: DEVICE int32[dim+1]; post: DEVICE
- * sps_posting[slice_nnz]; item_inv_norm: DEVICE float[slice_len] (the
- * slice's first item onwards). */
+ * synchronising `stream`. post: DEVICE sps_posting[slice_nnz] (the lists in
+ * ascending dim order); item_inv_norm: DEVICE float[slice_len] (the slice's
+ * first item onwards). */
 typedef struct {
   int64_t item_begin;
   int32_t slice_len;
   int32_t slice_nnz;
-  const int32_t *col_ptr;
   const sps_posting *post;
   const float *item_inv_norm;
 } sps_slice_view;
 
 sps_status sps_items_slice_view(const sps_items *h, int64_t slice, void *stream,
                                 sps_slice_view *view);
+
+/* The slice's canonical CSC column pointer, expanded from its dim index
+ * (asynchronous): col_ptr[d] = the number of the slice's entries with a
+ * column below d, d = 0..dim (col_ptr[0] = 0, col_ptr[dim] = slice nnz),
+ * the layout of a CSC's column pointer (§4.4 slicing; for verification and
+ * tools, not used by scoring). col_ptr: DEVICE int32[dim+1], caller-owned.
+ * status (nullable): DEVICE int32, zeroed by the caller; bit 1 is set if a
+ * list's length in the index disagrees with the next list's start (an
+ * inconsistent index). Errors: SPS_ERR_INVALID_ARGUMENT (NULL),
+ * SPS_ERR_CHUNK_RANGE (slice out of range). */
+sps_status sps_items_slice_col_ptr(const sps_items *h, int64_t slice, int32_t *col_ptr,
+                                   int32_t *status, void *stream);
 
 /* The heavy dims chosen by sps_prepare, ascending (SYNCHRONOUS). Writes at
  * most `capacity` dims to `dims` (nullable) and their number to *count

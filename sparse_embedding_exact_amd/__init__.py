@@ -59,8 +59,7 @@ class _Bsc(ctypes.Structure):
 
 class _SliceView(ctypes.Structure):
     _fields_ = [("item_begin", ctypes.c_int64), ("slice_len", ctypes.c_int32),
-                ("slice_nnz", ctypes.c_int32), ("col_ptr", ctypes.c_void_p),
-                ("post", ctypes.c_void_p),
+                ("slice_nnz", ctypes.c_int32), ("post", ctypes.c_void_p),
                 ("item_inv_norm", ctypes.c_void_p)]
 
 
@@ -80,6 +79,7 @@ SIGNATURES = {
     "sps_items_slices": (_I32, [_P, ctypes.POINTER(_I32), ctypes.POINTER(_I32),
                                 ctypes.POINTER(_I64)]),
     "sps_items_slice_view": (_I32, [_P, _I64, _P, ctypes.POINTER(_SliceView)]),
+    "sps_items_slice_col_ptr": (_I32, [_P, _I64, _P, _P, _P]),
     "sps_items_heavy_dims": (_I32, [_P, _P, _P, _I32, ctypes.POINTER(_I32)]),
     "sps_items_destroy": (None, [_P]),
     "sps_queries_workspace_size": (_I32, [_P, _I64, _I64, _I64, ctypes.POINTER(_SZ)]),
@@ -307,11 +307,21 @@ class Items:
 
         return {
             "item_begin": v.item_begin, "slice_len": v.slice_len, "slice_nnz": v.slice_nnz,
-            "col_ptr": view(v.col_ptr, self.dim + 1, torch.int32, 4),
             # sps_posting records: int32 pairs (item id, value bits)
             "post": view(v.post, v.slice_nnz, torch.int32, 8).view(-1, 2),
             "item_inv_norm": view(v.item_inv_norm, v.slice_len, torch.float32, 4),
         }
+
+    def slice_col_ptr(self, s: int, stream=None):
+        """(col_ptr int32[dim+1], consistent: bool) of slice s, expanded from its dim index
+        on the device (synchronous)."""
+        dev = self._persistent.device
+        cp = torch.empty(self.dim + 1, dtype=torch.int32, device=dev)
+        st = torch.zeros(1, dtype=torch.int32, device=dev)
+        _check(_lib.sps_items_slice_col_ptr(self._h, s, cp.data_ptr(), st.data_ptr(),
+                                            _stream_ptr(stream)))
+        (stream or torch.cuda.current_stream()).synchronize()
+        return cp, int(st.item()) == 0
 
     def heavy_dims(self, stream=None) -> list:
         """The dims kept as dense rows (ascending; synchronous)."""

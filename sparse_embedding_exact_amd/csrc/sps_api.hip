@@ -87,7 +87,7 @@ T *at(void *base, size_t off) {
 }
 
 struct ItemsLayout {
-  size_t inv, colp, post, sbase, heavy, slab, persistent;
+  size_t inv, dinfo, dtab, post, sbase, heavy, slab, persistent;
   size_t flags, norm64, skey0, skey1, spay, gdf, hsel, scratch;
   bool overflow;
 };
@@ -97,7 +97,9 @@ ItemsLayout items_layout(const sps::Geom &g, int64_t dim, int64_t nnz, bool dens
   ItemsLayout L{};
   Layout p;
   L.inv = p.add(g.n_items, 4);
-  L.colp = p.add((uint64_t)ns * (uint64_t)sps::cp_pitch(dim), 4);
+  L.dinfo = p.add(ns + 1, 16);
+  // a slice's table has max(1, 2 * distinct dims) buckets and distinct <= its nnz
+  L.dtab = p.add(sps::kBucketsPerDim * (uint64_t)nnz + (uint64_t)ns, 16);
   L.post = p.add(nnz + sps::kPostPad, 8);
   L.sbase = p.add(ns + 1, 4);
   L.heavy = p.add(sps::kHeavyMax + 1, 4);
@@ -148,7 +150,8 @@ struct sps_items {
   bool dense;
   int32_t pitch;  // slab row pitch (items), dense only
   float *inv_norm;
-  int32_t *col_ptr;
+  int4 *dinfo;
+  uint4 *dtab;
   uint2 *post;
   int32_t *slice_base;
   int32_t *heavy;
@@ -243,7 +246,8 @@ sps_status sps_prepare(const sps_csr *items, int32_t chunk_size, void *persisten
   d.indices = items->indices;
   d.values = items->values;
   d.inv_norm = at<float>(persistent, L.inv);
-  d.col_ptr = at<int32_t>(persistent, L.colp);
+  d.dinfo = at<int4>(persistent, L.dinfo);
+  d.dtab = at<uint4>(persistent, L.dtab);
   d.post = at<uint2>(persistent, L.post);
   d.slice_base = at<int32_t>(persistent, L.sbase);
   d.heavy = at<int32_t>(persistent, L.heavy);
@@ -270,7 +274,8 @@ sps_status sps_prepare(const sps_csr *items, int32_t chunk_size, void *persisten
   h->dense = dense;
   h->pitch = dense ? sps::slab_pitch(g.S) : 0;
   h->inv_norm = d.inv_norm;
-  h->col_ptr = d.col_ptr;
+  h->dinfo = d.dinfo;
+  h->dtab = d.dtab;
   h->post = d.post;
   h->slice_base = d.slice_base;
   h->heavy = d.heavy;
@@ -314,9 +319,21 @@ sps_status sps_items_slice_view(const sps_items *h, int64_t slice, void *stream,
   view->item_begin = h->g.slice_begin(slice);
   view->slice_len = (int32_t)(h->g.slice_end(slice) - view->item_begin);
   view->slice_nnz = be[1] - be[0];
-  view->col_ptr = h->col_ptr + slice * sps::cp_pitch(h->dim);
   view->post = reinterpret_cast<const sps_posting *>(h->post + be[0]);
   view->item_inv_norm = h->inv_norm + view->item_begin;
+  return SPS_OK;
+}
+
+sps_status sps_items_slice_col_ptr(const sps_items *h, int64_t slice, int32_t *col_ptr,
+                                   int32_t *status, void *stream) {
+  if (!h || !col_ptr) return fail(SPS_ERR_INVALID_ARGUMENT, "NULL handle or col_ptr");
+  if (slice < 0 || slice >= h->g.num_slices())
+    return fail(SPS_ERR_CHUNK_RANGE, "slice %lld outside [0, %lld)", (long long)slice,
+                (long long)h->g.num_slices());
+  const hipError_t e =
+      sps::launch_expand_col_ptr(h->dim, h->dinfo, h->dtab, h->slice_base, slice, col_ptr, status,
+                                 reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "sps_items_slice_col_ptr");
   return SPS_OK;
 }
 
@@ -453,7 +470,8 @@ static sps_status score_one(const sps_queries *q, const sps_items *items, int32_
   a.lptr = q->lptr;
   a.lrec = q->lrec;
   a.qh = q->qh;
-  a.col_ptr = items->col_ptr;
+  a.dinfo = items->dinfo;
+  a.dtab = items->dtab;
   a.post = items->post;
   a.post4 = items->post4;
   a.slice_base = items->slice_base;

@@ -64,6 +64,18 @@ __device__ __forceinline__ int32_t wave_incl_scan_dpp(int32_t x) {
   return x;
 }
 
+// Inclusive running maximum of a non-negative int over a wave64, with the
+// same DPP lane moves as wave_incl_scan_dpp (0 is the identity).
+__device__ __forceinline__ int32_t wave_incl_max_dpp(int32_t x) {
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true));  // row_shr:1
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true));  // row_shr:2
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true));  // row_shr:4
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true));  // row_shr:8
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false));  // row_bcast:15
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false));  // row_bcast:31
+  return x;
+}
+
 // Block-wide inclusive scan of a 32-bit int with one barrier. `ws` is NT/64
 // ints of LDS that the caller must not reuse before another barrier: two
 // calls need a barrier between them (the second would overwrite `ws` while

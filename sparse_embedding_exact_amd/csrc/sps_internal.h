@@ -103,9 +103,67 @@ __device__ inline void split_fp16(float x, uint16_t &hi, uint16_t &lo) {
 // Item pitch of a slice's heavy-dim slab: a whole number of 128-item groups
 // (one wave's share in the dense part).
 __host__ __device__ inline int32_t slab_pitch(int32_t S) { return (S + 127) / 128 * 128; }
-// Pitch (ints) of one slice's col_ptr[dim + 1]: rounded up to 4, so that each
-// slice's array starts 16-byte aligned.
-__host__ __device__ inline int64_t cp_pitch(int64_t dim) { return (dim + 1 + 3) / 4 * 4; }
+
+// ---- per-slice dim index: dim -> (first posting, list length) ----
+// A slice's inverted lists are the CSC of its items: lists in ascending dim
+// order, located by col_ptr[dim + 1]. Only the dims the slice holds have a
+// non-empty list, so instead of col_ptr (4 (dim + 1) bytes per slice, mostly
+// repeats) each slice keeps an open-addressing hash table of its non-empty
+// lists, small enough to stay in the L2 of the XCD that walks the slice.
+//  - info[s] = (first bucket, bucket count nb, wide, distinct dims); nb =
+//    max(1, 2 * distinct), so at most a quarter of the slots (narrow) or half
+//    of the buckets (wide) are used and a probe chain always ends (about 19
+//    lookups in 20 end in their home bucket);
+//  - a bucket is 16 bytes: two 8-byte slots (key = dim, value), or, for a
+//    "wide" slice (more than 2^22 entries), one key per bucket with the start
+//    and the length in separate words;
+//  - narrow value = start | (length - 1) << 22 (start is slice-relative, a
+//    length is at most the slice's item count, <= 1024);
+//  - home bucket = floor(nb * fib(d) / 2^32) with fib(d) = (d * 0x9E3779B1)
+//    mod 2^32 (Fibonacci hashing); linear probing by bucket.
+// Empty slots hold all ones (no dim is 2^32 - 1). The lookup result is
+// exact; the placement of keys in the table depends on insertion order and
+// is never observed.
+constexpr uint32_t kDimEmpty = 0xFFFFFFFFu;
+constexpr int kStartBits = 22;
+constexpr int64_t kNarrowMaxNnz = 1ll << kStartBits;
+constexpr int kBucketsPerDim = 2;
+__host__ __device__ inline uint32_t dim_bucket(uint32_t d, uint32_t nb) {
+  const uint32_t h = d * 0x9E3779B1u;
+  return (uint32_t)(((uint64_t)h * nb) >> 32);
+}
+// One bucket's verdict for dim d: 1 found (start, len set), 0 absent, -1 look
+// in the next bucket.
+__device__ __forceinline__ int dim_probe(uint4 e, uint32_t d, bool wide, int32_t &start,
+                                         int32_t &len) {
+  if (wide) {
+    if (e.x == d) {
+      start = (int32_t)e.y;
+      len = (int32_t)e.w;
+      return 1;
+    }
+    return e.x == kDimEmpty ? 0 : -1;
+  }
+  if (e.x == d || e.z == d) {
+    const uint32_t v = e.x == d ? e.y : e.w;
+    start = (int32_t)(v & ((1u << kStartBits) - 1u));
+    len = (int32_t)(v >> kStartBits) + 1;
+    return 1;
+  }
+  return (e.x == kDimEmpty || e.z == kDimEmpty) ? 0 : -1;
+}
+// the full lookup (a chain is never longer than nb buckets)
+__device__ __forceinline__ bool dim_lookup(const uint4 *__restrict__ tab, int4 info, uint32_t d,
+                                           int32_t &start, int32_t &len) {
+  const uint32_t nb = (uint32_t)info.y;
+  uint32_t b = dim_bucket(d, nb);
+  for (uint32_t k = 0; k < nb; ++k) {
+    const int r = dim_probe(tab[(int64_t)info.x + b], d, info.z != 0, start, len);
+    if (r >= 0) return r == 1;
+    b = b + 1 == nb ? 0u : b + 1;
+  }
+  return false;
+}
 // Row pitch (ints) of the score kernel's LDS accumulators: the slab pitch
 // plus 4, so that rows start 16 bytes apart modulo the LDS bank period.
 __host__ __device__ inline int32_t acc_pitch(int32_t S) { return slab_pitch(S) + 4; }
@@ -130,7 +188,8 @@ struct ItemsDev {
   const int32_t *indptr, *indices;
   const float *values;
   float *inv_norm;      // persistent, n_items
-  int32_t *col_ptr;     // persistent, num_slices * cp_pitch(dim)
+  int4 *dinfo;          // persistent, num_slices + 1: dim index per slice (info[ns].x = buckets)
+  uint4 *dtab;          // persistent, 2 nnz + num_slices buckets (the used prefix is filled)
   uint2 *post;          // persistent, nnz + kPostPad: (slice-local item id, value bits)
   int32_t *slice_base;  // persistent, num_slices + 1
   int32_t *heavy;       // persistent, kHeavyMax + 1: heavy dims ascending, then their count
@@ -144,6 +203,11 @@ struct ItemsDev {
 };
 constexpr int kHeavySelInts = 33 + 2 * 2048;
 hipError_t launch_prepare_items(const ItemsDev &d, hipStream_t s);
+// col_ptr[0..dim] of slice `slice` expanded from its dim index; *status |= 1
+// (nullable) where a list's length disagrees with the next list's start
+hipError_t launch_expand_col_ptr(int64_t dim, const int4 *dinfo, const uint4 *dtab,
+                                 const int32_t *slice_base, int64_t slice, int32_t *col_ptr,
+                                 int32_t *status, hipStream_t s);
 // 4-byte postings (item | fp16(256 value) << 16) from the prepared 8-byte
 // ones, plus kPostPad4 zero entries
 hipError_t launch_pack_half(const uint2 *post, int64_t nnz, uint32_t *post4, hipStream_t s);
@@ -179,7 +243,8 @@ struct ScoreArgs {
   const int32_t *lptr;
   const uint3 *lrec;          // light entries: (dim, value bits, row in group)
   const uint16_t *qh;         // [row groups] tiles of split fp16 (dense only)
-  const int32_t *col_ptr;     // all slices
+  const int4 *dinfo;          // dim index of every slice
+  const uint4 *dtab;
   const uint2 *post;          // all slices: (slice-local item id, value bits)
   const uint32_t *post4;      // reduced-precision variant: item | fp16(256 value) << 16
   const int32_t *slice_base;

@@ -14,7 +14,7 @@
 // All kernels are wave64. Device-side guards keep every access inside the
 // buffers the host sized, whatever the CSR contents: the prepare calls run
 // csr_check_kernel first, and every later kernel exits when it found a
-// structural fault (the col_ptr builder then writes empty lists).
+// structural fault (the dim index then holds no lists).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -243,17 +243,16 @@ __global__ void slice_base_kernel(Geom g, int64_t nnz, const int32_t *__restrict
   slice_base[s] = (int32_t)clamp64(indptr[i], 0, nnz);
 }
 
-// Per-slice inverted lists in two kernels, one workgroup per slice each:
+// Per-slice inverted lists, one workgroup per slice in each kernel:
 //  csc_sort_pass_kernel   a stable LSD radix sort of the slice's entries by
 //                         column (8-bit digits, one launch per digit). The
 //                         first pass reads the CSR in item order and carries
 //                         (slice-local item, fl32(v / |item|)); stability keeps
 //                         the items ascending within each column, and the last
 //                         pass writes the postings in place.
-//  csc_colptr_kernel      col_ptr of the slice from its sorted columns: tiles
-//                         of 8192 columns, each a histogram in LDS of the
-//                         keys that fall in it (a contiguous run of the sorted
-//                         keys), scanned and written once.
+//  dim_runs_kernel        the slice's dim index (sps_internal.h): each run
+//                         of equal sorted columns is one list; counted, then
+//                         inserted into the slice's hash table.
 constexpr int kSortNT = 1024;
 constexpr int kSortWaves = kSortNT / 64;
 
@@ -351,108 +350,200 @@ __global__ __launch_bounds__(kSortNT) void csc_sort_pass_kernel(
   }
 }
 
-// col_ptr[d] of the slice = the number of its entries with column < d, for
-// d = 0 .. dim; a structural fault leaves every list empty. With gdf, every
-// column holding at least hmin entries of the slice adds its count to gdf[d].
-// A tile of kCpTile columns is four segments of 4 kCpNT; thread t owns the
-// 4 columns at 4 t of each segment, so LDS reads and global stores are
-// lane-contiguous 16 bytes.
-constexpr int kCpNT = 512;
-constexpr int kCpTile = 16 * kCpNT;
-__global__ __launch_bounds__(kCpNT) void csc_colptr_kernel(
-    int64_t dim, const int32_t *__restrict__ flags, const int32_t *__restrict__ slice_base,
-    const int32_t *__restrict__ keys, int32_t *__restrict__ col_ptr, int32_t *__restrict__ gdf,
-    int32_t hmin) {
-  constexpr int NW = kCpNT / 64;
-  __shared__ int32_t s_h[kCpTile];
-  __shared__ int32_t s_ws[4][NW];
+// The slice's dim index (see sps_internal.h) from its sorted columns, in two
+// passes of one workgroup per slice over the sorted keys, tile by tile. An
+// entry ends a run (one dim's list) when the next key differs or the slice
+// ends; the run starts at the latest entry at or before it whose previous key
+// differs: a block-wide running maximum over the tile, carried from the
+// tiles before.
+//  COUNT   distinct dims -> info[s].w; with gdf, every list of at least hmin
+//          entries adds its length to gdf[d] (heavy-dim document frequency)
+//  INSERT  each list's (dim, start, length) into the slice's table
+// A structural fault leaves every slice with no lists.
+constexpr int kRunNT = 1024;
+template <bool INSERT>
+__global__ __launch_bounds__(kRunNT) void dim_runs_kernel(const int32_t *__restrict__ flags,
+                                                          const int32_t *__restrict__ slice_base,
+                                                          const int32_t *__restrict__ keys,
+                                                          int4 *__restrict__ info,
+                                                          uint4 *__restrict__ tab,
+                                                          int32_t *__restrict__ gdf, int32_t hmin) {
+  constexpr int NW = kRunNT / 64;
+  __shared__ int32_t s_ws[2][NW];
+  __shared__ int32_t s_cnt;
   const int64_t sl = blockIdx.x;
   const bool fault = flags[0] != 0;
   const int64_t b = fault ? 0 : slice_base[sl];
   const int64_t n = fault ? 0 : slice_base[sl + 1] - b;
   const int32_t *ks = keys + b;
-  int32_t *cp = col_ptr + sl * cp_pitch(dim);
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
-  const int64_t ncp = dim + 1;
-  int4 *h4 = reinterpret_cast<int4 *>(s_h);
-  int64_t p0 = 0;  // entries with a column below this tile
-  // the first key chunk of the next tile is loaded before this tile's scan
-  int32_t kc = t < n ? ks[t] : 0;
-  // Two barriers per tile: the histogram slots a thread reads after counting
-  // it clears at once, before the barrier that precedes its stores, so the
-  // next tile's counts (after that barrier) start from zero; and the next
-  // tile's counting loop passes at least one barrier before the wave totals
-  // of this tile are overwritten.
+  int4 inf = make_int4(0, 1, 0, 0);
+  if (INSERT) inf = info[sl];
+  if (!INSERT && t == 0) s_cnt = 0;
+  int32_t mine = 0;   // runs ending at this thread's entries
+  int32_t carry = 0;  // 1 + start of the run open at the tile's first entry
+  int parity = 0;
+  for (int64_t base = 0; base < n; base += kRunNT, parity ^= 1) {
+    const int64_t i = base + t;
+    const bool valid = i < n;
+    const int32_t k = valid ? ks[i] : 0;
+    const bool first = valid && (i == 0 || ks[i - 1] != k);
+    const bool last = valid && (i == n - 1 || ks[i + 1] != k);
+    // running maximum of 1 + (index of a run's first entry), 0 elsewhere
+    int32_t m = wave_incl_max_dpp(first ? (int32_t)i + 1 : 0);
+    if (lane == 63) s_ws[parity][wv] = m;
+    __syncthreads();
+    int32_t tile_max = 0;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) h4[k * kCpNT + t] = make_int4(0, 0, 0, 0);
-  __syncthreads();
-  for (int64_t D0 = 0; D0 < ncp; D0 += kCpTile) {
-    // the tile's keys are the next run of the sorted keys; equal keys of a
-    // wave are added once, by the first lane of their run
-    const int64_t Dend = D0 + kCpTile;
-    int64_t q = p0;
-    int32_t k = kc;
-    for (;;) {
-      const int64_t i = q + t;
-      const bool in = i < n && k < Dend;
-      const int32_t kprev = __shfl_up(k, 1, 64);
-      const bool start = in && (lane == 0 || kprev != k);
-      const uint64_t stop = __ballot(!in || lane == 0 || kprev != k);
-      if (start && k >= D0) {  // (sorted keys are >= D0 here)
-        const uint64_t above = stop & (lane == 63 ? 0ull : (~0ull << (lane + 1)));
-        const int next = above ? __ffsll((long long)above) - 1 : 64;
-        atomicAdd(&s_h[k - D0], next - lane);
-      }
-      const int c = __syncthreads_count(in);
-      q += c;
-      k = q + t < n ? ks[q + t] : 0;
-      if (c < kCpNT) break;
+    for (int w = 0; w < NW; ++w) {
+      const int32_t x = s_ws[parity][w];
+      if (w < wv) m = max(m, x);
+      tile_max = max(tile_max, x);
     }
-    kc = k;
-    // counts of this thread's four column groups, and their exclusive prefix
-    // in column order (segment-major), from one wave scan per segment
-    int4 v[4];
-    int32_t sg[4], incl[4];
-#pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) {
-      v[s4] = h4[s4 * kCpNT + t];
-      h4[s4 * kCpNT + t] = make_int4(0, 0, 0, 0);
-      sg[s4] = (v[s4].x + v[s4].y) + (v[s4].z + v[s4].w);
-      incl[s4] = wave_incl_scan_dpp(sg[s4]);
-      if (lane == 63) s_ws[s4][wv] = incl[s4];
+    const int32_t st = max(m, carry) - 1;  // (alternate buffers: no second barrier)
+    carry = max(carry, tile_max);
+    if (!last) continue;
+    const int32_t len = (int32_t)i - st + 1;
+    if (!INSERT) {
+      ++mine;
+      if (gdf != nullptr && len >= hmin) atomicAdd(&gdf[k], len);
+      continue;
+    }
+    const uint32_t nb = (uint32_t)inf.y;
+    uint32_t bk = dim_bucket((uint32_t)k, nb);
+    unsigned long long *t64 = reinterpret_cast<unsigned long long *>(tab + inf.x);
+    constexpr unsigned long long kEmpty64 = ~0ull;
+    for (uint32_t tries = 0; tries < nb; ++tries) {
+      unsigned long long *slot = t64 + 2 * (int64_t)bk;
+      if (inf.z) {  // wide: (dim, start) then (dim, length)
+        const unsigned long long w0 = (uint32_t)k | ((unsigned long long)(uint32_t)st << 32);
+        if (atomicCAS(slot, kEmpty64, w0) == kEmpty64) {
+          slot[1] = (uint32_t)k | ((unsigned long long)(uint32_t)len << 32);
+          break;
+        }
+      } else {
+        // a list is at most one entry per item of the slice (canonical CSR)
+        const uint32_t lm1 = (uint32_t)(len < kSliceMax ? len : kSliceMax) - 1u;
+        const uint32_t v = (uint32_t)st | (lm1 << kStartBits);
+        const unsigned long long w = (uint32_t)k | ((unsigned long long)v << 32);
+        if (atomicCAS(slot, kEmpty64, w) == kEmpty64) break;
+        if (atomicCAS(slot + 1, kEmpty64, w) == kEmpty64) break;
+      }
+      bk = bk + 1 == nb ? 0u : bk + 1;
+    }
+  }
+  if (INSERT) return;
+  __syncthreads();  // s_cnt is cleared
+  mine = wave_sum(mine);
+  if (lane == 0 && mine != 0) atomicAdd(&s_cnt, mine);
+  __syncthreads();
+  if (t == 0) info[sl] = make_int4(0, 0, 0, s_cnt);
+}
+
+// Bucket ranges of the slices' tables (one workgroup): nb = max(1, 2 distinct),
+// first bucket = the sum over earlier slices; info[ns].x = total buckets.
+__global__ __launch_bounds__(1024) void dim_layout_kernel(int64_t ns,
+                                                          const int32_t *__restrict__ slice_base,
+                                                          int4 *__restrict__ info) {
+  __shared__ int32_t ws[16];
+  int32_t carry = 0;
+  for (int64_t base = 0; base < ns; base += 1024) {
+    const int64_t s = base + threadIdx.x;
+    int4 x = make_int4(0, 0, 0, 0);
+    int32_t nb = 0;
+    if (s < ns) {
+      x = info[s];
+      nb = x.w > 0 ? kBucketsPerDim * x.w : 1;
+    }
+    int32_t tot;
+    const int32_t incl = block_incl_scan<1024>(nb, ws, &tot);
+    if (s < ns) {
+      const int64_t nnz_s = (int64_t)slice_base[s + 1] - slice_base[s];
+      info[s] = make_int4(carry + incl - nb, nb, nnz_s > kNarrowMaxNnz ? 1 : 0, x.w);
+    }
+    carry += tot;
+  }
+  if (threadIdx.x == 0) info[ns] = make_int4(carry, 0, 0, 0);
+}
+
+// every word of the first info[ns].x buckets set to all ones (empty)
+__global__ void dim_clear_kernel(const int4 *__restrict__ total, uint4 *__restrict__ tab) {
+  const int64_t n = total->x;
+  const uint4 e = make_uint4(kDimEmpty, kDimEmpty, kDimEmpty, kDimEmpty);
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    tab[i] = e;
+}
+
+// col_ptr of one slice from its index (for verification and tools): dims
+// with a list take their start, the others (and the end) the slice's entry
+// count, then a suffix minimum gives every dim the start of the next list.
+__global__ void expand_starts_kernel(int64_t dim, const int4 *__restrict__ dinfo,
+                                     const uint4 *__restrict__ dtab,
+                                     const int32_t *__restrict__ slice_base, int64_t slice,
+                                     int32_t *__restrict__ cp) {
+  const int4 inf = dinfo[slice];
+  const int32_t nnz_s = slice_base[slice + 1] - slice_base[slice];
+  for (int64_t d = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; d <= dim;
+       d += (int64_t)gridDim.x * blockDim.x) {
+    int32_t st = nnz_s, len = 0;
+    if (d < dim && !dim_lookup(dtab, inf, (uint32_t)d, st, len)) st = nnz_s;
+    cp[d] = st;
+  }
+}
+
+__global__ __launch_bounds__(1024) void suffix_min_kernel(int64_t n, int32_t *__restrict__ a) {
+  __shared__ int32_t ws[16];
+  int32_t carry = 0x7fffffff;
+  for (int64_t top = n; top > 0; top -= 1024) {
+    // element top - 1 - t, so that lane order runs from the end
+    const int64_t j = top - 1 - threadIdx.x;
+    const int32_t v = j >= 0 ? a[j] : 0x7fffffff;
+    // inclusive running minimum = -(running maximum of -v), via biased values
+    const uint32_t biased = 0x7fffffffu - (uint32_t)v;  // v >= 0: fits, and order reverses
+    int32_t m = wave_incl_max_dpp((int32_t)biased);
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    if (lane == 63) ws[wv] = m;
+    __syncthreads();
+    int32_t tmax = 0;
+    for (int w = 0; w < 16; ++w) {
+      if (w < wv) m = max(m, ws[w]);
+      tmax = max(tmax, ws[w]);
     }
     __syncthreads();
-    int32_t base = (int32_t)p0;
-#pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) {
-      int32_t before = 0, total = 0;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        const int32_t x = s_ws[s4][w];
-        before += w < wv ? x : 0;
-        total += x;
-      }
-      int32_t ex = base + before + incl[s4] - sg[s4];
-      const int64_t j = D0 + 4 * ((int64_t)s4 * kCpNT + t);
-      const int32_t vs[4] = {v[s4].x, v[s4].y, v[s4].z, v[s4].w};
-      int32_t o[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        o[u] = ex;
-        ex += vs[u];
-        if (gdf != nullptr && vs[u] >= hmin && j + u < dim) atomicAdd(&gdf[j + u], vs[u]);
-      }
-      if (j + 3 < ncp) {
-        reinterpret_cast<int4 *>(cp)[j >> 2] = make_int4(o[0], o[1], o[2], o[3]);
-      } else {
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          if (j + u < ncp) cp[j + u] = o[u];
-      }
-      base += total;
-    }
-    p0 = q;
+    const int32_t runmin = 0x7fffffff - m;
+    if (j >= 0) a[j] = min(runmin, carry);
+    carry = min(carry, 0x7fffffff - tmax);
   }
+}
+
+// *status |= 1 where a list's start plus its length is not the next entry of col_ptr
+__global__ void expand_check_kernel(int64_t dim, const int4 *__restrict__ dinfo,
+                                    const uint4 *__restrict__ dtab, int64_t slice,
+                                    const int32_t *__restrict__ cp, int32_t *status) {
+  const int4 inf = dinfo[slice];
+  for (int64_t d = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; d < dim;
+       d += (int64_t)gridDim.x * blockDim.x) {
+    int32_t st = 0, len = 0;
+    if (dim_lookup(dtab, inf, (uint32_t)d, st, len) && (cp[d] != st || cp[d + 1] != st + len))
+      atomicOr(status, 1);
+  }
+}
+
+hipError_t launch_expand_col_ptr(int64_t dim, const int4 *dinfo, const uint4 *dtab,
+                                 const int32_t *slice_base, int64_t slice, int32_t *col_ptr,
+                                 int32_t *status, hipStream_t s) {
+  int64_t blocks = (dim + 1 + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(expand_starts_kernel, dim3((unsigned)blocks), dim3(256), 0, s, dim, dinfo,
+                     dtab, slice_base, slice, col_ptr);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(suffix_min_kernel, dim3(1), dim3(1024), 0, s, dim + 1, col_ptr);
+  if ((e = hipGetLastError()) != hipSuccess || status == nullptr) return e;
+  hipLaunchKernelGGL(expand_check_kernel, dim3((unsigned)blocks), dim3(256), 0, s, dim, dinfo,
+                     dtab, slice, col_ptr, status);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
@@ -564,17 +655,19 @@ __global__ __launch_bounds__(1024) void heavy_rank_kernel(int32_t cap,
 
 // slab of slice s: item j's split-fp16 heavy values in its tile (pre-zeroed)
 __global__ __launch_bounds__(256) void slab_scatter_kernel(
-    int64_t dim, int32_t pitch, const int32_t *__restrict__ flags,
-    const int32_t *__restrict__ heavy, const int32_t *__restrict__ col_ptr,
+    int32_t pitch, const int32_t *__restrict__ flags, const int32_t *__restrict__ heavy,
+    const int4 *__restrict__ dinfo, const uint4 *__restrict__ dtab,
     const int32_t *__restrict__ slice_base, const uint2 *__restrict__ post,
     uint16_t *__restrict__ slab) {
   const int64_t c = blockIdx.x / kHeavyMax;
   const int h = blockIdx.x % kHeavyMax;
   if (flags[0] != 0 || h >= heavy[kHeavyMax]) return;
   const int32_t d = heavy[h];
-  const int32_t *cp = col_ptr + c * cp_pitch(dim);
   const int64_t base = slice_base[c];
-  const int32_t b = cp[d], e = cp[d + 1];
+  const int32_t snnz = slice_base[c + 1] - slice_base[c];
+  int32_t b = 0, len = 0;
+  if (!dim_lookup(dtab, dinfo[c], (uint32_t)d, b, len)) return;
+  const int32_t e = (int32_t)clamp64((int64_t)b + len, 0, snnz);
   uint16_t *sl = slab + c * (int64_t)pitch * kHeavyRec;
   for (int32_t k = b + threadIdx.x; k < e; k += 256) {
     const uint2 pe = post[base + k];
@@ -628,9 +721,17 @@ hipError_t launch_prepare_items(const ItemsDev &d, hipStream_t s) {
                          kd, pd, 8 * p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
+  // the dim index: count the lists, lay out the tables, clear them, insert
   const int32_t hmin = g.S / (2 * kHeavyFracInv) > 2 ? g.S / (2 * kHeavyFracInv) : 2;
-  hipLaunchKernelGGL(csc_colptr_kernel, dim3((unsigned)ns), dim3(kCpNT), 0, s, d.dim, d.flags,
-                     d.slice_base, d.skey[0], d.col_ptr, d.dense ? d.gdf : nullptr, hmin);
+  hipLaunchKernelGGL(dim_runs_kernel<false>, dim3((unsigned)ns), dim3(kRunNT), 0, s, d.flags,
+                     d.slice_base, d.skey[0], d.dinfo, d.dtab, d.dense ? d.gdf : nullptr, hmin);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(dim_layout_kernel, dim3(1), dim3(1024), 0, s, ns, d.slice_base, d.dinfo);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(dim_clear_kernel, dim3(2048), dim3(256), 0, s, d.dinfo + ns, d.dtab);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(dim_runs_kernel<true>, dim3((unsigned)ns), dim3(kRunNT), 0, s, d.flags,
+                     d.slice_base, d.skey[0], d.dinfo, d.dtab, nullptr, 0);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (!d.dense) return hipSuccess;
   const int64_t tg64 = (g.n_items + kHeavyFracInv - 1) / kHeavyFracInv;
@@ -652,7 +753,7 @@ hipError_t launch_prepare_items(const ItemsDev &d, hipStream_t s) {
   e = launch_fill_i32(reinterpret_cast<int32_t *>(d.slab), ns * (int64_t)pitch * kHeavyRec / 2, 0, s);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(slab_scatter_kernel, dim3((unsigned)(ns * kHeavyMax)), dim3(256), 0, s,
-                     d.dim, pitch, d.flags, d.heavy, d.col_ptr, d.slice_base, d.post, d.slab);
+                     pitch, d.flags, d.heavy, d.dinfo, d.dtab, d.slice_base, d.post, d.slab);
   return hipGetLastError();
 }
 

@@ -144,7 +144,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void sc
   const int32_t Sp = slab_pitch(g.S);  // slab row pitch (items)
   const int32_t Lp = acc_pitch(g.S);   // accumulator row pitch (ints)
 
-  const int32_t *cps = a.col_ptr + sl * cp_pitch(a.dim);
+  const int4 dix = a.dinfo[sl];  // the slice's dim index (uniform)
+  const uint4 *__restrict__ dtab = a.dtab + dix.x;
   const int32_t cb0 = a.slice_base[sl];
   const int32_t snnz = a.slice_base[sl + 1] - cb0 > 0 ? a.slice_base[sl + 1] - cb0 : 0;
   // light entries of group gi: [ge[gi], ge[gi + 1]) (the rows are consecutive)
@@ -163,7 +164,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void sc
   // the start, so both groups' lookups overlap the dense part.
   struct Raw {
     uint3 rec[2];  // (dim, value bits, row in group)
-    int32_t lo[2], hi[2];
+    uint4 bkt[2];  // the dim's home bucket in the slice's index
     bool ok[2];
   };
   struct Desc {
@@ -183,21 +184,28 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void sc
   auto fetch_ranges = [&](Raw &r) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const bool dok = r.rec[i].x < (uint64_t)a.dim;
-      r.ok[i] = r.ok[i] && dok;
-      const int32_t d = dok ? (int32_t)r.rec[i].x : 0;
-      // cps[d] and cps[d + 1] with one 8-byte load (4-byte aligned)
-      const u32x2 lh = *reinterpret_cast<const u32x2_a4 *>(cps + d);
-      r.lo[i] = (int32_t)lh.x;
-      r.hi[i] = (int32_t)lh.y;
+      r.ok[i] = r.ok[i] && r.rec[i].x < (uint64_t)a.dim;
+      // the home bucket of the dim: one 16-byte load; most lookups end there
+      r.bkt[i] = dtab[dim_bucket(r.rec[i].x, (uint32_t)dix.y)];
     }
   };
   auto finish_ranges = [&](const Raw &r, Desc &b) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const bool ok = r.ok[i];
-      b.s[i] = ok ? (int32_t)clamp64(r.lo[i], 0, snnz) : 0;
-      const int32_t L = ok ? (int32_t)clamp64(r.hi[i], b.s[i], snnz) - b.s[i] : 0;
+      const uint32_t d = r.rec[i].x;
+      int32_t st = 0, L = 0;
+      int res = r.ok[i] ? dim_probe(r.bkt[i], d, dix.z != 0, st, L) : 0;
+      if (res < 0) {  // a full home bucket: follow the chain
+        const uint32_t nb = (uint32_t)dix.y;
+        uint32_t bk = dim_bucket(d, nb);
+        for (uint32_t k = 1; k < nb && res < 0; ++k) {
+          bk = bk + 1 == nb ? 0u : bk + 1;
+          res = dim_probe(dtab[bk], d, dix.z != 0, st, L);
+        }
+      }
+      if (res != 1) st = L = 0;
+      b.s[i] = (int32_t)clamp64(st, 0, snnz);
+      L = (int32_t)clamp64((int64_t)b.s[i] + L, b.s[i], snnz) - b.s[i];
       b.L[i] = L < kSliceMax ? L : kSliceMax;  // a slice holds a dim once per item
       b.row[i] = (int32_t)(r.rec[i].z & (kRows - 1));
       b.qv[i] = __uint_as_float(r.rec[i].y);

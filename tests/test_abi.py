@@ -41,8 +41,9 @@ def test_items_sizing(lib):
     p, s = ctypes.c_size_t(), ctypes.c_size_t()
     assert lib.sps_items_workspace_size(2_000_000, 1_200_000, 86_000_000, 8192,
                                         ctypes.byref(p), ctypes.byref(s)) == 0
-    # col_ptr: 245 chunks x 8 slices x (1.2M + 1) int32; postings: 8 B each
-    assert p.value >= 1960 * 1_200_001 * 4 + 86_000_000 * 8
+    # dim index: 1960 slices, up to 2 x nnz + slices 16-byte buckets; postings: 8 B each
+    assert p.value >= (2 * 86_000_000 + 1960) * 16 + 86_000_000 * 8
+    assert p.value < 4 * 86_000_000 * 16  # no per-slice col_ptr[dim + 1]
     assert s.value >= 86_000_000 * 10
     assert p.value % 256 == 0 and s.value % 256 == 0
     bad = [(-1, 10, 0, 8192), (10, 0, 0, 8192), (10, 10, 0, 0), (10, 10, 0, (1 << 20) + 1),
