@@ -39,9 +39,11 @@
  *    and inside [0, n_cols), values finite (§3.1 note: the merge needs
  *    strictly ordered indices). The prepare calls check the structure on
  *    the device: on a structural fault (indptr out of order or range, an
- *    index outside [0, n_cols)) they do no out-of-range access; the handle
- *    then scores every affected row as empty. sps_validate_csr reports the
- *    fault to the host.
+ *    index outside [0, n_cols)) they do no out-of-range access, still
+ *    return SPS_OK, and the handle scores every row of that corpus or batch
+ *    as 0. They report nothing to the host: callers with untrusted input
+ *    run sps_validate_csr first (synchronous; it names the first faulty row
+ *    and the reason).
  */
 #ifndef SPS_H
 #define SPS_H
@@ -216,7 +218,11 @@ void sps_queries_destroy(sps_queries *q);
  * touched. out: DEVICE, n_rows * ld_out floats, ld_out >= min(chunk_size,
  * n_items). row_sums (nullable): DEVICE double[n_rows]; row_sums[q] = the
  * float64 sum of the float32 scores written for row q (a per-chunk checksum).
- * No clamping to [-1, 1] is applied. Results are bitwise reproducible. */
+ * No clamping to [-1, 1] is applied. Results are bitwise reproducible.
+ * Concurrency: with chunk_size above 1024 the per-slice partial row sums go
+ * through a buffer in the query batch's workspace, so calls that pass
+ * row_sums for the same sps_queries must be ordered on one stream (calls
+ * without row_sums, or on different query batches, may run concurrently). */
 sps_status sps_cosine_chunk(const sps_queries *q, const sps_items *items, int32_t chunk,
                             float *out, int64_t ld_out, double *row_sums, void *stream);
 

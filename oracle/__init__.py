@@ -84,9 +84,10 @@ class Oracle:
                                  ctypes.c_int]
         L.orc_chunk_row_sums.restype = None
         L.orc_chunk_row_sums.argtypes = [_P, _P, _P, _P, _I64, _P, _P, _P, _P, _I64, _I64,
-                                         _I64, _P, ctypes.c_int]
+                                         _I64, _P, ctypes.c_int, ctypes.c_int]
         L.orc_col_sums.restype = None
-        L.orc_col_sums.argtypes = [_P, _P, _P, _P, _I64, _P, _P, _P, _P, _I64, _I64, _I64, _P]
+        L.orc_col_sums.argtypes = [_P, _P, _P, _P, _I64, _P, _P, _P, _P, _I64, _I64, _I64, _P,
+                                   ctypes.c_int]
         self.L = L
 
     # -- validation -------------------------------------------------------
@@ -159,8 +160,12 @@ class Oracle:
 
     # -- closed-form checksums -------------------------------------------
     def chunk_row_sums(self, queries, items, chunk_size: int, q_norm=None, i_norm=None,
-                       n_threads: int | None = None):
-        """float64 [n_chunks, n_q]: sum of S over each chunk's items, per query row."""
+                       n_threads: int | None = None, kind: int = 0):
+        """float64 [n_chunks, n_q]: sum of S over each chunk's items, per query row.
+
+        kind 1: the same sum of sum_d |q^_d i^_d| (the scale of each pair's rounding
+        error); kind 2: of the number of shared stored dims (rows with a zero norm
+        count none)."""
         if q_norm is None:
             q_norm = self.row_norms(queries)[0]
         if i_norm is None:
@@ -176,12 +181,13 @@ class Oracle:
                                   qn.ctypes.data, queries.n_rows, iip.ctypes.data,
                                   iix.ctypes.data, iv.ctypes.data, inn.ctypes.data,
                                   items.n_rows, items.n_cols, chunk_size, out.ctypes.data,
-                                  n_threads or _threads())
+                                  n_threads or _threads(), int(kind))
         return out
 
     def col_sums(self, queries, items, item_begin: int = 0, item_end: int | None = None,
-                 q_norm=None, i_norm=None):
-        """float64 [item_end-item_begin]: sum over all query rows of S[q, i]."""
+                 q_norm=None, i_norm=None, kind: int = 0):
+        """float64 [item_end-item_begin]: sum over all query rows of S[q, i] (kind 1 and 2
+        as in chunk_row_sums)."""
         if q_norm is None:
             q_norm = self.row_norms(queries)[0]
         if i_norm is None:
@@ -197,7 +203,7 @@ class Oracle:
         self.L.orc_col_sums(qip.ctypes.data, qix.ctypes.data, qv.ctypes.data, qn.ctypes.data,
                             queries.n_rows, iip.ctypes.data, iix.ctypes.data, iv.ctypes.data,
                             inn.ctypes.data, items.n_cols, item_begin, item_end,
-                            out.ctypes.data)
+                            out.ctypes.data, int(kind))
         return out
 
 

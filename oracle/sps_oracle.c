@@ -226,7 +226,24 @@ void orc_scores(const int32_t *q_indptr, const int32_t *q_indices, const float *
 /*   sum_{i in chunk} S[q,i] = q^ . (sum_{i in chunk} i^)               */
 /*   sum_q S[q,i]            = (sum_q q^) . i^                          */
 /* where x^ = x / ||x|| (0 for a zero-norm row).                        */
+/*                                                                    */
+/* The same closed forms hold with every normalised value x passed    */
+/* through t() on both sides, since the sums are over products of     */
+/* matched entries: kind 0 t(x) = x (the sums of S); kind 1 t(x) = |x| */
+/* (the sums of sum_d |q^_d i^_d|, the scale of a pair's rounding      */
+/* error); kind 2 t(x) = 1 for every stored entry of a row with a      */
+/* non-zero norm (the number of shared dims, summed over the pairs).   */
 /* ------------------------------------------------------------------ */
+
+static double orc_t(double x, int kind) {
+#if ORC_MUTANT == 9
+  if (kind == 1) return x;
+#else
+  if (kind == 1) return fabs(x);
+#endif
+  if (kind == 2) return 1.0;
+  return x;
+}
 
 typedef struct {
   const int32_t *q_indptr, *q_indices; const float *q_values; const double *q_norm;
@@ -234,6 +251,7 @@ typedef struct {
   const int32_t *i_indptr, *i_indices; const float *i_values; const double *i_norm;
   int64_t n_items, dim, chunk_size, n_chunks;
   double *row_sums; /* n_chunks x n_q */
+  int kind;
   int64_t next;
   pthread_mutex_t mu;
 } rowsum_job;
@@ -252,7 +270,7 @@ static void *rowsum_worker(void *arg) {
       const double n = J->i_norm[i];
       if (!(n > 0.0)) continue;
       for (int64_t k = J->i_indptr[i]; k < J->i_indptr[i + 1]; ++k)
-        s[J->i_indices[k]] += (double)J->i_values[k] / n;
+        s[J->i_indices[k]] += orc_t((double)J->i_values[k] / n, J->kind);
     }
     double *out = J->row_sums + c * J->n_q;
     for (int64_t q = 0; q < J->n_q; ++q) {
@@ -261,9 +279,9 @@ static void *rowsum_worker(void *arg) {
       if (n > 0.0) {
         for (int64_t k = J->q_indptr[q]; k < J->q_indptr[q + 1]; ++k) {
 #if ORC_MUTANT == 7
-          acc += (double)J->q_values[k] * s[J->q_indices[k]];
+          acc += orc_t((double)J->q_values[k], J->kind) * s[J->q_indices[k]];
 #else
-          acc += ((double)J->q_values[k] / n) * s[J->q_indices[k]];
+          acc += orc_t((double)J->q_values[k] / n, J->kind) * s[J->q_indices[k]];
 #endif
         }
       }
@@ -277,13 +295,16 @@ static void *rowsum_worker(void *arg) {
   return NULL;
 }
 
-/* row_sums[c * n_q + q] = sum over items of chunk c of S[q, i], for every chunk */
+/* row_sums[c * n_q + q] = sum over items of chunk c of S[q, i], for every
+ * chunk (kind 0; kinds 1 and 2 as above) */
 void orc_chunk_row_sums(const int32_t *q_indptr, const int32_t *q_indices,
                         const float *q_values, const double *q_norm, int64_t n_q,
                         const int32_t *i_indptr, const int32_t *i_indices,
                         const float *i_values, const double *i_norm, int64_t n_items,
-                        int64_t dim, int64_t chunk_size, double *row_sums, int n_threads) {
+                        int64_t dim, int64_t chunk_size, double *row_sums, int n_threads,
+                        int kind) {
   rowsum_job J;
+  J.kind = kind;
   J.q_indptr = q_indptr; J.q_indices = q_indices; J.q_values = q_values; J.q_norm = q_norm;
   J.n_q = n_q;
   J.i_indptr = i_indptr; J.i_indices = i_indices; J.i_values = i_values; J.i_norm = i_norm;
@@ -302,24 +323,26 @@ void orc_chunk_row_sums(const int32_t *q_indptr, const int32_t *q_indices,
   pthread_mutex_destroy(&J.mu);
 }
 
-/* col_sums[i - item_begin] = sum over all queries of S[q, i] */
+/* col_sums[i - item_begin] = sum over all queries of S[q, i] (kind 0; kinds
+ * 1 and 2 as above) */
 void orc_col_sums(const int32_t *q_indptr, const int32_t *q_indices, const float *q_values,
                   const double *q_norm, int64_t n_q, const int32_t *i_indptr,
                   const int32_t *i_indices, const float *i_values, const double *i_norm,
-                  int64_t dim, int64_t item_begin, int64_t item_end, double *col_sums) {
+                  int64_t dim, int64_t item_begin, int64_t item_end, double *col_sums,
+                  int kind) {
   double *qbar = (double *)calloc((size_t)dim, sizeof(double));
   for (int64_t q = 0; q < n_q; ++q) {
     const double n = q_norm[q];
     if (!(n > 0.0)) continue;
     for (int64_t k = q_indptr[q]; k < q_indptr[q + 1]; ++k)
-      qbar[q_indices[k]] += (double)q_values[k] / n;
+      qbar[q_indices[k]] += orc_t((double)q_values[k] / n, kind);
   }
   for (int64_t i = item_begin; i < item_end; ++i) {
     const double n = i_norm[i];
     double acc = 0.0;
     if (n > 0.0)
       for (int64_t k = i_indptr[i]; k < i_indptr[i + 1]; ++k)
-        acc += qbar[i_indices[k]] * ((double)i_values[k] / n);
+        acc += qbar[i_indices[k]] * orc_t((double)i_values[k] / n, kind);
     col_sums[i - item_begin] = acc;
   }
   free(qbar);

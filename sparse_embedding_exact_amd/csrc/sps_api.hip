@@ -604,6 +604,8 @@ sps_status sps_cosine_stream_host(const sps_queries *q, const sps_items *items,
   const hipStream_t cs = reinterpret_cast<hipStream_t>(copy_stream);
   float *buf[2] = {dev_buf0, dev_buf1};
   hipEvent_t scored[2] = {nullptr, nullptr}, copied[2] = {nullptr, nullptr};
+  bool recorded[2] = {false, false};  // copied[k] marks an enqueued copy
+  bool unmarked = false;
   hipError_t e = hipSuccess;
   for (int k = 0; k < 2 && e == hipSuccess; ++k) {
     e = hipEventCreateWithFlags(&scored[k], hipEventDisableTiming);
@@ -624,12 +626,21 @@ sps_status sps_cosine_stream_host(const sps_queries *q, const sps_items *items,
       e = hipMemcpy2DAsync(host_out + (items->g.chunk_begin(c) - item0), (size_t)ld_host * 4,
                            buf[k], (size_t)ld_dev * 4, (size_t)len * 4, (size_t)q->n_rows,
                            hipMemcpyDeviceToHost, cs);
-    if (e == hipSuccess) e = hipEventRecord(copied[k], cs);
+    if (e == hipSuccess) {
+      e = hipEventRecord(copied[k], cs);
+      if (e == hipSuccess) recorded[k] = true;
+      else unmarked = true;  // a copy no event marks: wait for the copy stream below
+    }
   }
-  // the call completes in `stream` order: the stream waits for the last copies
-  const int used = chunk_end - chunk_begin < 2 ? chunk_end - chunk_begin : 2;
-  for (int k = 0; k < used && e == hipSuccess && st == SPS_OK; ++k)
-    e = hipStreamWaitEvent(s, copied[k], 0);
+  // the call completes in `stream` order: the stream waits for every copy
+  // that was enqueued, also after an error, so that later work on `stream`
+  // (the caller freeing or reusing the buffers) never overtakes a copy
+  for (int k = 0; k < 2; ++k)
+    if (recorded[k]) {
+      const hipError_t w = hipStreamWaitEvent(s, copied[k], 0);
+      if (e == hipSuccess) e = w;
+    }
+  if (unmarked) (void)hipStreamSynchronize(cs);
   for (int k = 0; k < 2; ++k) {
     if (scored[k]) (void)hipEventDestroy(scored[k]);
     if (copied[k]) (void)hipEventDestroy(copied[k]);

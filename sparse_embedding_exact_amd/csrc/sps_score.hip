@@ -122,7 +122,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void sc
   // table past its last segment)
   __shared__ uint32_t s_spos[kSegMax + kSegPad], s_sqv[kSegMax + kSegPad],
       s_smeta[kSegMax + kSegPad];
-  __shared__ int32_t ws[NW];
+  __shared__ int32_t ws[2][NW];
   // threshold epilogue: hits per wave of the current group, and the group's
   // first position in the hit buffer
   __shared__ int32_t s_wtot[NW];
@@ -320,7 +320,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void sc
   const uint32_t *__restrict__ ppost4 = HALF ? a.post4 + cb0 : nullptr;
   const int64_t col0 = ib - g.chunk_begin(a.chunk);
   const bool v4 = vec4 && (col0 % 4 == 0);
-  double *rsum = g.n_sub == 1 ? a.row_sums : a.rs_part;
+  // per-slice partial row sums only when row sums are asked for
+  double *rsum = a.row_sums == nullptr ? nullptr : (g.n_sub == 1 ? a.row_sums : a.rs_part);
+  int scan_par = 0;
   for (int gi = 0; gi < ng; ++gi) {
     const int64_t q0 = (grp0 + gi) * kRows;
     if (gi > 0) {
@@ -358,8 +360,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void sc
 #pragma unroll
       for (int i = 0; i < 2; ++i) nseg[i] = (c.L[i] + kSeg - 1) / kSeg;
       int32_t total;
-      // (a barrier inside; the previous call is behind the barriers of its round)
-      const int32_t pend = block_incl_scan_1b<NT>(nseg[0] + nseg[1], ws, &total);
+      // (a barrier inside). Consecutive scans alternate between two buffers: a
+      // batch with no segments has no barrier after its scan, so without them
+      // a fast wave's next scan could overwrite totals a slow wave still reads.
+      const int32_t pend = block_incl_scan_1b<NT>(nseg[0] + nseg[1], ws[scan_par], &total);
+      scan_par ^= 1;
       const int32_t sp[2] = {pend - nseg[0] - nseg[1], pend - nseg[1]};
       for (int32_t r0 = 0; r0 < total; r0 += kSegMax) {
         // the segments of this round that belong to this thread's lists

@@ -212,6 +212,32 @@ def pin_checksums(orc):
         assert np.abs(rs[c] - S[:, b:e].sum(1)).max() <= 1e-9
     cs = orc.col_sums(q, items, 100, 900)
     assert np.abs(cs - S[:, 100:900].sum(0)).max() <= 1e-9
+    # the same closed forms over |q^_d i^_d| and over shared-dim counts, against
+    # brute-force densified rows: |Q^| |I^|^T and the product of the stored-entry masks
+    qn, _ = orc.row_norms(q)
+    inn, _ = orc.row_norms(items)
+    dq, di = dense64(q), dense64(items)
+    qh = np.where(qn[:, None] > 0, dq / np.where(qn > 0, qn, 1.0)[:, None], 0.0)
+    ih = np.where(inn[:, None] > 0, di / np.where(inn > 0, inn, 1.0)[:, None], 0.0)
+
+    def mask(m, nrm):
+        z = np.zeros((m.n_rows, m.n_cols))
+        for r in range(m.n_rows):
+            if nrm[r] > 0:
+                z[r, m.indices[m.indptr[r]:m.indptr[r + 1]]] = 1.0
+        return z
+    A = np.abs(qh) @ np.abs(ih).T
+    M = mask(q, qn) @ mask(items, inn).T
+    rs1 = orc.chunk_row_sums(q, items, C, kind=1)
+    rs2 = orc.chunk_row_sums(q, items, C, kind=2)
+    for c in range(3):
+        b, e = c * C, min((c + 1) * C, items.n_rows)
+        assert np.abs(rs1[c] - A[:, b:e].sum(1)).max() <= 1e-9
+        assert np.array_equal(rs2[c], M[:, b:e].sum(1))
+    assert np.abs(orc.col_sums(q, items, 100, 900, kind=1) - A[:, 100:900].sum(0)).max() <= 1e-9
+    assert np.array_equal(orc.col_sums(q, items, 100, 900, kind=2), M[:, 100:900].sum(0))
+    # |S| <= the absolute sum (termwise), with equality for the non-negative pairs
+    assert np.all(np.abs(S) <= A + 1e-12)
 
 
 ALL_PINS = [pin_worked_examples, pin_bruteforce, pin_scipy, pin_invariants, pin_csc,

@@ -18,6 +18,25 @@ pytestmark = pytest.mark.gpu
 TOL = 1e-5
 SLICE_MAX = 1024  # items per slice at most (the prepare call's slice rule)
 
+# Per-score rounding budget of the GPU path (derived in the design notes, §4):
+#   |S_gpu - S| <= EPS_ABS * A + EPS_TERM * (m + 1)
+# with A = sum_d |q^_d i^_d| over the shared dims, m their number, u = 2^-24:
+# inputs rounded once to fp32 (2u), fp32 products (u), the heavy dims' split
+# fp16 (3 * 2^-22 = 12u) and fp32 accumulation over 32 dims (< 32u), the final
+# fp32 conversion (u |S| <= u A): below 49u of A in all; every light product
+# and the dense part are each rounded once to 2^-30 fixed point (2^-31 each).
+# Sums of scores add the per-score bounds, whose sums over a chunk row or an
+# item column are closed forms of the oracle (kinds 1 and 2); float64 summation
+# adds far less than FP64_SLACK.
+EPS_ABS = 49.0 * 2.0 ** -24
+EPS_TERM = 2.0 ** -31
+FP64_SLACK = 1e-7
+
+
+def sum_bar(abs_sums, counts, n_terms):
+    """Bound on |sum of GPU scores - sum of exact scores| over n_terms pairs."""
+    return EPS_ABS * abs_sums + EPS_TERM * (counts + n_terms) + FP64_SLACK
+
 
 @pytest.fixture(scope="module")
 def env():
@@ -59,12 +78,12 @@ def gpu_chunks(env, q, items, chunk_size, rows=None, sums=False):
 # norms and inverted lists: bit-exact
 # ---------------------------------------------------------------------------
 
-def _check_structures(env, orc, items, chunk_size, name):
+def _check_structures(env, orc, items, chunk_size, name, slices=None):
     torch, sps, dev = env
     n64, inv32 = orc.row_norms(items)
     it = sps.prepare(sps.CSR.from_host(items, dev), chunk_size=chunk_size)
     assert it.slices_per_chunk == -(-chunk_size // SLICE_MAX)
-    for sl in range(it.num_slices):
+    for sl in (range(it.num_slices) if slices is None else slices(it)):
         v = it.slice_view(sl)
         b = v["item_begin"]
         e = b + v["slice_len"]
@@ -80,11 +99,13 @@ def _check_structures(env, orc, items, chunk_size, name):
         assert np.array_equal(g_val.view(np.uint32), val.view(np.uint32)), (name, sl, "values")
         g_inv = v["item_inv_norm"].cpu().numpy()
         assert np.array_equal(g_inv.view(np.uint32), inv32[b:e].view(np.uint32)), (name, sl)
-    # the slices tile every chunk in order
-    ends = [it.slice_view(sl)["item_begin"] + it.slice_view(sl)["slice_len"]
-            for sl in range(it.num_slices)]
-    assert max(ends) == items.n_rows
-    print("\n[parity] %s: %d slices, inverted lists + norms bit-exact" % (name, it.num_slices),
+    if slices is None:
+        # the slices tile every chunk in order
+        ends = [it.slice_view(sl)["item_begin"] + it.slice_view(sl)["slice_len"]
+                for sl in range(it.num_slices)]
+        assert max(ends) == items.n_rows
+    n_checked = it.num_slices if slices is None else len(list(slices(it)))
+    print("\n[parity] %s: %d slices, inverted lists + norms bit-exact" % (name, n_checked),
           file=sys.stderr, flush=True)
     return it
 
@@ -104,6 +125,25 @@ def test_structures_dense_and_edge(env, orc):
     _check_structures(env, orc, items, 8192, "dense 20000 items")
     _, items, _ = synth.make_workload("edge", n_item=17000)
     _check_structures(env, orc, items, 8192, "edge 17000 items (empty rows, signed)")
+
+
+@pytest.mark.parametrize("name", ["pages", "dense", "edge"])
+def test_structures_full_size_sample(env, orc, name):
+    """Bit-exact inverted lists on a seeded sample of the full-size corpora's
+    slices: the first and last slice, every slice of the last (partial) chunk,
+    and 16 random others."""
+    w = synth.WORKLOADS[name]
+    _, items, _ = synth.make_workload(name)
+
+    def pick(it):
+        spc = it.slices_per_chunk
+        rng = np.random.default_rng(4321)
+        chosen = {0, it.num_slices - 1}
+        chosen |= set(range((it.num_chunks - 1) * spc, it.num_slices))
+        chosen |= set(rng.choice(it.num_slices, 16, replace=False).tolist())
+        return sorted(chosen)
+    _check_structures(env, orc, items, w.chunk_size, "%s full size, sampled slices" % name,
+                      slices=pick)
 
 
 def test_query_inverse_norms(env, orc):
@@ -152,7 +192,7 @@ def test_scores_mid_full(env, orc):
 # every chunk (the sums of the exact scores, by linearity)
 # ---------------------------------------------------------------------------
 
-def _sampled(env, orc, name, n_rows_sampled, self_scores=False):
+def _sampled(env, orc, name, n_rows_sampled, self_scores=False, col_chunks=()):
     w = synth.WORKLOADS[name]
     q, items, extra = synth.make_workload(name)
     rng = np.random.default_rng(1234)
@@ -160,6 +200,10 @@ def _sampled(env, orc, name, n_rows_sampled, self_scores=False):
     qn, _ = orc.row_norms(q)
     inn, _ = orc.row_norms(items)
     ref_sums = orc.chunk_row_sums(q, items, w.chunk_size, q_norm=qn, i_norm=inn)
+    abs_sums = orc.chunk_row_sums(q, items, w.chunk_size, q_norm=qn, i_norm=inn, kind=1)
+    cnt_sums = orc.chunk_row_sums(q, items, w.chunk_size, q_norm=qn, i_norm=inn, kind=2)
+    max_abs = 0.0  # largest |S| over the whole matrix
+    col_worst = 0.0  # largest column-sum error / its bar
     worst, worst_sum, n = 0.0, 0.0, 0
     self_err = 0.0
     torch, sps, dev = env
@@ -178,6 +222,19 @@ def _sampled(env, orc, name, n_rows_sampled, self_scores=False):
         n_c = it.chunk_len(c)
         b = c * w.chunk_size
         got_rows[:, b:b + n_c] = out[sel, :n_c].cpu().numpy()
+        max_abs = max(max_abs, float(out[:, :n_c].abs().max().item()))
+        if c in col_chunks:
+            g_col = out[:, :n_c].double().sum(0).cpu().numpy()
+            r_col = orc.col_sums(q, items, b, b + n_c, q_norm=qn, i_norm=inn)
+            bar = sum_bar(orc.col_sums(q, items, b, b + n_c, q_norm=qn, i_norm=inn, kind=1),
+                          orc.col_sums(q, items, b, b + n_c, q_norm=qn, i_norm=inn, kind=2),
+                          q.n_rows)
+            e_col = np.abs(g_col - r_col)
+            report("%s column sums, chunk %d (%d items); worst err/bar %.3f" % (
+                name, c, n_c, float((e_col / bar).max())), float(e_col.max()), n_c,
+                bar=float(bar[np.argmax(e_col)]))
+            assert np.all(e_col <= bar), (c, int(np.argmax(e_col - bar)))
+            col_worst = max(col_worst, float((e_col / bar).max()))
         if self_scores:
             inside = np.nonzero((perm >= b) & (perm < b + n_c))[0]
             if len(inside):
@@ -189,13 +246,23 @@ def _sampled(env, orc, name, n_rows_sampled, self_scores=False):
     worst = float(np.abs(got_rows - ref).max())
     n = got_rows.size
     g_sums = rs.cpu().numpy()
-    worst_sum = float(np.abs(g_sums - ref_sums).max())
-    # each row sum adds at most chunk_len fp32 errors of the scores
+    e_sums = np.abs(g_sums - ref_sums)
+    worst_sum = float(e_sums.max())
+    chunk_lens = np.array([it.chunk_len(c) for c in range(it.num_chunks)], dtype=np.float64)
+    bars = sum_bar(abs_sums, cnt_sums, chunk_lens[:, None])
     report("%s %d sampled rows x all items" % (name, len(rows)), worst, n)
-    report("%s row sums, %d chunks x %d rows" % (name, it.num_chunks, q.n_rows), worst_sum,
-           it.num_chunks * q.n_rows, bar=TOL * w.chunk_size)
+    err_all = np.abs(got_rows - ref)
+    within = float((err_all <= 1e-6).mean())
+    report("%s share of compared scores within 1e-6: %.6f" % (name, within), worst, n, bar=1e-6)
+    report("%s max |S| over all %d scores: excess over 1 = %.3g" % (
+        name, q.n_rows * items.n_rows, max(0.0, max_abs - 1.0)), max(0.0, max_abs - 1.0),
+        q.n_rows * items.n_rows)
+    report("%s row sums, %d chunks x %d rows; worst err/bar %.3f" % (
+        name, it.num_chunks, q.n_rows, float((e_sums / bars).max())), worst_sum,
+        it.num_chunks * q.n_rows, bar=float(bars.flat[np.argmax(e_sums)]))
     assert worst <= TOL
-    assert worst_sum <= TOL * w.chunk_size
+    assert max_abs <= 1.0 + TOL  # no clamp; |S| <= 1 up to rounding
+    assert np.all(e_sums <= bars), np.unravel_index(int(np.argmax(e_sums - bars)), bars.shape)
     if self_scores:
         empty = np.diff(q.indptr) == 0
         self_err = float(np.abs(self_vals[~empty] - 1.0).max())
@@ -206,15 +273,15 @@ def _sampled(env, orc, name, n_rows_sampled, self_scores=False):
 
 
 def test_pages_shape_sampled(env, orc):
-    _sampled(env, orc, "pages", 64)
+    _sampled(env, orc, "pages", 64, col_chunks=(0, 122, 244))
 
 
 def test_dense_overlap_sampled(env, orc):
-    _sampled(env, orc, "dense", 128)
+    _sampled(env, orc, "dense", 128, col_chunks=(0, 61))
 
 
 def test_edge_heavy_tail_sampled(env, orc):
-    _sampled(env, orc, "edge", 128, self_scores=True)
+    _sampled(env, orc, "edge", 128, self_scores=True, col_chunks=(0, 122))
 
 
 # ---------------------------------------------------------------------------
@@ -286,6 +353,35 @@ def test_row_permutation_invariance(env):
     report("mid 203x12000 rows shuffled: bitwise equal", 0.0, a.size)
 
 
+def test_group_first_batch_misses_slice(env, orc):
+    """One 16-row group with more than 1024 light entries (two batches; such a
+    group keeps its records in row order): every entry of the first batch is a
+    dim no item holds, so that batch has no segments, and the second batch's
+    entries share dims with the slice. Scores must match the oracle."""
+    from synth import HostCSR
+    rng = np.random.default_rng(5)
+    _, items, _ = synth.make_workload("mid", n_item=2048)
+    dim_hi = items.n_cols  # query dims >= this are absent from every item
+    D = dim_hi + 100000
+    rows = []
+    for r in range(15):
+        d = np.sort(rng.choice(np.arange(dim_hi, D), 70, replace=False))
+        rows.append(list(zip(d.tolist(), rng.lognormal(0, 1, 70).astype(np.float32).tolist())))
+    present = np.unique(items.indices)
+    d = np.sort(rng.choice(present, 60, replace=False))
+    rows.append(list(zip(d.tolist(), rng.lognormal(0, 1, 60).astype(np.float32).tolist())))
+    import pins
+    q = pins.csr_from_rows(rows, D)
+    items_d = HostCSR(items.indptr, items.indices, items.values, items.n_rows, D)
+    assert q.nnz > 1024 + 40
+    ref = orc.scores(q, items_d)
+    got = np.concatenate([g for _, _, g, _ in gpu_chunks(env, q, items_d, 1024)], axis=1)
+    err = float(np.abs(got - ref).max())
+    report("16x2048: first batch of the group misses every slice", err, got.size)
+    assert err <= TOL
+    assert np.abs(got[15]).max() > 0.01  # the second batch did contribute
+
+
 def test_edge_rows_and_ld(env, orc):
     """Empty rows on both sides, explicit zeros, a dim no item has, a chunk
     length that is not a multiple of 4, ld > chunk_len (the tail untouched)."""
@@ -344,11 +440,13 @@ def test_chunk_size_extremes(env, orc):
 
 
 def test_chunk_size_invariance(env):
-    """Scores with 4096-item and 8192-item chunks agree (to fp32 accumulation order)."""
+    """Scores with 4096-item and 8192-item chunks are bitwise equal: both cut the
+    items into the same 1024-item slices, pick the same heavy dims, and the
+    light sums are integers."""
     q, items, _ = synth.make_workload("mid", n_item=16384, n_query=200)
     a = np.concatenate([g for _, _, g, _ in gpu_chunks(env, q, items, 4096)], axis=1)
     b = np.concatenate([g for _, _, g, _ in gpu_chunks(env, q, items, 8192)], axis=1)
-    assert np.abs(a - b).max() <= 2e-6
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
 
 
 def test_stream_entry_and_bulk(env, orc):

@@ -19,6 +19,7 @@ MUTANTS = {
     6: "transpose stores global instead of chunk-local item ids",
     7: "row checksum uses raw instead of normalised query values",
     8: "merge multiplies the query value by itself (wrong operand)",
+    9: "absolute-value closed form keeps the sign",
 }
 
 
