@@ -226,6 +226,22 @@ void sps_queries_destroy(sps_queries *q);
 sps_status sps_cosine_chunk(const sps_queries *q, const sps_items *items, int32_t chunk,
                             float *out, int64_t ld_out, double *row_sums, void *stream);
 
+/* sps_cosine_chunk for callers that cannot allocate device memory, or would
+ * rather not keep a per-batch partial-row-sum buffer in use (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc). Same
+ * arguments, results and errors as sps_cosine_chunk, bit for bit; the only
+ * difference is where the per-slice partial row sums live (chunk_size above
+ * 1024 with row_sums != NULL): in a 4 MiB static device array that the
+ * library holds on each GPU it runs on until the process ends, instead of
+ * the query batch's workspace. Nothing is allocated by this call. Limit:
+ * n_rows * ceil(chunk_size / 1024) <= 524288 when row_sums is given
+ * (SPS_ERR_UNSUPPORTED otherwise). All calls of it on one GPU share that
+ * array: calls that overlap on one GPU (on different streams, or from
+ * several threads without ordering) race and their row sums are
+ * unspecified; calls ordered on one stream are fine. */
+sps_status sps_cosine_chunk_static(const sps_queries *q, const sps_items *items, int32_t chunk,
+                                   float *out, int64_t ld_out, double *row_sums, void *stream);
+
 /* Score chunks [chunk_begin, chunk_end) one after another into the same
  * rotating buffer `out` (the streaming loop of §2.2 and §4.4 with the chunk
  * output kept on the device). row_sums (nullable): DEVICE

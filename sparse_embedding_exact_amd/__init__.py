@@ -87,6 +87,7 @@ SIGNATURES = {
     "sps_queries_inv_norms": (_I32, [_P, ctypes.POINTER(_P)]),
     "sps_queries_destroy": (None, [_P]),
     "sps_cosine_chunk": (_I32, [_P, _P, _I32, _P, _I64, _P, _P]),
+    "sps_cosine_chunk_static": (_I32, [_P, _P, _I32, _P, _I64, _P, _P]),
     "sps_cosine_stream": (_I32, [_P, _P, _I32, _I32, _P, _I64, _P, _P]),
     "sps_cosine_stream_host": (_I32, [_P, _P, _I32, _I32, _P, _I64, _P, _P, _I64, _P, _P, _P]),
     "sps_cosine_chunk_threshold": (_I32, [_P, _P, _I32, ctypes.c_float, _P, _I64, _P, _P, _P]),
@@ -419,6 +420,18 @@ def cosine_chunk(q: Queries, items: Items, chunk: int, out: torch.Tensor,
         assert row_sums.numel() >= q.n_rows
     _check(_lib.sps_cosine_chunk(q._h, items._h, chunk, out.data_ptr(), ld, rs,
                                  _stream_ptr(stream)))
+
+
+def cosine_chunk_static(q: Queries, items: Items, chunk: int, out: torch.Tensor,
+                        row_sums: torch.Tensor | None = None, stream=None) -> None:
+    """cosine_chunk with the partial row sums in the library's static device scratch
+    (no allocation; calls overlapping on one GPU race)."""
+    ld, rs = _out_args(q, out, row_sums)
+    assert out.shape[1] >= items.chunk_len(chunk)
+    if row_sums is not None:
+        assert row_sums.numel() >= q.n_rows
+    _check(_lib.sps_cosine_chunk_static(q._h, items._h, chunk, out.data_ptr(), ld, rs,
+                                        _stream_ptr(stream)))
 
 
 def cosine_chunk_half(q: Queries, items: Items, chunk: int, out: torch.Tensor,

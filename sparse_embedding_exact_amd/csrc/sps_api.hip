@@ -7,10 +7,19 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 
 #include "sps.h"
 #include "sps_internal.h"
+
+// Device scratch of sps_cosine_chunk_static: the per-slice partial row sums,
+// held by the library on every GPU it runs on until the process ends. Host
+// code must never use this name as a device address (in host code it is a
+// host-side stand-in): the device address comes from hipGetSymbolAddress,
+// once per device (scratch_address below).
+constexpr int64_t kStaticScratchDoubles = 1 << 19;  // 4 MiB
+static __device__ __align__(256) double scratch[kStaticScratchDoubles];
 
 namespace {
 
@@ -61,6 +70,30 @@ sps_status check_csr_shape(const sps_csr *m, const char *what) {
   if (!m->indptr) return fail(SPS_ERR_INVALID_ARGUMENT, "%s: NULL indptr", what);
   if (m->nnz > 0 && (!m->indices || !m->values))
     return fail(SPS_ERR_INVALID_ARGUMENT, "%s: NULL indices or values", what);
+  return SPS_OK;
+}
+
+// The device address of `scratch` on the current device, looked up on the
+// first call on each device and kept (each GPU holds its own copy).
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_addr[kMaxDevices];
+
+sps_status scratch_address(double **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(SPS_ERR_UNSUPPORTED, "device %d beyond the %d this library tracks", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_addr[dev] == nullptr) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    g_scratch_addr[dev] = p;
+  }
+  *out = static_cast<double *>(g_scratch_addr[dev]);
   return SPS_OK;
 }
 
@@ -457,7 +490,8 @@ static sps_status check_score_args(const sps_queries *q, const sps_items *items,
 
 static sps_status score_one(const sps_queries *q, const sps_items *items, int32_t chunk,
                             sps::ScoreMode mode, float *out, uint16_t *out16, int64_t ld_out,
-                            double *row_sums, hipStream_t s, const sps::ScoreArgs *extra = nullptr) {
+                            double *row_sums, hipStream_t s, const sps::ScoreArgs *extra = nullptr,
+                            double *rs_part = nullptr) {
   sps::ScoreArgs a{};
   if (extra) a = *extra;
   a.mode = mode;
@@ -481,7 +515,7 @@ static sps_status score_one(const sps_queries *q, const sps_items *items, int32_
   a.out = out;
   a.out16 = out16;
   a.ld = ld_out;
-  a.rs_part = q->rs_part;
+  a.rs_part = rs_part != nullptr ? rs_part : q->rs_part;
   a.row_sums = row_sums;
   const hipError_t e = sps::launch_score(a, s);
   if (e != hipSuccess) return hip_fail(e, "score kernel");
@@ -496,6 +530,28 @@ sps_status sps_cosine_chunk(const sps_queries *q, const sps_items *items, int32_
     return fail(SPS_ERR_CHUNK_RANGE, "chunk %d outside [0, %d)", chunk, items->g.num_chunks);
   return score_one(q, items, chunk, sps::kModeExact, out, nullptr, ld_out, row_sums,
                    reinterpret_cast<hipStream_t>(stream));
+}
+
+sps_status sps_cosine_chunk_static(const sps_queries *q, const sps_items *items, int32_t chunk,
+                                   float *out, int64_t ld_out, double *row_sums, void *stream) {
+  sps_status st = check_score_args(q, items, out, ld_out);
+  if (st != SPS_OK) return st;
+  if (chunk < 0 || chunk >= items->g.num_chunks)
+    return fail(SPS_ERR_CHUNK_RANGE, "chunk %d outside [0, %d)", chunk, items->g.num_chunks);
+  double *part = nullptr;
+  if (row_sums != nullptr && items->g.n_sub > 1) {
+    const int64_t need = (int64_t)items->g.n_sub * q->n_rows;
+    if (need > kStaticScratchDoubles)
+      return fail(SPS_ERR_UNSUPPORTED,
+                  "row sums of %lld rows x %d slices need %lld doubles of scratch; the "
+                  "library's static scratch holds %lld (use sps_cosine_chunk)",
+                  (long long)q->n_rows, items->g.n_sub, (long long)need,
+                  (long long)kStaticScratchDoubles);
+    st = scratch_address(&part);
+    if (st != SPS_OK) return st;
+  }
+  return score_one(q, items, chunk, sps::kModeExact, out, nullptr, ld_out, row_sums,
+                   reinterpret_cast<hipStream_t>(stream), nullptr, part);
 }
 
 sps_status sps_cosine_chunk_threshold(const sps_queries *q, const sps_items *items, int32_t chunk,
