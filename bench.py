@@ -55,6 +55,12 @@ def parse():
                          "variant's timing (0 skips it)")
     ap.add_argument("--no-bsc", action="store_true",
                     help="skip the Block-Sparse CSR codec's timing")
+    ap.add_argument("--configs", default="tiny,mid,dense,edge",
+                    help="other workloads whose score launches are timed and reported under "
+                         "variants.configs (comma list; '' skips)")
+    ap.add_argument("--no-dense-ab", action="store_true",
+                    help="skip the timing of the path with the heavy-dim matrix-core part off "
+                         "(SPS_DENSE=0) on pages and dense")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles",
                                                       "score_kernel_pages_traffic.txt"),
                     help="measured HBM bytes per score launch (rocprofv3 FETCH_SIZE / "
@@ -100,6 +106,51 @@ def measured_traffic(path, workload):
         return float(kv["bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def host_cpus():
+    """CPU model, the affinity mask, this process's CPU share (cgroup quota, and
+    OMP_NUM_THREADS where the job sets it), and the cores one pinned thread each
+    should use: the first `share` cores of the mask."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    mask = sorted(os.sched_getaffinity(0))
+    quota = None
+    for path, parse_q in (("/sys/fs/cgroup/cpu.max", lambda t: t.split()),
+                          ("/sys/fs/cgroup/cpu/cpu.cfs_quota_us", None)):
+        try:
+            with open(path) as f:
+                txt = f.read().strip()
+        except OSError:
+            continue
+        if parse_q is not None:
+            q, per = parse_q(txt)
+            if q != "max":
+                quota = max(1, int(int(q) // int(per)))
+        else:
+            try:
+                with open("/sys/fs/cgroup/cpu/cpu.cfs_period_us") as f:
+                    per = int(f.read())
+                if int(txt) > 0:
+                    quota = max(1, int(txt) // per)
+            except (OSError, ValueError):
+                pass
+        break
+    omp = os.environ.get("OMP_NUM_THREADS")
+    share = len(mask)
+    if quota:
+        share = min(share, quota)
+    if omp and omp.isdigit() and int(omp) > 0:
+        share = min(share, int(omp))
+    return {"cpu_model": model, "affinity_cores": len(mask), "cgroup_cpu_quota": quota,
+            "omp_num_threads": omp, "cores_used": mask[:share]}
 
 
 def main():
@@ -183,19 +234,24 @@ def main():
         kern = np.zeros(n_chunks)
         prep = 0.0
         keep = []
+        per_step = []
         t0 = time.perf_counter()
         for _ in range(args.steps):
+            ts = time.perf_counter()
             keep.append(step(True))
             torch.cuda.synchronize()  # events of this step are read before the next records them
+            per_step.append(time.perf_counter() - ts)
             kern += np.array([a.elapsed_time(b) for a, b in ev])
             prep += ev_prep[0].elapsed_time(ev_prep[1])
             keep.clear()
         torch.cuda.synchronize()
+        run_timed.median_ms = 1e3 * float(np.median(per_step))
         return time.perf_counter() - t0, kern / args.steps, prep / args.steps
 
     t_total, kern_ms, prep_ms = run_timed(
         make_step(lambda qq, it, c: sps.cosine_chunk(qq, it, c, out, sums[c])))
     ms_per_step = 1e3 * t_total / args.steps
+    median_step_ms = run_timed.median_ms
     scores = float(n_q) * float(n_i)
     value = scores * args.steps / t_total
 
@@ -340,22 +396,126 @@ def main():
         log("bsc: %.3f index bytes per entry (CSR 4), encode %.1f ms, decode %.3f ms" %
             (bscv["index_bytes_per_entry"], enc_ms, dec_ms))
 
+    # ---- other workloads: every chunk's score launch, events around each ----
+    def time_chunks(qh, ih, C, reps=2, dense=None):
+        """Prepare once (optionally with the heavy-dim part forced on or off), then time
+        each chunk's score launch: per-launch ms (mean of `reps` passes after a warm-up
+        pass), prepare ms, algorithmic bytes per launch."""
+        old = os.environ.get("SPS_DENSE")
+        if dense is not None:
+            os.environ["SPS_DENSE"] = "1" if dense else "0"
+        try:
+            ci, cq = sps.CSR.from_host(ih, dev), sps.CSR.from_host(qh, dev)
+            p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            p0.record(stream)
+            it = sps.prepare(ci, chunk_size=C)
+            qq = sps.prepare_queries(cq, it)
+            p1.record(stream)
+        finally:
+            if old is None:
+                os.environ.pop("SPS_DENSE", None)
+            else:
+                os.environ["SPS_DENSE"] = old
+        nch = it.num_chunks
+        o = torch.empty(qh.n_rows, min(C, ih.n_rows), dtype=torch.float32, device=dev)
+        rs = torch.empty(qh.n_rows, dtype=torch.float64, device=dev)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(nch)]
+        for c in range(nch):
+            sps.cosine_chunk(qq, it, c, o, rs)
+        torch.cuda.synchronize()
+        prep = p0.elapsed_time(p1)
+        kern = np.zeros(nch)
+        for _ in range(reps):
+            for c in range(nch):
+                evs[c][0].record(stream)
+                sps.cosine_chunk(qq, it, c, o, rs)
+                evs[c][1].record(stream)
+            torch.cuda.synchronize()
+            kern += np.array([x.elapsed_time(y) for x, y in evs])
+        clen = np.minimum(C, ih.n_rows - np.arange(nch) * C)
+        cnnz = np.diff(ih.indptr[np.minimum(np.arange(nch + 1) * C, ih.n_rows)])
+        alg = 4.0 * qh.n_rows * clen + 8.0 * cnnz + 8.0 * qh.n_rows
+        del it, qq, ci, cq, o, rs
+        return kern / reps, prep, alg
+
+    def summary(kern, prep, alg, nq, ni):
+        avg = float(kern.mean())
+        ach = float(alg.mean()) / (avg * 1e-3) / 1e9
+        return {"scores": float(nq) * ni, "chunks": int(len(kern)), "ms_per_launch": avg,
+                "score_loop_ms": float(kern.sum()), "prepare_ms": prep,
+                "scores_per_s": float(nq) * ni / (float(kern.sum()) * 1e-3),
+                "alg_bytes_per_launch": float(alg.mean()),
+                "floor_ms_per_launch": float(alg.mean()) / (HBM_PEAK_GBPS * 1e9) * 1e3,
+                "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBPS,
+                             "unit": "GB/s", "frac": ach / HBM_PEAK_GBPS}}
+
+    configs = {}
+    for name in [x for x in args.configs.split(",") if x and x != w.name]:
+        wc = synth.WORKLOADS[name]
+        qc, ic, _ = synth.make_workload(wc)
+        k, pr, al = time_chunks(qc, ic, wc.chunk_size)
+        configs[name] = summary(k, pr, al, qc.n_rows, ic.n_rows)
+        configs[name]["workload"] = "%s: %s" % (wc.name, wc.description)
+        log("config %s: %d launches, avg %.4f ms (%.1f%% of the HBM roofline), prepare %.2f ms"
+            % (name, len(k), k.mean(), 100 * configs[name]["roofline"]["frac"], pr))
+        if name == "dense" and not args.no_dense_ab:
+            k0, pr0, al0 = time_chunks(qc, ic, wc.chunk_size, dense=False)
+            configs[name]["heavy_dims_off"] = summary(k0, pr0, al0, qc.n_rows, ic.n_rows)
+            log("config dense, heavy-dim part off: avg %.4f ms" % k0.mean())
+        del qc, ic
+    dense_ab = None
+    if not args.no_dense_ab:
+        k1, pr1, al1 = time_chunks(q_host, i_host, C, dense=True)
+        k0, pr0, al0 = time_chunks(q_host, i_host, C, dense=False)
+        dense_ab = {"on": summary(k1, pr1, al1, n_q, n_i), "off": summary(k0, pr0, al0, n_q, n_i),
+                    "note": "same workload, prepared with the heavy-dim matrix-core part on "
+                            "(default) and off (SPS_DENSE=0: every dim through the inverted "
+                            "lists)"}
+        log("%s heavy-dim part on/off: avg launch %.4f / %.4f ms" % (w.name, k1.mean(),
+                                                                    k0.mean()))
+
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
         o = oracle.default()
-        nthreads = max(1, min(len(os.sched_getaffinity(0)), 16))
+        hc = host_cpus()
+        pin = hc["cores_used"]
+        nthreads = len(pin)
+
+        def oracle_rate(qh, ih, rows=None):
+            qn, _ = o.row_norms(qh)
+            inn, _ = o.row_norms(ih)
+            t = time.perf_counter()
+            o.scores(qh, ih, q_norm=qn, i_norm=inn, q_rows=rows, n_threads=nthreads,
+                     pin_cpus=pin)
+            dt = time.perf_counter() - t
+            pairs = (qh.n_rows if rows is None else len(rows)) * float(ih.n_rows)
+            return pairs / dt, dt, pairs
+
+        full = {}
+        for name in ("tiny", "mid"):
+            qc, ic, _ = synth.make_workload(name)
+            r, dt, pairs = oracle_rate(qc, ic)
+            full[name] = {"scores_per_s": r, "seconds": dt, "pairs": pairs}
+            del qc, ic
         rows = np.arange(min(args.cpu_rows, n_q))
-        qn, _ = o.row_norms(q_host)
-        inn, _ = o.row_norms(i_host)
-        t = time.perf_counter()
-        o.scores(q_host, i_host, q_norm=qn, i_norm=inn, q_rows=rows, n_threads=nthreads)
-        dt = time.perf_counter() - t
-        cpu = {"value": len(rows) * float(n_i) / dt, "unit": "scores/s", "cores": nthreads,
-               "kind": "oracle",
-               "sample": "%d query rows x all %d items (%.3g pairs), float64 two-pointer "
-                         "merge, %.1f s wall" % (len(rows), n_i, len(rows) * float(n_i), dt)}
-        log("cpu oracle: %.3g scores/s on %d threads" % (cpu["value"], nthreads))
+        r, dt, pairs = oracle_rate(q_host, i_host, rows)
+        cpu = {"value": r, "unit": "scores/s", "cores": nthreads, "kind": "oracle",
+               "sample": "%d query rows x all %d items (%.3g pairs) of the %s workload, float64 "
+                         "two-pointer merge, %.1f s wall" % (len(rows), n_i, pairs, w.name, dt),
+               "threads_pinned": True, "cpu_model": hc["cpu_model"],
+               "affinity_cores": hc["affinity_cores"], "cgroup_cpu_quota": hc["cgroup_cpu_quota"],
+               "omp_num_threads": hc["omp_num_threads"],
+               "full_runs": full,
+               "extrapolated_whole_run_s": float(n_q) * n_i / r,
+               "extrapolated_note": "EXTRAPOLATED, not measured: n_query x n_item / the sampled "
+                                    "rate"}
+        log("cpu oracle: %.3g scores/s on %d pinned threads (%s; mask %d cores); full tiny %.3g, "
+            "mid %.3g scores/s; whole %s run extrapolated to %.0f s" % (
+                r, nthreads, hc["cpu_model"], hc["affinity_cores"],
+                full["tiny"]["scores_per_s"], full["mid"]["scores_per_s"], w.name,
+                cpu["extrapolated_whole_run_s"]))
 
     res = {
         "metric": "cosine scores/sec + achieved HBM GB/s vs peak, 50k q x 2M items, nnz~43",
@@ -368,7 +528,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f32 (light dims: fp32 products into int32 fixed point; heavy dims: split-fp16 "
+                 "matrix cores, fp32 accumulation)",
         "data": "synthetic (seeded Philox CSR shaped like the page's workload)",
         "config": {"workload": "%s: %s" % (w.name, w.description), "n_query": n_q,
                    "n_item": n_i, "dim": w.dim, "chunk_size": C, "chunks": n_chunks,
@@ -377,11 +538,14 @@ def main():
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic},
         "cpu_baseline": cpu,
         "breakdown_ms": {"prepare": prep_ms, "score_loop": loop_ms,
-                         "score_launch_avg": avg_launch_ms},
+                         "score_launch_avg": avg_launch_ms,
+                         "score_launch_median": float(np.median(kern_ms)),
+                         "step_median": median_step_ms},
         "step_hbm_gbps_algorithmic": float(alg_bytes.sum()) / (ms_per_step * 1e-3) / 1e9,
         "write_ceiling_gbps": write_ceiling,
         "frac_of_write_ceiling": achieved / write_ceiling,
-        "variants": {"fp16": half, "threshold": thr, "host_stream": host, "bsc": bscv},
+        "variants": {"fp16": half, "threshold": thr, "host_stream": host, "bsc": bscv,
+                     "configs": configs, "heavy_dims_on_off": dense_ab},
     }
     print(json.dumps(res), flush=True)
 

@@ -82,6 +82,8 @@ class Oracle:
         L.orc_scores.restype = None
         L.orc_scores.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P,
                                  ctypes.c_int]
+        L.orc_set_thread_cpus.restype = None
+        L.orc_set_thread_cpus.argtypes = [_P, ctypes.c_int]
         L.orc_chunk_row_sums.restype = None
         L.orc_chunk_row_sums.argtypes = [_P, _P, _P, _P, _I64, _P, _P, _P, _P, _I64, _I64,
                                          _I64, _P, ctypes.c_int, ctypes.c_int]
@@ -130,8 +132,12 @@ class Oracle:
 
     # -- scores -----------------------------------------------------------
     def scores(self, queries, items, q_norm=None, i_norm=None, q_rows=None,
-               item_begin: int = 0, item_end: int | None = None, n_threads: int | None = None):
-        """float64 S[q_rows x items[item_begin:item_end]] by per-pair merge."""
+               item_begin: int = 0, item_end: int | None = None, n_threads: int | None = None,
+               pin_cpus=None):
+        """float64 S[q_rows x items[item_begin:item_end]] by per-pair merge.
+
+        pin_cpus: optional CPU ids; thread t (the caller is thread 0) then runs on
+        pin_cpus[t % len(pin_cpus)] (placement only, for timing)."""
         if q_norm is None:
             q_norm = self.row_norms(queries)[0]
         if i_norm is None:
@@ -152,10 +158,17 @@ class Oracle:
             rows_p = rows.ctypes.data
             n_sel = len(rows)
         out = np.empty((n_sel, item_end - item_begin), dtype=np.float64)
-        self.L.orc_scores(qip.ctypes.data, qix.ctypes.data, qv.ctypes.data, qn.ctypes.data,
-                          iip.ctypes.data, iix.ctypes.data, iv.ctypes.data, inn.ctypes.data,
-                          rows_p, n_sel, item_begin, item_end, out.ctypes.data,
-                          n_threads or _threads())
+        cpus = None if not pin_cpus else _a(list(pin_cpus), np.int32)
+        if cpus is not None:
+            self.L.orc_set_thread_cpus(cpus.ctypes.data, len(cpus))
+        try:
+            self.L.orc_scores(qip.ctypes.data, qix.ctypes.data, qv.ctypes.data, qn.ctypes.data,
+                              iip.ctypes.data, iix.ctypes.data, iv.ctypes.data, inn.ctypes.data,
+                              rows_p, n_sel, item_begin, item_end, out.ctypes.data,
+                              n_threads or _threads())
+        finally:
+            if cpus is not None:
+                self.L.orc_set_thread_cpus(None, 0)
         return out
 
     # -- closed-form checksums -------------------------------------------

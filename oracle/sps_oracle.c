@@ -30,8 +30,10 @@
  * builds those variants to show its pins catch each one. The default build
  * (ORC_MUTANT undefined or 0) is the oracle.
  */
+#define _GNU_SOURCE /* pthread_setaffinity_np */
 #include <math.h>
 #include <pthread.h>
+#include <sched.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -197,6 +199,40 @@ static void *score_worker(void *arg) {
   return NULL;
 }
 
+/* Optional thread placement for orc_scores (timing runs): thread t (the
+ * caller is thread 0) runs on cpus[t % n]; n = 0 leaves placement to the OS.
+ * Placement only; it changes nothing in the arithmetic. */
+static int g_pin_n = 0;
+static int g_pin_cpus[256];
+
+void orc_set_thread_cpus(const int32_t *cpus, int n) {
+  if (n < 0) n = 0;
+  if (n > 256) n = 256;
+  for (int k = 0; k < n; ++k) g_pin_cpus[k] = cpus[k];
+  g_pin_n = n;
+}
+
+static void pin_self(int t) {
+  if (g_pin_n <= 0) return;
+  cpu_set_t set;
+  CPU_ZERO(&set);
+  CPU_SET(g_pin_cpus[t % g_pin_n], &set);
+  pthread_setaffinity_np(pthread_self(), sizeof set, &set);
+}
+
+typedef struct {
+  void *job;
+  int t;
+} pinned_arg;
+
+static void *score_worker(void *arg);
+
+static void *pinned_score_worker(void *arg) {
+  pinned_arg *p = (pinned_arg *)arg;
+  pin_self(p->t);
+  return score_worker(p->job);
+}
+
 /* out[s * (item_end-item_begin) + (i-item_begin)] = S[q_rows[s], i] (q_rows NULL: s) */
 void orc_scores(const int32_t *q_indptr, const int32_t *q_indices, const float *q_values,
                 const double *q_norm, const int32_t *i_indptr, const int32_t *i_indices,
@@ -212,11 +248,20 @@ void orc_scores(const int32_t *q_indptr, const int32_t *q_indices, const float *
   if (n_threads < 1) n_threads = 1;
   if (n_threads > 256) n_threads = 256;
   pthread_t th[256];
+  pinned_arg pa[256];
   int started = 0;
   for (int t = 1; t < n_threads; ++t) {
-    if (pthread_create(&th[started], NULL, score_worker, &J) == 0) ++started;
+    pa[t].job = &J;
+    pa[t].t = t;
+    if (pthread_create(&th[started], NULL, pinned_score_worker, &pa[t]) == 0) ++started;
   }
+  /* the calling thread works too, on cpus[0] when pinned, then gets its placement back */
+  cpu_set_t before;
+  const int restore = g_pin_n > 0 &&
+                      pthread_getaffinity_np(pthread_self(), sizeof before, &before) == 0;
+  pin_self(0);
   score_worker(&J);
+  if (restore) pthread_setaffinity_np(pthread_self(), sizeof before, &before);
   for (int t = 0; t < started; ++t) pthread_join(th[t], NULL);
   pthread_mutex_destroy(&J.mu);
 }
