@@ -116,6 +116,10 @@ def load_library(path: str | None = None):
     global _lib
     if _lib is not None and path is None:
         return _lib
+    # torch ships its own HIP runtime and this library links the system one: the
+    # process holds both, and torch's must initialise the GPU first
+    if torch.cuda.is_available():
+        torch.cuda.init()
     p = path or LIB_PATH
     if not os.path.exists(p):
         from . import _build
