@@ -107,26 +107,33 @@ static_assert(kRows * kSliceMax * 4 < (1 << 27), "row byte offset fits the segme
 // postings, four per lane and load, the slab's hi halves only, fp16 output.
 // kOutThreshold: the exact scores, of which only those >= a.threshold are
 // written, as (row, item, score) hits (see sps_cosine_chunk_threshold).
+// The workgroup's LDS, declared once in the kernel (the body below is
+// instantiated twice in it): the accumulators, the segment table of a round
+// (first posting, query value, and the LDS byte offset of the row << 5 |
+// postings in the segment, 1..16, 0 padding the table past its last
+// segment), the block scan's two buffers, and the threshold epilogue's hits
+// per wave and first hit position.
+struct ScoreLds {
+  int *acc;
+  uint32_t *s_spos, *s_sqv, *s_smeta;
+  int32_t (*ws)[NW];
+  int32_t *s_wtot;
+  unsigned long long *s_hbase;
+};
+
 template <bool DENSE, int MODE>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void score_kernel(
-    const ScoreArgs a, int vec4) {
+__device__ __forceinline__ void score_body(const ScoreArgs &a, int vec4, const ScoreLds &L) {
   constexpr bool HALF = MODE == kOutHalf;
   constexpr int U = 2;                      // segment groups per wave per walk step
   constexpr int PPL = HALF ? 4 : 2;         // postings per lane (one 16-byte load)
   constexpr int LPS = kSeg / PPL;           // lanes per segment
   constexpr int SPI = 64 / LPS;             // segments per wave per load
   static_assert(SPI * NW * U <= kSegPad, "the segment table pads one walk step per wave");
-  extern __shared__ int acc[];
-  // segment table of a round: first posting, query value, and the LDS byte
-  // offset of the row << 5 | postings in the segment (1..16; 0 pads the
-  // table past its last segment)
-  __shared__ uint32_t s_spos[kSegMax + kSegPad], s_sqv[kSegMax + kSegPad],
-      s_smeta[kSegMax + kSegPad];
-  __shared__ int32_t ws[2][NW];
-  // threshold epilogue: hits per wave of the current group, and the group's
-  // first position in the hit buffer
-  __shared__ int32_t s_wtot[NW];
-  __shared__ unsigned long long s_hbase;
+  int *const acc = L.acc;
+  uint32_t *const s_spos = L.s_spos, *const s_sqv = L.s_sqv, *const s_smeta = L.s_smeta;
+  int32_t (*const ws)[NW] = L.ws;
+  int32_t *const s_wtot = L.s_wtot;
+  unsigned long long &s_hbase = *L.s_hbase;
 
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const Geom &g = a.g;
@@ -583,6 +590,22 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void sc
       }
     }
   }
+}
+
+template <bool DENSE, int MODE>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void score_kernel(
+    const ScoreArgs a, int vec4) {
+  extern __shared__ int acc[];
+  __shared__ uint32_t s_spos[kSegMax + kSegPad], s_sqv[kSegMax + kSegPad],
+      s_smeta[kSegMax + kSegPad];
+  __shared__ int32_t ws[2][NW];
+  __shared__ int32_t s_wtot[NW];
+  __shared__ unsigned long long s_hbase;
+  const ScoreLds L{acc, s_spos, s_sqv, s_smeta, ws, s_wtot, &s_hbase};
+  // a corpus with no heavy dims (all its slab rows zero) takes the path
+  // without the dense part; the choice is uniform across the workgroup
+  if (DENSE && a.heavy[kHeavyMax] == 0) score_body<false, MODE>(a, vec4, L);
+  else score_body<DENSE, MODE>(a, vec4, L);
 }
 
 // row_sums[q] = sum over the chunk's slices, in slice order
