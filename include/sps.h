@@ -123,11 +123,17 @@ sps_status sps_prepare(const sps_csr *items, int32_t chunk_size, void *persisten
                        size_t persistent_bytes, void *scratch, size_t scratch_bytes,
                        void *stream, sps_items **out);
 
+/* Sizes of a prepared corpus (pure host): items, dimension, nonzeros, the
+ * chunk size and the number of chunks, ceil(n_items / chunk_size) (the
+ * chunk loop of §4.4 runs over them). Each output pointer is nullable.
+ * Errors: SPS_ERR_INVALID_ARGUMENT for a NULL handle. */
 sps_status sps_items_info(const sps_items *h, int64_t *n_items, int64_t *dim, int64_t *nnz,
                           int32_t *chunk_size, int32_t *num_chunks);
 
-/* Slice geometry (see sps_prepare step 2). Slice s of the corpus is slice
- * s % slices_per_chunk of chunk s / slices_per_chunk. Pure host. */
+/* Slice geometry (see sps_prepare step 2): how each chunk of §4.4 is cut
+ * for the device. Slice s of the corpus is slice s % slices_per_chunk of
+ * chunk s / slices_per_chunk. Pure host; output pointers nullable; errors:
+ * SPS_ERR_INVALID_ARGUMENT for a NULL handle. */
 sps_status sps_items_slices(const sps_items *h, int32_t *slice_size, int32_t *slices_per_chunk,
                             int64_t *num_slices);
 
@@ -167,12 +173,17 @@ sps_status sps_items_slice_view(const sps_items *h, int64_t slice, void *stream,
 sps_status sps_items_slice_col_ptr(const sps_items *h, int64_t slice, int32_t *col_ptr,
                                    int32_t *status, void *stream);
 
-/* The heavy dims chosen by sps_prepare, ascending (SYNCHRONOUS). Writes at
- * most `capacity` dims to `dims` (nullable) and their number to *count
- * (0 when the dense rows are off). */
+/* The heavy dims chosen by sps_prepare, ascending (SYNCHRONOUS: waits for
+ * `stream`, then copies 132 bytes back). The page notes that term ids
+ * cluster in a dictionary prefix (§3.2, Block-Sparse CSR motivation); the
+ * few dims most items hold are scored as dense rows. Writes at most
+ * `capacity` dims to `dims` (host, nullable) and their number to *count
+ * (host; 0 when the dense rows are off or no dim qualifies). Errors:
+ * SPS_ERR_INVALID_ARGUMENT (NULL handle or count), SPS_ERR_HIP. */
 sps_status sps_items_heavy_dims(const sps_items *h, void *stream, int32_t *dims,
                                 int32_t capacity, int32_t *count);
 
+/* Free the host handle (never the caller's workspaces). NULL is ignored. */
 void sps_items_destroy(sps_items *h);
 
 /* ------------------------------------------------------------------ */
@@ -198,9 +209,13 @@ sps_status sps_prepare_queries(const sps_csr *queries, const sps_items *items,
                                void *workspace, size_t workspace_bytes, void *stream,
                                sps_queries **out);
 
-/* DEVICE float[n_rows] inverse norms of a prepared query batch. */
+/* The query batch's inverse norms fl32(1 / ||q||) (§5.2), computed by
+ * sps_prepare_queries: *inv_norm receives a DEVICE float[n_rows] pointer
+ * into the batch's workspace (valid while the workspace is; read it after
+ * the prepare's stream work). Errors: SPS_ERR_INVALID_ARGUMENT (NULL). */
 sps_status sps_queries_inv_norms(const sps_queries *q, const float **inv_norm);
 
+/* Free the host handle (never the caller's workspace). NULL is ignored. */
 void sps_queries_destroy(sps_queries *q);
 
 /* ------------------------------------------------------------------ */
@@ -402,7 +417,8 @@ sps_status sps_bsc_decode(const sps_bsc *b, int32_t *indices, int32_t *status, v
  * (§5.2). */
 sps_status sps_row_inv_norms(const sps_csr *rows, float *inv_norm, void *stream);
 
-/* Full canonical-CSR check (SYNCHRONOUS). scratch: DEVICE, >= 64 bytes.
+/* Full canonical-CSR check (SYNCHRONOUS), the precondition of the page's
+ * merge (§3.1 note: strictly ordered indices). scratch: DEVICE, >= 64 bytes.
  * Returns SPS_OK, or SPS_ERR_BAD_CSR with *first_bad_row (nullable) set to
  * the lowest offending row (0 for a fault in indptr[0] or indptr[n_rows])
  * and *reason (nullable): 1 indptr, 2 order/duplicate, 3 index range,
@@ -410,7 +426,10 @@ sps_status sps_row_inv_norms(const sps_csr *rows, float *inv_norm, void *stream)
 sps_status sps_validate_csr(const sps_csr *m, void *scratch, void *stream,
                             int64_t *first_bad_row, int32_t *reason);
 
+/* A static English name for a status ("unknown status" for other values). */
 const char *sps_status_string(sps_status s);
+/* The detail of the calling thread's last failed call (thread-local; empty
+ * until a call fails; overwritten by the next failure on the thread). */
 const char *sps_last_error_message(void);
 
 #ifdef __cplusplus
