@@ -55,7 +55,10 @@
 extern "C" {
 #endif
 
-typedef enum {
+/* Status codes. The type is a plain 32-bit integer, so any value a caller
+ * hands back (sps_status_string(-99), say) is well defined on both sides. */
+typedef int32_t sps_status;
+enum {
   SPS_OK = 0,
   SPS_ERR_INVALID_ARGUMENT = -1,   /* NULL pointer, negative size, bad chunk size, ... */
   SPS_ERR_BAD_CSR = -2,            /* sps_validate_csr found a non-canonical CSR */
@@ -65,7 +68,7 @@ typedef enum {
   SPS_ERR_OVERFLOW = -6,           /* a size reaches 2^31 (or a byte count overflows) */
   SPS_ERR_HIP = -7,                /* a HIP runtime call or launch failed */
   SPS_ERR_UNSUPPORTED = -8         /* e.g. chunk too large for the device's LDS */
-} sps_status;
+};
 
 /* A CSR matrix. n_rows, n_cols and nnz are host values; the three arrays
  * are DEVICE arrays: indptr[n_rows+1] int32, indices[nnz] int32,
@@ -379,7 +382,8 @@ typedef struct {
 
 /* Bytes of the offset stream for nnz entries: ceil(10 nnz / 8) rounded up to
  * a multiple of 4 (sps_bsc_encode writes whole 32-bit words; the tail bits
- * are zero). Pure host. */
+ * are zero). Pure host. SPS_ERR_OVERFLOW for nnz above the codec's limit
+ * (floor((2^31 - 1) / 3), the limit of sps_bsc_encode_sizes). */
 sps_status sps_bsc_offsets_bytes(int64_t nnz, size_t *bytes);
 
 /* First half of the encoder (SYNCHRONOUS): checks that m is canonical (as

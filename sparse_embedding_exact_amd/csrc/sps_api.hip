@@ -716,6 +716,9 @@ static int64_t bsc_offsets_needed(int64_t nnz) { return (10 * nnz + 7) / 8; }
 
 sps_status sps_bsc_offsets_bytes(int64_t nnz, size_t *bytes) {
   if (!bytes || nnz < 0) return fail(SPS_ERR_INVALID_ARGUMENT, "NULL argument or negative nnz");
+  if (nnz > kBscMaxNnz)
+    return fail(SPS_ERR_OVERFLOW, "nnz %lld above the codec's %lld", (long long)nnz,
+                (long long)kBscMaxNnz);
   *bytes = (size_t)((bsc_offsets_needed(nnz) + 3) / 4 * 4);
   return SPS_OK;
 }
