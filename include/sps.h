@@ -116,10 +116,15 @@ sps_status sps_items_workspace_size(int64_t n_items, int64_t dim, int64_t nnz,
  *     the slice holds (dim -> first posting, length), about 32 bytes per
  *     distinct dim, instead of a col_ptr[dim+1] per slice; the canonical
  *     col_ptr can be expanded from it (sps_items_slice_col_ptr);
- *  4. when slices hold at least 512 items: the "heavy" dims (at most 32, the
- *     most frequent among those held by at least 1/16 of the items) and, per
- *     slice, their values as dense rows (0 where an item lacks the dim). This
- *     is a speed device; results do not depend on it (SPS_DENSE=0 turns it off).
+ *  4. when slices hold at least 512 items: the "heavy" dims, the most
+ *     frequent among those held by at least 1/16 of the items (a dim counted
+ *     only in the slices where its list holds 1/32 of the slice), in blocks of
+ *     32: the first block, and up to three more while a block's dims carry
+ *     enough of the expected work (the sum over its dims of (df / n_items)^2
+ *     above 0.4, SPS_HEAVY_GAIN overrides); at most 128, SPS_HEAVY_MAX caps
+ *     it (and sizes the slab); per slice, their values as dense rows (0 where
+ *     an item lacks the dim). This is a speed device; results do not depend
+ *     on it beyond rounding (SPS_DENSE=0 turns it off).
  * The item CSR may be released once this stream work has completed.
  * On success *out receives a new handle (free with sps_items_destroy). */
 sps_status sps_prepare(const sps_csr *items, int32_t chunk_size, void *persistent,
@@ -176,8 +181,8 @@ sps_status sps_items_slice_view(const sps_items *h, int64_t slice, void *stream,
 sps_status sps_items_slice_col_ptr(const sps_items *h, int64_t slice, int32_t *col_ptr,
                                    int32_t *status, void *stream);
 
-/* The heavy dims chosen by sps_prepare, ascending (SYNCHRONOUS: waits for
- * `stream`, then copies 132 bytes back). The page notes that term ids
+/* The heavy dims chosen by sps_prepare, ascending, at most 128
+ * (SYNCHRONOUS: waits for `stream`, then copies 516 bytes back). The page notes that term ids
  * cluster in a dictionary prefix (§3.2, Block-Sparse CSR motivation); the
  * few dims most items hold are scored as dense rows. Writes at most
  * `capacity` dims to `dims` (host, nullable) and their number to *count

@@ -330,9 +330,9 @@ class Items:
 
     def heavy_dims(self, stream=None) -> list:
         """The dims kept as dense rows (ascending; synchronous)."""
-        buf = (_I32 * 64)()
+        buf = (_I32 * 128)()
         n = _I32()
-        _check(_lib.sps_items_heavy_dims(self._h, _stream_ptr(stream), buf, 64, ctypes.byref(n)))
+        _check(_lib.sps_items_heavy_dims(self._h, _stream_ptr(stream), buf, 128, ctypes.byref(n)))
         return [int(buf[i]) for i in range(n.value)]
 
     def __del__(self):

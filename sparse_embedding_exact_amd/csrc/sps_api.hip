@@ -114,6 +114,17 @@ int32_t heavy_cap() {
   return sps::kHeavyMax;
 }
 
+// Gain a further heavy-dim block must bring (see heavy_rank_kernel):
+// kHeavyBlockGain unless SPS_HEAVY_GAIN (>= 0) says otherwise (a tuning knob:
+// results do not depend on it beyond rounding).
+float heavy_gain() {
+  if (const char *env = getenv("SPS_HEAVY_GAIN")) {
+    const double v = atof(env);
+    if (v >= 0.0 && v < 1e30) return (float)v;
+  }
+  return sps::kHeavyBlockGain;
+}
+
 template <typename T>
 T *at(void *base, size_t off) {
   return reinterpret_cast<T *>(reinterpret_cast<char *>(base) + off);
@@ -125,7 +136,12 @@ struct ItemsLayout {
   bool overflow;
 };
 
-ItemsLayout items_layout(const sps::Geom &g, int64_t dim, int64_t nnz, bool dense) {
+// Halves from one heavy-dim block's slab to the next's.
+int64_t slab_block_stride(const sps::Geom &g) {
+  return g.num_slices() * (int64_t)sps::kHeavyRec * sps::slab_pitch(g.S);
+}
+
+ItemsLayout items_layout(const sps::Geom &g, int64_t dim, int64_t nnz, bool dense, int32_t cap) {
   const int64_t ns = g.num_slices();
   ItemsLayout L{};
   Layout p;
@@ -136,7 +152,7 @@ ItemsLayout items_layout(const sps::Geom &g, int64_t dim, int64_t nnz, bool dens
   L.post = p.add(nnz + sps::kPostPad, 8);
   L.sbase = p.add(ns + 1, 4);
   L.heavy = p.add(sps::kHeavyMax + 1, 4);
-  L.slab = p.add(dense ? (uint64_t)ns * sps::kHeavyRec * (uint64_t)sps::slab_pitch(g.S) : 0, 2);
+  L.slab = p.add(dense ? (uint64_t)sps::heavy_blocks(cap) * (uint64_t)slab_block_stride(g) : 0, 2);
   L.persistent = p.off;
   Layout s;
   L.flags = s.add(sps::kFlagsInts, 4);
@@ -156,7 +172,7 @@ struct QueriesLayout {
   bool overflow;
 };
 
-QueriesLayout queries_layout(int64_t n, int64_t nnz, int32_t n_sub, bool dense) {
+QueriesLayout queries_layout(int64_t n, int64_t nnz, int32_t n_sub, bool dense, int32_t qh_gstride) {
   const int64_t ng = (n + sps::kRows - 1) / sps::kRows;
   QueriesLayout L{};
   Layout p;
@@ -167,7 +183,7 @@ QueriesLayout queries_layout(int64_t n, int64_t nnz, int32_t n_sub, bool dense) 
   // at least one light entry each: the score kernel may read entry 0 of an
   // empty batch (and ignores it)
   L.lrec = p.add(nnz > 0 ? nnz : 1, 12);
-  L.qh = p.add(dense ? (uint64_t)ng * sps::kHeavyRec * sps::kRows : 0, 2);
+  L.qh = p.add(dense ? (uint64_t)ng * (uint64_t)qh_gstride : 0, 2);
   L.rspart = p.add(n_sub > 1 ? (uint64_t)n_sub * (uint64_t)n : 0, 8);
   L.total = p.off;
   L.overflow = p.overflow;
@@ -181,7 +197,9 @@ struct sps_items {
   int64_t dim, nnz;
   int device;
   bool dense;
-  int32_t pitch;  // slab row pitch (items), dense only
+  int32_t pitch;         // slab row pitch (items), dense only
+  int32_t heavy_blocks;  // heavy-dim blocks the slab holds (dense only)
+  int64_t slab_bstride;  // halves from one block's slab to the next's
   float *inv_norm;
   int4 *dinfo;
   uint4 *dtab;
@@ -202,8 +220,15 @@ struct sps_queries {
   int32_t *lptr;
   uint3 *lrec;
   uint16_t *qh;
+  int32_t qh_gstride;  // halves per row group in qh
   double *rs_part;
 };
+
+namespace {
+// halves per 16-row group of a query batch's heavy-dim tiles: one tile per
+// block the items' slab holds
+int32_t qh_group_stride(const sps_items *items) { return items->heavy_blocks * sps::kTileHalves; }
+}  // namespace
 
 extern "C" {
 
@@ -238,7 +263,7 @@ sps_status sps_items_workspace_size(int64_t n_items, int64_t dim, int64_t nnz,
   if (nnz >= (1ll << 29) - 64)
     return fail(SPS_ERR_OVERFLOW, "item nnz must be below 2^29 - 64 (32-bit posting byte offsets)");
   const sps::Geom g = sps::make_geom(n_items, chunk_size);
-  const ItemsLayout L = items_layout(g, dim, nnz, dense_wanted(g));
+  const ItemsLayout L = items_layout(g, dim, nnz, dense_wanted(g), heavy_cap());
   if (L.overflow) return fail(SPS_ERR_OVERFLOW, "workspace byte count overflows");
   *persistent_bytes = L.persistent;
   *scratch_bytes = L.scratch;
@@ -268,13 +293,16 @@ sps_status sps_prepare(const sps_csr *items, int32_t chunk_size, void *persisten
 
   const sps::Geom g = sps::make_geom(items->n_rows, chunk_size);
   const bool dense = dense_wanted(g);
-  const ItemsLayout L = items_layout(g, items->n_cols, items->nnz, dense);
+  const int32_t cap = heavy_cap();
+  const ItemsLayout L = items_layout(g, items->n_cols, items->nnz, dense, cap);
   sps::ItemsDev d{};
   d.g = g;
   d.dim = items->n_cols;
   d.nnz = items->nnz;
   d.dense = dense;
-  d.heavy_cap = heavy_cap();
+  d.heavy_cap = cap;
+  d.slab_bstride = slab_block_stride(g);
+  d.heavy_gain = heavy_gain();
   d.indptr = items->indptr;
   d.indices = items->indices;
   d.values = items->values;
@@ -306,6 +334,8 @@ sps_status sps_prepare(const sps_csr *items, int32_t chunk_size, void *persisten
   h->device = dev;
   h->dense = dense;
   h->pitch = dense ? sps::slab_pitch(g.S) : 0;
+  h->heavy_blocks = dense ? sps::heavy_blocks(cap) : 0;
+  h->slab_bstride = d.slab_bstride;
   h->inv_norm = d.inv_norm;
   h->dinfo = d.dinfo;
   h->dtab = d.dtab;
@@ -397,7 +427,8 @@ sps_status sps_queries_workspace_size(const sps_items *items, int64_t n_rows, in
   if (dim != items->dim)
     return fail(SPS_ERR_DIM_MISMATCH, "query dim %lld != item dim %lld", (long long)dim,
                 (long long)items->dim);
-  const QueriesLayout L = queries_layout(n_rows, nnz, items->g.n_sub, items->dense);
+  const QueriesLayout L =
+      queries_layout(n_rows, nnz, items->g.n_sub, items->dense, qh_group_stride(items));
   if (L.overflow) return fail(SPS_ERR_OVERFLOW, "workspace byte count overflows");
   *bytes = L.total;
   return SPS_OK;
@@ -421,7 +452,8 @@ sps_status sps_prepare_queries(const sps_csr *queries, const sps_items *items, v
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return fail(SPS_ERR_HIP, "no HIP device");
   const bool dense = items->dense;
-  const QueriesLayout L = queries_layout(queries->n_rows, queries->nnz, items->g.n_sub, dense);
+  const QueriesLayout L = queries_layout(queries->n_rows, queries->nnz, items->g.n_sub, dense,
+                                         qh_group_stride(items));
   sps::QueriesDev d{};
   d.n_rows = queries->n_rows;
   d.dim = queries->n_cols;
@@ -432,6 +464,7 @@ sps_status sps_prepare_queries(const sps_csr *queries, const sps_items *items, v
   d.indices = queries->indices;
   d.values = queries->values;
   d.heavy = items->heavy;
+  d.qh_gstride = qh_group_stride(items);
   d.flags = at<int32_t>(workspace, L.flags);
   d.inv_norm = at<float>(workspace, L.inv);
   d.norm64 = at<double>(workspace, L.norm64);
@@ -456,6 +489,7 @@ sps_status sps_prepare_queries(const sps_csr *queries, const sps_items *items, v
   h->lptr = d.lptr;
   h->lrec = d.lrec;
   h->qh = d.qh;
+  h->qh_gstride = d.qh_gstride;
   h->rs_part = items->g.n_sub > 1 ? at<double>(workspace, L.rspart) : nullptr;
   *out = h;
   return SPS_OK;
@@ -504,6 +538,7 @@ static sps_status score_one(const sps_queries *q, const sps_items *items, int32_
   a.lptr = q->lptr;
   a.lrec = q->lrec;
   a.qh = q->qh;
+  a.qh_gstride = q->qh_gstride;
   a.dinfo = items->dinfo;
   a.dtab = items->dtab;
   a.post = items->post;
@@ -511,6 +546,8 @@ static sps_status score_one(const sps_queries *q, const sps_items *items, int32_
   a.slice_base = items->slice_base;
   a.heavy = items->heavy;
   a.slab = items->slab;
+  a.slab_bstride = items->slab_bstride;
+  a.heavy_blocks = items->heavy_blocks;
   a.pitch = items->pitch;
   a.out = out;
   a.out16 = out16;

@@ -26,11 +26,22 @@ constexpr int kPostPad = 2;
 // four at a time
 constexpr int kPostPad4 = 4;
 
-// Dense path for heavy dims: at most kHeavyMax dims (a multiple of 4, the
-// MFMA depth) whose item document frequency is at least n_items /
-// kHeavyFracInv; only for slices of at least kDenseMinSlice items.
-constexpr int kHeavyMax = 32;
+// Dense path for heavy dims: blocks of kHeavyBlock dims (the depth of one
+// v_mfma_f32_16x16x32_f16), at most kHeavyBlocksMax of them, taken from the
+// dims whose item document frequency is at least n_items / kHeavyFracInv;
+// only for slices of at least kDenseMinSlice items. The prepare takes one
+// block, and each further block while it moves enough of the expected
+// sparse work onto the matrix cores (see heavy_rank_kernel).
+constexpr int kHeavyBlock = 32;
+constexpr int kHeavyBlocksMax = 4;
+constexpr int kHeavyMax = kHeavyBlock * kHeavyBlocksMax;
 constexpr int kHeavyFracInv = 16;
+// The walk's cost of a further block's dims must exceed this many (query
+// entry, posting) products per score to take that block (heavy_rank_kernel):
+// a block of 32 dims on the matrix cores costs about as much as 0.4 such
+// products of the sparse walk per score (both measured on gfx950 at the
+// pages' shape: 0.17 and 0.8 ps per score and per product).
+constexpr float kHeavyBlockGain = 0.4f;
 constexpr int kDenseMinSlice = 512;
 
 // 32-bit fixed point of the on-chip accumulators: 30 fraction bits.
@@ -78,19 +89,27 @@ inline Geom make_geom(int64_t n_items, int32_t chunk_size) {
 }
 // Heavy-dim values are kept as split fp16 pairs for the matrix cores: with
 // X = 256 x (exact), hi = fp16(X) and lo = fp16((X - hi) * 2048), so that
-// X = hi + lo / 2048 up to 2^-22 |X|. Items (and query rows) are stored in
-// tiles of 16: a tile is kTileHalves halves, the hi part then the lo part,
-// each [dim block of 8][item of the tile][8 dims] -- exactly the per-lane
-// operand order of v_mfma_f32_16x16x32_f16 (lane l = item l%16, dim block
-// l/16), so one 16-byte load per lane reads 1 KiB of contiguous memory.
-// Dims past the heavy count are zero.
-constexpr int kHeavyRec = 2 * kHeavyMax;   // halves per item
+// X = hi + lo / 2048 up to 2^-22 |X|. Items (and query rows) are stored per
+// block of kHeavyBlock dims in tiles of 16: a tile is kTileHalves halves,
+// the hi part then the lo part, each [dim group of 8][item of the tile][8
+// dims] -- exactly the per-lane operand order of v_mfma_f32_16x16x32_f16
+// (lane l = item l%16, dim group l/16), so one 16-byte load per lane reads
+// 1 KiB of contiguous memory. Dims past the heavy count are zero. Heavy dim
+// k (its position in the ascending heavy list) is dim k % kHeavyBlock of
+// block k / kHeavyBlock.
+constexpr int kHeavyRec = 2 * kHeavyBlock;  // halves per item and block
 constexpr int kTileHalves = 16 * kHeavyRec;
 constexpr float kHeavyScale = 256.0f;  // X = x * 256
 constexpr float kLoScale = 2048.0f;    // lo = (X - hi) * 2048
-// position of (item j, heavy dim h, part 0 hi / 1 lo) from its tile's start
+// position of (item j, dim h of the block, part 0 hi / 1 lo) from its
+// tile's start
 __host__ __device__ inline int heavy_tile_index(int j, int h, int part) {
-  return part * (16 * kHeavyMax) + (h >> 3) * 128 + (j & 15) * 8 + (h & 7);
+  return part * (16 * kHeavyBlock) + ((h & (kHeavyBlock - 1)) >> 3) * 128 + (j & 15) * 8 +
+         (h & 7);
+}
+// blocks of kHeavyBlock dims needed for `cap` heavy dims
+__host__ __device__ inline int32_t heavy_blocks(int32_t cap) {
+  return (cap + kHeavyBlock - 1) / kHeavyBlock;
 }
 __device__ inline void split_fp16(float x, uint16_t &hi, uint16_t &lo) {
   const float X = x * kHeavyScale;
@@ -185,6 +204,8 @@ struct ItemsDev {
   int64_t dim, nnz;
   bool dense;           // build heavy-dim slabs
   int32_t heavy_cap;    // at most this many heavy dims (<= kHeavyMax)
+  int64_t slab_bstride; // halves from one block's slab to the next's
+  float heavy_gain;     // a further block needs this many products per score (heavy_rank_kernel)
   const int32_t *indptr, *indices;
   const float *values;
   float *inv_norm;      // persistent, n_items
@@ -193,7 +214,8 @@ struct ItemsDev {
   uint2 *post;          // persistent, nnz + kPostPad: (slice-local item id, value bits)
   int32_t *slice_base;  // persistent, num_slices + 1
   int32_t *heavy;       // persistent, kHeavyMax + 1: heavy dims ascending, then their count
-  uint16_t *slab;       // persistent, [num_slices][pitch / 16 tiles] split fp16 (dense only)
+  uint16_t *slab;       // persistent, [heavy_blocks(heavy_cap)][num_slices][pitch / 16 tiles]
+                        // split fp16 (dense only)
   int32_t *flags;       // scratch
   double *norm64;       // scratch, n_items
   int32_t *skey[2];     // scratch, nnz each: columns during the radix sort (sorted: skey[0])
@@ -220,12 +242,13 @@ struct QueriesDev {
   const int32_t *indptr, *indices;
   const float *values;
   const int32_t *heavy;  // the items' heavy dims (dense only)
+  int32_t qh_gstride;    // halves per row group in qh: heavy_blocks(items' cap) tiles
   int32_t *flags;
   float *inv_norm;       // n_rows
   double *norm64;        // n_rows
   int32_t *lptr;         // n_rows + 1: light (non-heavy) entries per row, prefix
   uint3 *lrec;           // nnz: (dim, bits of fl32(q / |q|) * 2^30, row within its group)
-  uint16_t *qh;          // [n_groups] tiles of split fp16: fl32(q / |q|) on heavy dims
+  uint16_t *qh;          // [n_groups][blocks] tiles of split fp16: fl32(q / |q|) on heavy dims
 };
 hipError_t launch_prepare_queries(const QueriesDev &d, hipStream_t s);
 
@@ -242,14 +265,17 @@ struct ScoreArgs {
   bool dense;
   const int32_t *lptr;
   const uint3 *lrec;          // light entries: (dim, value bits, row in group)
-  const uint16_t *qh;         // [row groups] tiles of split fp16 (dense only)
+  const uint16_t *qh;         // [row groups][blocks] tiles of split fp16 (dense only)
+  int32_t qh_gstride;         // halves per row group in qh
   const int4 *dinfo;          // dim index of every slice
   const uint4 *dtab;
   const uint2 *post;          // all slices: (slice-local item id, value bits)
   const uint32_t *post4;      // reduced-precision variant: item | fp16(256 value) << 16
   const int32_t *slice_base;
   const int32_t *heavy;
-  const uint16_t *slab;       // [slices][pitch / 16] tiles of split fp16 (dense only)
+  const uint16_t *slab;       // [blocks][slices][pitch / 16] tiles of split fp16 (dense only)
+  int64_t slab_bstride;       // halves from one block's slab to the next's
+  int32_t heavy_blocks;       // blocks the slab and qh hold (the heavy count never needs more)
   int32_t pitch;
   float *out;
   uint16_t *out16;            // fp16 output of the reduced-precision variant (else null)

@@ -616,13 +616,22 @@ __global__ __launch_bounds__(256) void heavy_collect_kernel(const int32_t *__res
   }
 }
 
-__global__ __launch_bounds__(1024) void heavy_rank_kernel(int32_t cap,
+// How many blocks of kHeavyBlock dims: the first always; block b (the
+// candidates of frequency rank 32 b .. 32 b + 31) while the sum over its dims
+// of (df / n_items)^2 exceeds `gain`. That sum is what the block takes off
+// the sparse walk per score, in (query entry, posting) products, if queries
+// hold each dim about as often as items do; a block on the matrix cores
+// costs about as much as `gain` such products per score.
+__global__ __launch_bounds__(1024) void heavy_rank_kernel(int32_t cap, float gain,
+                                                         int64_t n_items,
                                                          const int32_t *__restrict__ flags,
                                                          const int32_t *__restrict__ hsel,
                                                          int32_t *__restrict__ heavy) {
   constexpr int NT = 1024;
   __shared__ int32_t s_cd[kCandCap], s_cv[kCandCap];
-  __shared__ uint8_t s_sel[kCandCap];
+  __shared__ int16_t s_rank[kCandCap];
+  __shared__ unsigned long long s_bsum[kHeavyBlocksMax];
+  __shared__ int32_t s_count;
   const int t = threadIdx.x;
   if (flags[0] != 0 || cap <= 0) {
     if (t == 0) heavy[kHeavyMax] = 0;
@@ -633,6 +642,7 @@ __global__ __launch_bounds__(1024) void heavy_rank_kernel(int32_t cap,
     s_cd[i] = hsel[33 + i];
     s_cv[i] = hsel[33 + kCandCap + i];
   }
+  if (t < kHeavyBlocksMax) s_bsum[t] = 0ull;
   __syncthreads();
   for (int i = t; i < n; i += NT) {
     int rank = 0;
@@ -641,26 +651,37 @@ __global__ __launch_bounds__(1024) void heavy_rank_kernel(int32_t cap,
       const int32_t vj = s_cv[j], dj = s_cd[j];
       rank += (vj > vi || (vj == vi && dj < di)) ? 1 : 0;
     }
-    s_sel[i] = rank < cap ? 1 : 0;
+    s_rank[i] = (int16_t)rank;
+    if (rank < cap) atomicAdd(&s_bsum[rank / kHeavyBlock], (unsigned long long)vi * (uint64_t)vi);
   }
   __syncthreads();
+  if (t == 0) {
+    const int lim = n < cap ? n : cap;
+    const double nn = (double)n_items * (double)n_items;
+    int nb = 1;
+    while (nb < heavy_blocks(lim) && (double)s_bsum[nb] > (double)gain * nn) ++nb;
+    s_count = lim < nb * kHeavyBlock ? lim : nb * kHeavyBlock;
+  }
+  __syncthreads();
+  const int count = s_count;
   for (int i = t; i < n; i += NT) {
-    if (!s_sel[i]) continue;
+    if (s_rank[i] >= count) continue;
     int pos = 0;
-    for (int j = 0; j < n; ++j) pos += (s_sel[j] && s_cd[j] < s_cd[i]) ? 1 : 0;
+    for (int j = 0; j < n; ++j) pos += (s_rank[j] < count && s_cd[j] < s_cd[i]) ? 1 : 0;
     heavy[pos] = s_cd[i];
   }
-  if (t == 0) heavy[kHeavyMax] = n < cap ? n : cap;
+  if (t == 0) heavy[kHeavyMax] = count;
 }
 
 // slab of slice s: item j's split-fp16 heavy values in its tile (pre-zeroed)
 __global__ __launch_bounds__(256) void slab_scatter_kernel(
-    int32_t pitch, const int32_t *__restrict__ flags, const int32_t *__restrict__ heavy,
+    int32_t cap, int32_t pitch, int64_t bstride, const int32_t *__restrict__ flags,
+    const int32_t *__restrict__ heavy,
     const int4 *__restrict__ dinfo, const uint4 *__restrict__ dtab,
     const int32_t *__restrict__ slice_base, const uint2 *__restrict__ post,
     uint16_t *__restrict__ slab) {
-  const int64_t c = blockIdx.x / kHeavyMax;
-  const int h = blockIdx.x % kHeavyMax;
+  const int64_t c = blockIdx.x / cap;
+  const int h = blockIdx.x % cap;
   if (flags[0] != 0 || h >= heavy[kHeavyMax]) return;
   const int32_t d = heavy[h];
   const int64_t base = slice_base[c];
@@ -668,7 +689,7 @@ __global__ __launch_bounds__(256) void slab_scatter_kernel(
   int32_t b = 0, len = 0;
   if (!dim_lookup(dtab, dinfo[c], (uint32_t)d, b, len)) return;
   const int32_t e = (int32_t)clamp64((int64_t)b + len, 0, snnz);
-  uint16_t *sl = slab + c * (int64_t)pitch * kHeavyRec;
+  uint16_t *sl = slab + (h / kHeavyBlock) * bstride + c * (int64_t)pitch * kHeavyRec;
   for (int32_t k = b + threadIdx.x; k < e; k += 256) {
     const uint2 pe = post[base + k];
     if (pe.x < (uint32_t)pitch) {
@@ -746,14 +767,17 @@ hipError_t launch_prepare_items(const ItemsDev &d, hipStream_t s) {
   hipLaunchKernelGGL(heavy_collect_kernel, dim3((unsigned)hblocks), dim3(256), 0, s, d.gdf, d.dim,
                      tglob, d.flags, d.hsel);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(heavy_rank_kernel, dim3(1), dim3(1024), 0, s, d.heavy_cap, d.flags, d.hsel,
-                     d.heavy);
+  hipLaunchKernelGGL(heavy_rank_kernel, dim3(1), dim3(1024), 0, s, d.heavy_cap, d.heavy_gain,
+                     g.n_items, d.flags, d.hsel, d.heavy);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (d.heavy_cap <= 0) return hipSuccess;
   const int32_t pitch = slab_pitch(g.S);
-  e = launch_fill_i32(reinterpret_cast<int32_t *>(d.slab), ns * (int64_t)pitch * kHeavyRec / 2, 0, s);
+  e = launch_fill_i32(reinterpret_cast<int32_t *>(d.slab),
+                      heavy_blocks(d.heavy_cap) * d.slab_bstride / 2, 0, s);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(slab_scatter_kernel, dim3((unsigned)(ns * kHeavyMax)), dim3(256), 0, s,
-                     pitch, d.flags, d.heavy, d.dinfo, d.dtab, d.slice_base, d.post, d.slab);
+  hipLaunchKernelGGL(slab_scatter_kernel, dim3((unsigned)(ns * d.heavy_cap)), dim3(256), 0, s,
+                     d.heavy_cap, pitch, d.slab_bstride, d.flags, d.heavy, d.dinfo, d.dtab,
+                     d.slice_base, d.post, d.slab);
   return hipGetLastError();
 }
 
@@ -796,7 +820,7 @@ template <bool FILL>
 __global__ __launch_bounds__(256) void light_split_kernel(
     int64_t n_rows, const int32_t *__restrict__ indptr, const int32_t *__restrict__ indices,
     const float *__restrict__ values, const double *__restrict__ norm64,
-    const int32_t *__restrict__ flags, const int32_t *__restrict__ heavy,
+    const int32_t *__restrict__ flags, const int32_t *__restrict__ heavy, int32_t qh_gstride,
     int32_t *__restrict__ lptr, uint3 *__restrict__ lrec, uint16_t *__restrict__ qh) {
   const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (q >= n_rows) return;
@@ -818,7 +842,7 @@ __global__ __launch_bounds__(256) void light_split_kernel(
       if (hs >= 0) {
         uint16_t hi, lo;
         split_fp16(v, hi, lo);
-        uint16_t *tile = qh + (q / kRows) * kTileHalves;
+        uint16_t *tile = qh + (q / kRows) * qh_gstride + (hs / kHeavyBlock) * kTileHalves;
         tile[heavy_tile_index((int)(q % kRows), hs, 0)] = hi;
         tile[heavy_tile_index((int)(q % kRows), hs, 1)] = lo;
       } else {
@@ -902,22 +926,22 @@ hipError_t launch_prepare_queries(const QueriesDev &d, hipStream_t s) {
   if (e != hipSuccess) return e;
   if (d.n_rows == 0) return hipSuccess;
   if (d.dense) {
-    e = launch_fill_i32(reinterpret_cast<int32_t *>(d.qh),
-                        (int64_t)d.n_groups * kRows * kHeavyRec / 2, 0, s);
+    e = launch_fill_i32(reinterpret_cast<int32_t *>(d.qh), (int64_t)d.n_groups * d.qh_gstride / 2,
+                        0, s);
     if (e != hipSuccess) return e;
   }
   const int32_t *heavy = d.dense ? d.heavy : nullptr;
   const unsigned blocks = (unsigned)((d.n_rows + 255) / 256);
   hipLaunchKernelGGL(light_split_kernel<false>, dim3(blocks), dim3(256), 0, s, d.n_rows,
-                     d.indptr, d.indices, d.values, d.norm64, d.flags, heavy, d.lptr, d.lrec,
-                     d.qh);
+                     d.indptr, d.indices, d.values, d.norm64, d.flags, heavy, d.qh_gstride,
+                     d.lptr, d.lrec, d.qh);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(scan_inplace_kernel<1024>, dim3(1), dim3(1024), 0, s, d.lptr,
                      d.n_rows + 1);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(light_split_kernel<true>, dim3(blocks), dim3(256), 0, s, d.n_rows,
-                     d.indptr, d.indices, d.values, d.norm64, d.flags, heavy, d.lptr, d.lrec,
-                     d.qh);
+                     d.indptr, d.indices, d.values, d.norm64, d.flags, heavy, d.qh_gstride,
+                     d.lptr, d.lrec, d.qh);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(light_sort_kernel, dim3((unsigned)d.n_groups), dim3(kLightSortNT), 0, s,
                      d.n_rows, d.lptr, d.lrec);

@@ -23,11 +23,12 @@
 // Dense part (heavy dims): v_mfma_f32_16x16x32_f16 on values split in two
 // fp16 halves (hi, lo) after scaling by 256, so the dot of two values is
 // hi.hi + (hi.lo + lo.hi) / 2048 up to 3 * 2^-22 of |x y| (the lo.lo term is
-// dropped). A is the 16 rows' values on the 32 heavy dims, B the slab's 16
-// items of a tile, both stored in the MFMA operand order (A[i][k] in lane
-// i + 16 (k / 8), element k % 8). Each slab value loaded feeds all 16 rows of
-// both row groups. fp32 sums, rounded once to fixed point, start the
-// accumulators.
+// dropped). A is the 16 rows' values on a block of 32 heavy dims, B the
+// slab's 16 items of a tile, both stored in the MFMA operand order (A[i][k]
+// in lane i + 16 (k / 8), element k % 8). Each slab value loaded feeds all 16
+// rows of both row groups. Per block, fp32 sums rounded once to fixed point;
+// the blocks' sums start the accumulators (one to four blocks, chosen per
+// corpus by the prepare).
 //
 // Sparse part (all other dims): the 16 rows' light entries (dim, value,
 // row) are taken in batches of 1024, two per thread; each looks up its
@@ -94,7 +95,7 @@ constexpr int kBatch = 2 * NT;  // light entries per batch, two per thread
 constexpr int kGroups = 2;      // row groups per workgroup (they share the slab loads)
 static_assert(kRows % NW == 0, "whole rows per wave in the epilogue");
 static_assert(kSliceMax <= NW * 128, "128 items per wave cover a slice");
-static_assert(kRows == 16 && kHeavyMax == 32, "one 16x16x32 MFMA tile covers the rows and heavy dims");
+static_assert(kRows == 16 && kHeavyBlock == 32, "one 16x16x32 MFMA tile covers the rows and a block");
 // Sparse part: posting lists are cut into segments of kSeg entries, one per
 // 16 lanes, described in an LDS table.
 constexpr int kSeg = 16;
@@ -122,7 +123,8 @@ struct ScoreLds {
 };
 
 template <bool DENSE, int MODE>
-__device__ __forceinline__ void score_body(const ScoreArgs &a, int vec4, const ScoreLds &L) {
+__device__ __forceinline__ void score_body(const ScoreArgs &a, int vec4, const ScoreLds &L,
+                                           int nblk) {
   constexpr bool HALF = MODE == kOutHalf;
   constexpr int U = 2;                      // segment groups per wave per walk step
   constexpr int PPL = HALF ? 4 : 2;         // postings per lane (one 16-byte load)
@@ -234,6 +236,7 @@ __device__ __forceinline__ void score_body(const ScoreArgs &a, int vec4, const S
   // 1's waits in registers. Each slab tile loaded serves both groups.
   const int32_t wcol = wv * 128;
   constexpr int kTiles = 8, kHalf = 4;  // tiles per wave, loaded in two halves
+  constexpr int kXT = 1;                // tiles per load of a further block
   h16x8 a_hi[kGroups], a_lo[kGroups], b_hi[kHalf], b_lo[kHalf];
   int32_t dpend[kTiles][4];  // group 1's initial values, fixed point
   const bool wdense = DENSE && wcol < Sp;
@@ -244,20 +247,24 @@ __device__ __forceinline__ void score_body(const ScoreArgs &a, int vec4, const S
   static_assert(kTileHalves == 2 * 64 * 8, "a tile is one 16-byte load per lane per part");
   const h16x8 *st = reinterpret_cast<const h16x8 *>(
       a.slab + (sl * (int64_t)a.pitch + (wdense ? wcol : 0)) * kHeavyRec);
-  auto load_half = [&](int h) {
+  // tiles T0 .. T0 + N - 1 of the wave's share into b_hi/b_lo[0 .. N - 1]
+  auto load_tiles = [&](const h16x8 *sb, int T0, int N) {
 #pragma unroll
-    for (int tt = 0; tt < kHalf; ++tt) {
-      b_hi[tt] = st[(h * kHalf + tt) * 128 + lane];
-      if (!HALF) b_lo[tt] = st[(h * kHalf + tt) * 128 + 64 + lane];
+    for (int tt = 0; tt < N; ++tt) {
+      b_hi[tt] = sb[(T0 + tt) * 128 + lane];
+      if (!HALF) b_lo[tt] = sb[(T0 + tt) * 128 + 64 + lane];
     }
   };
+  auto load_half = [&](const h16x8 *sb, int h) { load_tiles(sb, h * kHalf, kHalf); };
   // lane l holds rows 4(l/16) + i of item 16 tt + l%16
   int *const dbase = acc + (4 * (lane >> 4)) * Lp + wcol + (lane & 15);
-  auto mfma_half = [&](int h) {
+  // products of tiles T0 .. T0 + N - 1 (add: a further block, summed into
+  // the first block's values)
+  auto mfma_tiles = [&](int T0, int N, bool add) {
     if (!wdense) return;
 #pragma unroll
-    for (int tt = 0; tt < kHalf; ++tt) {
-      const int T = h * kHalf + tt;
+    for (int tt = 0; tt < N; ++tt) {
+      const int T = T0 + tt;
 #pragma unroll
       for (int gi = 0; gi < kGroups; ++gi) {
         const f32x4 z = {0.f, 0.f, 0.f, 0.f};
@@ -272,12 +279,13 @@ __device__ __forceinline__ void score_body(const ScoreArgs &a, int vec4, const S
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int v = round_fix((mn[i] + cr[i] * (1.0f / kLoScale)) * kDenseToFix);
-          if (gi == 0) dbase[i * Lp + 16 * T] = v;
-          else dpend[T][i] = v;
+          if (gi == 0) dbase[i * Lp + 16 * T] = add ? dbase[i * Lp + 16 * T] + v : v;
+          else dpend[T][i] = add ? dpend[T][i] + v : v;
         }
       }
     }
   };
+  auto mfma_half = [&](int h, bool add) { mfma_tiles(h * kHalf, kHalf, add); };
   // The A tiles of both groups (4 KiB) are loaded once per workgroup by the
   // first 256 threads and shared through LDS (the segment table's space,
   // unused until the sparse part), not loaded by every wave.
@@ -287,9 +295,9 @@ __device__ __forceinline__ void score_body(const ScoreArgs &a, int vec4, const S
   if (DENSE && t < kGroups * 128) {
     const int gi = t >> 7;
     aq = reinterpret_cast<const h16x8 *>(
-        a.qh + (grp0 + (gi < ng ? gi : 0)) * (int64_t)kTileHalves)[t & 127];
+        a.qh + (grp0 + (gi < ng ? gi : 0)) * (int64_t)a.qh_gstride)[t & 127];
   }
-  if (DENSE) load_half(0);
+  if (DENSE) load_half(st, 0);
   __builtin_amdgcn_sched_barrier(0);
   if (DENSE) {
     if (t < kGroups * 128) astage[t] = aq;
@@ -306,21 +314,46 @@ __device__ __forceinline__ void score_body(const ScoreArgs &a, int vec4, const S
   // range lookups, so its products wait for the slab only and the lookups
   // (random, often an L2 miss) overlap them.
   if (DENSE) {
-    mfma_half(0);
+    mfma_half(0, false);
   } else {
     int4 *acc4 = reinterpret_cast<int4 *>(acc);
     for (int k = t; k < kRows * Lp / 4; k += NT) acc4[k] = make_int4(0, 0, 0, 0);
   }
   __builtin_amdgcn_sched_barrier(0);
-  if (DENSE) load_half(1);
+  if (DENSE) load_half(st, 1);
   fetch_ranges(r0);
   fetch_ranges(r1);
   __builtin_amdgcn_sched_barrier(0);
-  if (DENSE) mfma_half(1);
+  if (DENSE) mfma_half(1, false);
   __builtin_amdgcn_sched_barrier(0);
+  // Further blocks of 32 heavy dims (corpora with many dims held by a large
+  // share of the items): the same two halves per block, each block's values
+  // rounded to fixed point and added, so that every block keeps the error
+  // bound of one. Each wave reads a block's A tiles itself (L1 hits after the
+  // first wave).
+  auto load_block = [&](int b) {
+#pragma unroll
+    for (int gi = 0; gi < kGroups; ++gi) {
+      const h16x8 *qb = reinterpret_cast<const h16x8 *>(
+          a.qh + (grp0 + (gi < ng ? gi : 0)) * (int64_t)a.qh_gstride + b * kTileHalves);
+      a_hi[gi] = qb[lane];
+      a_lo[gi] = qb[64 + lane];
+    }
+    load_tiles(st + b * (a.slab_bstride / 8), 0, kXT);
+  };
   Desc cur, nxt;  // first batch of this group and of the next
   finish_ranges(r0, cur);
   finish_ranges(r1, nxt);
+  // (a further block goes kXT tiles at a time: fewer registers held)
+  for (int b = 1; DENSE && b < nblk; ++b) {
+    load_block(b);
+    const h16x8 *sb = st + b * (a.slab_bstride / 8);
+#pragma unroll
+    for (int T0 = 0; T0 < kTiles; T0 += kXT) {
+      if (T0 > 0) load_tiles(sb, T0, kXT);
+      mfma_tiles(T0, kXT, true);
+    }
+  }
   __syncthreads();  // accumulators initialised before any sparse update
 
   const uint2 *__restrict__ ppost = a.post + cb0;
@@ -602,10 +635,14 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void sc
   __shared__ int32_t s_wtot[NW];
   __shared__ unsigned long long s_hbase;
   const ScoreLds L{acc, s_spos, s_sqv, s_smeta, ws, s_wtot, &s_hbase};
-  // a corpus with no heavy dims (all its slab rows zero) takes the path
-  // without the dense part; the choice is uniform across the workgroup
-  if (DENSE && a.heavy[kHeavyMax] == 0) score_body<false, MODE>(a, vec4, L);
-  else score_body<DENSE, MODE>(a, vec4, L);
+  // heavy-dim blocks in use (the slab and the query tiles hold a.heavy_blocks);
+  // a corpus with no heavy dims takes the path without the dense part. The
+  // choice is uniform across the workgroup.
+  const int nh = DENSE ? a.heavy[kHeavyMax] : 0;
+  int nblk = heavy_blocks(nh);
+  nblk = nblk < a.heavy_blocks ? nblk : a.heavy_blocks;
+  if (DENSE && nblk == 0) score_body<false, MODE>(a, vec4, L, 0);
+  else score_body<DENSE, MODE>(a, vec4, L, nblk);
 }
 
 // row_sums[q] = sum over the chunk's slices, in slice order

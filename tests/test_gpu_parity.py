@@ -19,12 +19,14 @@ TOL = 1e-5
 SLICE_MAX = 1024  # items per slice at most (the prepare call's slice rule)
 
 # Per-score rounding budget of the GPU path (derived in the design notes, §4):
-#   |S_gpu - S| <= EPS_ABS * A + EPS_TERM * (m + 1)
-# with A = sum_d |q^_d i^_d| over the shared dims, m their number, u = 2^-24:
-# inputs rounded once to fp32 (2u), fp32 products (u), the heavy dims' split
-# fp16 (3 * 2^-22 = 12u) and fp32 accumulation over 32 dims (< 32u), the final
-# fp32 conversion (u |S| <= u A): below 49u of A in all; every light product
-# and the dense part are each rounded once to 2^-30 fixed point (2^-31 each).
+#   |S_gpu - S| <= EPS_ABS * A + EPS_TERM * (m + b)
+# with A = sum_d |q^_d i^_d| over the shared dims, m their number, b the
+# heavy-dim blocks (1 to 4; 1 when there are none), u = 2^-24: inputs rounded
+# once to fp32 (2u), fp32 products (u), the heavy dims' split fp16 (3 * 2^-22
+# = 12u) and fp32 accumulation within a block of 32 dims (< 32u of the
+# block's part of A), the final fp32 conversion (u |S| <= u A): below 49u of A
+# in all; every light product and each block's dense sum are rounded once to
+# 2^-30 fixed point (2^-31 each).
 # Sums of scores add the per-score bounds, whose sums over a chunk row or an
 # item column are closed forms of the oracle (kinds 1 and 2); float64 summation
 # adds far less than FP64_SLACK.
@@ -33,9 +35,14 @@ EPS_TERM = 2.0 ** -31
 FP64_SLACK = 1e-7
 
 
-def sum_bar(abs_sums, counts, n_terms):
-    """Bound on |sum of GPU scores - sum of exact scores| over n_terms pairs."""
-    return EPS_ABS * abs_sums + EPS_TERM * (counts + n_terms) + FP64_SLACK
+def sum_bar(abs_sums, counts, n_terms, blocks=1):
+    """Bound on |sum of GPU scores - sum of exact scores| over n_terms pairs
+    (blocks: the corpus's heavy-dim blocks)."""
+    return EPS_ABS * abs_sums + EPS_TERM * (counts + max(1, blocks) * n_terms) + FP64_SLACK
+
+
+def heavy_blocks(it):
+    return (len(it.heavy_dims()) + 31) // 32
 
 
 @pytest.fixture(scope="module")
@@ -209,6 +216,7 @@ def _sampled(env, orc, name, n_rows_sampled, self_scores=False, col_chunks=()):
     torch, sps, dev = env
     it = sps.prepare(sps.CSR.from_host(items, dev), chunk_size=w.chunk_size)
     qq = sps.prepare_queries(sps.CSR.from_host(q, dev), it)
+    nblk = heavy_blocks(it)
     out = torch.empty(q.n_rows, w.chunk_size, dtype=torch.float32, device=dev)
     rs = torch.empty(it.num_chunks, q.n_rows, dtype=torch.float64, device=dev)
     sel = torch.as_tensor(rows, device=dev)
@@ -228,7 +236,7 @@ def _sampled(env, orc, name, n_rows_sampled, self_scores=False, col_chunks=()):
             r_col = orc.col_sums(q, items, b, b + n_c, q_norm=qn, i_norm=inn)
             bar = sum_bar(orc.col_sums(q, items, b, b + n_c, q_norm=qn, i_norm=inn, kind=1),
                           orc.col_sums(q, items, b, b + n_c, q_norm=qn, i_norm=inn, kind=2),
-                          q.n_rows)
+                          q.n_rows, nblk)
             e_col = np.abs(g_col - r_col)
             report("%s column sums, chunk %d (%d items); worst err/bar %.3f" % (
                 name, c, n_c, float((e_col / bar).max())), float(e_col.max()), n_c,
@@ -249,7 +257,7 @@ def _sampled(env, orc, name, n_rows_sampled, self_scores=False, col_chunks=()):
     e_sums = np.abs(g_sums - ref_sums)
     worst_sum = float(e_sums.max())
     chunk_lens = np.array([it.chunk_len(c) for c in range(it.num_chunks)], dtype=np.float64)
-    bars = sum_bar(abs_sums, cnt_sums, chunk_lens[:, None])
+    bars = sum_bar(abs_sums, cnt_sums, chunk_lens[:, None], nblk)
     report("%s %d sampled rows x all items" % (name, len(rows)), worst, n)
     err_all = np.abs(got_rows - ref)
     within = float((err_all <= 1e-6).mean())
@@ -316,12 +324,74 @@ def test_dense_rows_on_and_off(env, orc, dense, monkeypatch):
     assert err <= TOL
 
 
+def expected_heavy(items, chunk_size, cap=128, gain=0.4):
+    """The heavy-dim rule, restated on the host. A dim's frequency counts the
+    items of each slice whose list of that dim holds at least 1/32 of the
+    slice size (so that dims held here and there do not qualify); candidates
+    reach 1/16 of the items; ranked by that frequency (ties to the lower dim):
+    the first block of 32, and block b while the sum over its dims of
+    (df / n)^2 exceeds `gain`; at most `cap` dims."""
+    n = items.n_rows
+    n_sub = -(-chunk_size // SLICE_MAX)
+    S = -(-chunk_size // n_sub)
+    hmin = max(2, S // 32)
+    df = np.zeros(items.n_cols, dtype=np.int64)
+    for c0 in range(0, n, chunk_size):
+        c1 = min(n, c0 + chunk_size)
+        for s0 in range(c0, c1, S):
+            s1 = min(c1, s0 + S)
+            cnt = np.bincount(items.indices[items.indptr[s0]:items.indptr[s1]],
+                              minlength=items.n_cols)
+            df += np.where(cnt >= hmin, cnt, 0)
+    t = max(2, -(-n // 16))
+    cand = np.nonzero(df >= t)[0]
+    order = cand[np.lexsort((cand, -df[cand]))]
+    lim = min(len(order), cap)
+    top = df[order[:lim]].astype(np.float64)
+    nb = 1
+    while nb < -(-lim // 32) and float((top[32 * nb:32 * nb + 32] ** 2).sum()) > gain * float(n) ** 2:
+        nb += 1
+    return sorted(order[:min(lim, 32 * nb)].tolist()) if lim > 0 else []
+
+
 def test_heavy_choice_is_deterministic(env):
+    """Dense-overlap items (Zipf 1.0 over 30,522 dims): four blocks of 32
+    heavy dims, the ones the rule picks, the same on every prepare."""
     torch, sps, dev = env
     _, items, _ = synth.make_workload("dense", n_item=30000)
     a = sps.prepare(sps.CSR.from_host(items, dev), chunk_size=8192).heavy_dims()
     b = sps.prepare(sps.CSR.from_host(items, dev), chunk_size=8192).heavy_dims()
-    assert a == b and len(a) == 32
+    assert a == b and len(a) == 128
+    assert a == expected_heavy(items, 8192)
+
+
+@pytest.mark.parametrize("gain,cap", [("0", "128"), ("0", "40"), ("0.4", "128"), ("0.4", "0")])
+def test_heavy_blocks(env, orc, gain, cap, monkeypatch):
+    """The heavy-dim blocks: every further block forced (gain 0: as many
+    blocks as the candidates fill, the last one partial), a cap of 40 (a
+    second block of 8 dims), the default rule (one block on this Zipf(1.1)
+    corpus) and no heavy dims at all; each the rule's choice, and every score
+    within the bar of the oracle and within rounding of the path without
+    the dense part."""
+    monkeypatch.setenv("SPS_HEAVY_GAIN", gain)
+    monkeypatch.setenv("SPS_HEAVY_MAX", cap)
+    torch, sps, dev = env
+    q, items, _ = synth.make_workload("mid", n_item=9001, n_query=37)
+    it = sps.prepare(sps.CSR.from_host(items, dev), chunk_size=4096)
+    heavy = it.heavy_dims()
+    assert heavy == expected_heavy(items, 4096, int(cap), float(gain))
+    if gain == "0" and cap == "128":
+        assert len(heavy) > 64  # three blocks at least
+    if cap == "40":
+        assert len(heavy) == 40
+    ref = orc.scores(q, items)
+    got = np.concatenate([g for _, _, g, _ in gpu_chunks(env, q, items, 4096)], axis=1)
+    err = float(np.abs(got - ref).max())
+    report("heavy gain %s cap %s (%d dims) 37x9001" % (gain, cap, len(heavy)), err, got.size)
+    assert err <= TOL
+    monkeypatch.setenv("SPS_DENSE", "0")
+    flat = np.concatenate([g for _, _, g, _ in gpu_chunks(env, q, items, 4096)], axis=1)
+    assert float(np.abs(got - flat).max()) <= 2e-6
 
 
 def test_bitwise_reproducible(env):
