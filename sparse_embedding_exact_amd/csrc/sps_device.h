@@ -76,6 +76,31 @@ __device__ __forceinline__ int32_t wave_incl_max_dpp(int32_t x) {
   return x;
 }
 
+// A double moved between lanes by one DPP control (each 32-bit half moved
+// alike); lanes the move has no source for, or rows outside ROW_MASK, get 0.
+template <int CTRL, int ROW_MASK, bool BOUND_CTRL>
+__device__ __forceinline__ double dpp_f64(double x) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, x);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, ROW_MASK,
+                                                            0xf, BOUND_CTRL);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL,
+                                                            ROW_MASK, 0xf, BOUND_CTRL);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// Sum of a double over a wave64, in lane 63 (the other lanes hold partial
+// sums): the lane moves of wave_incl_scan_dpp, no LDS traffic. Every lane
+// must be active.
+__device__ __forceinline__ double wave_total_f64(double x) {
+  x += dpp_f64<0x111, 0xf, true>(x);   // row_shr:1
+  x += dpp_f64<0x112, 0xf, true>(x);   // row_shr:2
+  x += dpp_f64<0x114, 0xf, true>(x);   // row_shr:4
+  x += dpp_f64<0x118, 0xf, true>(x);   // row_shr:8
+  x += dpp_f64<0x142, 0xa, false>(x);  // row_bcast:15
+  x += dpp_f64<0x143, 0xc, false>(x);  // row_bcast:31
+  return x;
+}
+
 // Block-wide inclusive scan of a 32-bit int with one barrier. `ws` is NT/64
 // ints of LDS that the caller must not reuse before another barrier: two
 // calls need a barrier between them (the second would overwrite `ws` while

@@ -46,6 +46,11 @@
 // 16-byte nontemporal stores when aligned (the scores are not re-read, so
 // they should not displace posting lists from L2), and the float64 sum of
 // what it wrote (a per-chunk checksum; slices are folded in a fixed order).
+// That sum is exact in any order: every score written is an integer multiple
+// of 2^-30 below 2 in magnitude and a chunk row holds at most 2^20 of them,
+// so every partial sum is an integer multiple of 2^-30 below 2^21, which a
+// float64 holds exactly. The lanes' sums are added with DPP lane moves, not
+// through LDS.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -525,8 +530,8 @@ __device__ __forceinline__ void score_body(const ScoreArgs &a, int vec4, const S
         tot[rr] = __builtin_amdgcn_readlane(incl[rr], 63);
         wtot += tot[rr];
         if (rsum != nullptr && q < a.n_q) {
-          rs = wave_sum(rs);
-          if (lane == 0) rsum[(g.n_sub == 1 ? 0 : (int64_t)ks * a.n_q) + q] = rs;
+          rs = wave_total_f64(rs);
+          if (lane == 63) rsum[(g.n_sub == 1 ? 0 : (int64_t)ks * a.n_q) + q] = rs;
         }
       }
       if (lane == 0) s_wtot[wv] = wtot;
@@ -595,14 +600,22 @@ __device__ __forceinline__ void score_body(const ScoreArgs &a, int vec4, const S
           }
         }
         if (rsum != nullptr) {
-          rs = wave_sum(rs);
-          if (lane == 0) rsum[(g.n_sub == 1 ? 0 : (int64_t)ks * a.n_q) + q] = rs;
+          rs = wave_total_f64(rs);
+          if (lane == 63) rsum[(g.n_sub == 1 ? 0 : (int64_t)ks * a.n_q) + q] = rs;
         }
         continue;
       }
       float *orow = a.out + q * a.ld + col0;
-      for (int j0 = 4 * lane; j0 < slen; j0 += 256) {
-        const int4 x = arow[j0 >> 2];
+      // the row's (at most four) 16-byte accumulator reads go out together
+      int4 xs[kSliceMax / 256];
+#pragma unroll
+      for (int k = 0; k < kSliceMax / 256; ++k)
+        if (4 * lane + 256 * k < slen) xs[k] = arow[lane + 64 * k];
+#pragma unroll
+      for (int k = 0; k < kSliceMax / 256; ++k) {
+        const int j0 = 4 * lane + 256 * k;
+        if (j0 >= slen) continue;
+        const int4 x = xs[k];
         const f32x4 v = {(float)x.x * kFixInv, (float)x.y * kFixInv, (float)x.z * kFixInv,
                          (float)x.w * kFixInv};
         if (v4 && j0 + 3 < slen) {
@@ -618,8 +631,8 @@ __device__ __forceinline__ void score_body(const ScoreArgs &a, int vec4, const S
         }
       }
       if (rsum != nullptr) {
-        rs = wave_sum(rs);
-        if (lane == 0) rsum[(g.n_sub == 1 ? 0 : (int64_t)ks * a.n_q) + q] = rs;
+        rs = wave_total_f64(rs);
+        if (lane == 63) rsum[(g.n_sub == 1 ? 0 : (int64_t)ks * a.n_q) + q] = rs;
       }
     }
   }
