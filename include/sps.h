@@ -331,7 +331,7 @@ sps_status sps_cosine_chunk_threshold(const sps_queries *q, const sps_items *ite
 
 /* The page allows fp16 value data where a loss below 1e-3 is acceptable,
  * with the norms kept in float32 (§5.3). This variant stores each item value
- * as fp16(256 * fl32(v / ||item||)) (a 4-byte posting with the slice-local
+ * as fp16(2^15 * fl32(v / ||item||)) (a 4-byte posting with the slice-local
  * item id) and writes fp16 scores; query values and all norms stay float32
  * and the accumulation is the same as in sps_cosine_chunk. Error: the item
  * values contribute at most 2^-11 * sum_d |q_d i_d| <= 2^-11 (Cauchy-Schwarz

@@ -88,7 +88,7 @@ inline Geom make_geom(int64_t n_items, int32_t chunk_size) {
   return g;
 }
 // Heavy-dim values are kept as split fp16 pairs for the matrix cores: with
-// X = 256 x (exact), hi = fp16(X) and lo = fp16((X - hi) * 2048), so that
+// X = 2^15 x (exact), hi = fp16(X) and lo = fp16((X - hi) * 2048), so that
 // X = hi + lo / 2048 up to 2^-22 |X|. Items (and query rows) are stored per
 // block of kHeavyBlock dims in tiles of 16: a tile is kTileHalves halves,
 // the hi part then the lo part, each [dim group of 8][item of the tile][8
@@ -99,7 +99,11 @@ inline Geom make_geom(int64_t n_items, int32_t chunk_size) {
 // block k / kHeavyBlock.
 constexpr int kHeavyRec = 2 * kHeavyBlock;  // halves per item and block
 constexpr int kTileHalves = 16 * kHeavyRec;
-constexpr float kHeavyScale = 256.0f;  // X = x * 256
+// The scale 2^15 makes a product of two scaled values 2^30 times the product
+// of the values -- the fixed-point scale of the accumulators -- so the dense
+// sums need no rescaling; |x| <= 1 keeps X within fp16's range (|X| <=
+// 32768, |lo| <= 16384), and values down to 2^-29 stay normal in fp16.
+constexpr float kHeavyScale = 32768.0f;  // X = x * 2^15
 constexpr float kLoScale = 2048.0f;    // lo = (X - hi) * 2048
 // position of (item j, dim h of the block, part 0 hi / 1 lo) from its
 // tile's start
@@ -230,7 +234,7 @@ hipError_t launch_prepare_items(const ItemsDev &d, hipStream_t s);
 hipError_t launch_expand_col_ptr(int64_t dim, const int4 *dinfo, const uint4 *dtab,
                                  const int32_t *slice_base, int64_t slice, int32_t *col_ptr,
                                  int32_t *status, hipStream_t s);
-// 4-byte postings (item | fp16(256 value) << 16) from the prepared 8-byte
+// 4-byte postings (item | fp16(2^15 value) << 16) from the prepared 8-byte
 // ones, plus kPostPad4 zero entries
 hipError_t launch_pack_half(const uint2 *post, int64_t nnz, uint32_t *post4, hipStream_t s);
 
@@ -270,7 +274,7 @@ struct ScoreArgs {
   const int4 *dinfo;          // dim index of every slice
   const uint4 *dtab;
   const uint2 *post;          // all slices: (slice-local item id, value bits)
-  const uint32_t *post4;      // reduced-precision variant: item | fp16(256 value) << 16
+  const uint32_t *post4;      // reduced-precision variant: item | fp16(2^15 value) << 16
   const int32_t *slice_base;
   const int32_t *heavy;
   const uint16_t *slab;       // [blocks][slices][pitch / 16] tiles of split fp16 (dense only)

@@ -21,7 +21,7 @@
 // order independent: the result does not depend on how waves interleave.
 //
 // Dense part (heavy dims): v_mfma_f32_16x16x32_f16 on values split in two
-// fp16 halves (hi, lo) after scaling by 256, so the dot of two values is
+// fp16 halves (hi, lo) after scaling by 2^15, so the dot of two values is
 // hi.hi + (hi.lo + lo.hi) / 2048 up to 3 * 2^-22 of |x y| (the lo.lo term is
 // dropped). A is the 16 rows' values on a block of 32 heavy dims, B the
 // slab's 16 items of a tile, both stored in the MFMA operand order (A[i][k]
@@ -65,7 +65,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h16x8 __attribute__((ext_vector_type(8)));
 
 // dense sums are of values scaled by kHeavyScale on both sides
-constexpr float kDenseToFix = kFixScale / (kHeavyScale * kHeavyScale);  // 2^14
+constexpr float kDenseToFix = kFixScale / (kHeavyScale * kHeavyScale);  // 1
+static_assert(kDenseToFix == 1.0f, "dense sums are already in fixed-point units");
 
 // x rounded to the nearest integer, ties upward: floor(x + 0.5) in one
 // instruction (|x| <= 2^30 here, so no saturation).
@@ -233,12 +234,13 @@ __device__ __forceinline__ void score_body(const ScoreArgs &a, int vec4, const S
 
   // ---- dense part: heavy dims on the matrix cores ----
   // Wave w owns items [128 w, 128 w + 128) of the slice as 8 tiles of 16.
-  // Per tile and row group, three v_mfma_f32_16x16x32_f16 over all
-  // kHeavyMax dims: main = hi.hi and cross = hi.lo + lo.hi of the split
+  // Per tile and row group, three v_mfma_f32_16x16x32_f16 over a block of
+  // 32 heavy dims: main = hi.hi and cross = hi.lo + lo.hi of the split
   // values, so that the dot of the scaled values is main + cross / 2048
-  // (fp32). Scaled back by 2^-16 and to fixed point (2^30) it is the
-  // accumulators' initial value: group 0's is written to LDS at once, group
-  // 1's waits in registers. Each slab tile loaded serves both groups.
+  // (fp32). Both sides carry 2^15, so that sum is already in the
+  // accumulators' fixed-point units (2^30): rounded once, it is their
+  // initial value. Group 0's is written to LDS at once, group 1's waits in
+  // registers. Each slab tile loaded serves both groups.
   const int32_t wcol = wv * 128;
   constexpr int kTiles = 8, kHalf = 4;  // tiles per wave, loaded in two halves
   constexpr int kXT = 1;                // tiles per load of a further block
@@ -464,7 +466,7 @@ __device__ __forceinline__ void score_body(const ScoreArgs &a, int vec4, const S
           for (int u = 0; u < U; ++u) {
             char *const rbase = reinterpret_cast<char *>(acc) + aoff[u];
             if (HALF) {
-              // (item | fp16(256 w) << 16) per posting
+              // (item | fp16(2^15 w) << 16) per posting
 #pragma unroll
               for (int k = 0; k < 4; ++k) {
                 const uint32_t x = pe[u][k];
