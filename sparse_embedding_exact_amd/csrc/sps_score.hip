@@ -219,8 +219,11 @@ __device__ __forceinline__ void score_body(const ScoreArgs &a, int vec4, const S
         }
       }
       if (res != 1) st = L = 0;
-      b.s[i] = (int32_t)clamp64(st, 0, snnz);
-      L = (int32_t)clamp64((int64_t)b.s[i] + L, b.s[i], snnz) - b.s[i];
+      // (clamped to the slice's postings in 32-bit arithmetic: 0 <= s <= snnz,
+      // so snnz - s cannot overflow)
+      const int32_t s0 = min(max(st, 0), snnz);
+      L = min(max(L, 0), snnz - s0);
+      b.s[i] = s0;
       b.L[i] = L < kSliceMax ? L : kSliceMax;  // a slice holds a dim once per item
       b.row[i] = (int32_t)(r.rec[i].z & (kRows - 1));
       b.qv[i] = __uint_as_float(r.rec[i].y);
@@ -243,7 +246,6 @@ __device__ __forceinline__ void score_body(const ScoreArgs &a, int vec4, const S
   // registers. Each slab tile loaded serves both groups.
   const int32_t wcol = wv * 128;
   constexpr int kTiles = 8, kHalf = 4;  // tiles per wave, loaded in two halves
-  constexpr int kXT = 1;                // tiles per load of a further block
   h16x8 a_hi[kGroups], a_lo[kGroups], b_hi[kHalf], b_lo[kHalf];
   int32_t dpend[kTiles][4];  // group 1's initial values, fixed point
   const bool wdense = DENSE && wcol < Sp;
@@ -255,11 +257,11 @@ __device__ __forceinline__ void score_body(const ScoreArgs &a, int vec4, const S
   const h16x8 *st = reinterpret_cast<const h16x8 *>(
       a.slab + (sl * (int64_t)a.pitch + (wdense ? wcol : 0)) * kHeavyRec);
   // tiles T0 .. T0 + N - 1 of the wave's share into b_hi/b_lo[0 .. N - 1]
-  auto load_tiles = [&](const h16x8 *sb, int T0, int N) {
+  auto load_tiles = [&](const h16x8 *sb, int T0, int N, int bs = 0) {
 #pragma unroll
     for (int tt = 0; tt < N; ++tt) {
-      b_hi[tt] = sb[(T0 + tt) * 128 + lane];
-      if (!HALF) b_lo[tt] = sb[(T0 + tt) * 128 + 64 + lane];
+      b_hi[bs + tt] = sb[(T0 + tt) * 128 + lane];
+      if (!HALF) b_lo[bs + tt] = sb[(T0 + tt) * 128 + 64 + lane];
     }
   };
   auto load_half = [&](const h16x8 *sb, int h) { load_tiles(sb, h * kHalf, kHalf); };
@@ -267,7 +269,7 @@ __device__ __forceinline__ void score_body(const ScoreArgs &a, int vec4, const S
   int *const dbase = acc + (4 * (lane >> 4)) * Lp + wcol + (lane & 15);
   // products of tiles T0 .. T0 + N - 1 (add: a further block, summed into
   // the first block's values)
-  auto mfma_tiles = [&](int T0, int N, bool add) {
+  auto mfma_tiles = [&](int T0, int N, bool add, int bs = 0) {
     if (!wdense) return;
 #pragma unroll
     for (int tt = 0; tt < N; ++tt) {
@@ -275,13 +277,14 @@ __device__ __forceinline__ void score_body(const ScoreArgs &a, int vec4, const S
 #pragma unroll
       for (int gi = 0; gi < kGroups; ++gi) {
         const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        const f32x4 mn = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_hi[gi], b_hi[tt], z, 0, 0, 0);
+        const f32x4 mn =
+            __builtin_amdgcn_mfma_f32_16x16x32_f16(a_hi[gi], b_hi[bs + tt], z, 0, 0, 0);
         f32x4 cr;
         if (HALF) {  // item values in one fp16 (hi) each: query hi and lo times it
-          cr = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_lo[gi], b_hi[tt], z, 0, 0, 0);
+          cr = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_lo[gi], b_hi[bs + tt], z, 0, 0, 0);
         } else {
-          cr = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_hi[gi], b_lo[tt], z, 0, 0, 0);
-          cr = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_lo[gi], b_hi[tt], cr, 0, 0, 0);
+          cr = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_hi[gi], b_lo[bs + tt], z, 0, 0, 0);
+          cr = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_lo[gi], b_hi[bs + tt], cr, 0, 0, 0);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -334,9 +337,8 @@ __device__ __forceinline__ void score_body(const ScoreArgs &a, int vec4, const S
   if (DENSE) mfma_half(1, false);
   __builtin_amdgcn_sched_barrier(0);
   // Further blocks of 32 heavy dims (corpora with many dims held by a large
-  // share of the items): the same two halves per block, each block's values
-  // rounded to fixed point and added, so that every block keeps the error
-  // bound of one. Each wave reads a block's A tiles itself (L1 hits after the
+  // share of the items): tile by tile, each block's values rounded to fixed
+  // point and added, so that every block keeps the error bound of one. Each wave reads a block's A tiles itself (L1 hits after the
   // first wave).
   auto load_block = [&](int b) {
 #pragma unroll
@@ -346,19 +348,22 @@ __device__ __forceinline__ void score_body(const ScoreArgs &a, int vec4, const S
       a_hi[gi] = qb[lane];
       a_lo[gi] = qb[64 + lane];
     }
-    load_tiles(st + b * (a.slab_bstride / 8), 0, kXT);
+    load_tiles(st + b * (a.slab_bstride / 8), 0, 1);
   };
   Desc cur, nxt;  // first batch of this group and of the next
   finish_ranges(r0, cur);
   finish_ranges(r1, nxt);
-  // (a further block goes kXT tiles at a time: fewer registers held)
+  // (a further block goes one tile at a time, the next tile's loads in flight
+  // during this tile's products: two tiles held, not four)
   for (int b = 1; DENSE && b < nblk; ++b) {
     load_block(b);
     const h16x8 *sb = st + b * (a.slab_bstride / 8);
 #pragma unroll
-    for (int T0 = 0; T0 < kTiles; T0 += kXT) {
-      if (T0 > 0) load_tiles(sb, T0, kXT);
-      mfma_tiles(T0, kXT, true);
+    for (int T = 0; T < kTiles; ++T) {
+      // the next tile's loads go out before this tile's products
+      if (T + 1 < kTiles) load_tiles(sb, T + 1, 1, (T + 1) & 1);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_tiles(T, 1, true, T & 1);
     }
   }
   __syncthreads();  // accumulators initialised before any sparse update
@@ -367,6 +372,7 @@ __device__ __forceinline__ void score_body(const ScoreArgs &a, int vec4, const S
   const uint32_t *__restrict__ ppost4 = HALF ? a.post4 + cb0 : nullptr;
   const int64_t col0 = ib - g.chunk_begin(a.chunk);
   const bool v4 = vec4 && (col0 % 4 == 0);
+  const bool full = v4 && slen == kSliceMax;
   // per-slice partial row sums only when row sums are asked for
   double *rsum = a.row_sums == nullptr ? nullptr : (g.n_sub == 1 ? a.row_sums : a.rs_part);
   int scan_par = 0;
@@ -477,10 +483,13 @@ __device__ __forceinline__ void score_body(const ScoreArgs &a, int vec4, const S
                   atomicAdd(reinterpret_cast<int *>(rbase + 4 * it), round_fix(qv[u] * w));
               }
             } else {
-              if (nn[u] > 0 && pe[u].x < (uint32_t)slen)
+              // (no bound check on the item: every posting the prepare writes,
+              // the zero padding included, holds a slice-local id below the
+              // slice size S <= Lp, so the address stays in acc[row][0, Lp))
+              if (nn[u] > 0)
                 atomicAdd(reinterpret_cast<int *>(rbase + 4 * pe[u].x),
                           round_fix(qv[u] * __uint_as_float(pe[u].y)));
-              if (nn[u] > 1 && pe[u].z < (uint32_t)slen)
+              if (nn[u] > 1)
                 atomicAdd(reinterpret_cast<int *>(rbase + 4 * pe[u].z),
                           round_fix(qv[u] * __uint_as_float(pe[u].w)));
             }
@@ -608,6 +617,33 @@ __device__ __forceinline__ void score_body(const ScoreArgs &a, int vec4, const S
         continue;
       }
       float *orow = a.out + q * a.ld + col0;
+      if (full) {
+        // a whole slice with aligned rows (every slice but a corpus's last):
+        // four 16-byte reads and stores per lane and no per-lane conditions
+        int4 xs[kSliceMax / 256];
+#pragma unroll
+        for (int k = 0; k < kSliceMax / 256; ++k) xs[k] = arow[lane + 64 * k];
+        float *const o = orow + 4 * lane;
+        double fs = 0.0;
+#pragma unroll
+        for (int k = 0; k < kSliceMax / 256; ++k) {
+          const int4 x = xs[k];
+          const f32x4 v = {(float)x.x * kFixInv, (float)x.y * kFixInv, (float)x.z * kFixInv,
+                           (float)x.w * kFixInv};
+          __builtin_nontemporal_store(v, reinterpret_cast<f32x4 *>(o + 256 * k));
+          const double s4 = ((double)v[0] + (double)v[1]) + ((double)v[2] + (double)v[3]);
+          fs = k == 0 ? s4 : fs + s4;
+          // one store per block of conversions: a burst of stores stalls the
+          // other workgroup's loads
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        rs = fs;
+        if (rsum != nullptr) {
+          rs = wave_total_f64(rs);
+          if (lane == 63) rsum[(g.n_sub == 1 ? 0 : (int64_t)ks * a.n_q) + q] = rs;
+        }
+        continue;
+      }
       // the row's (at most four) 16-byte accumulator reads go out together
       int4 xs[kSliceMax / 256];
 #pragma unroll
