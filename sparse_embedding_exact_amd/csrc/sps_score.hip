@@ -318,11 +318,15 @@ __device__ __forceinline__ void score_body(const ScoreArgs &a, int vec4, const S
       a_lo[gi] = astage[gi * 128 + 64 + lane];
     }
   }
+  fetch_ranges(r0);
+  fetch_ranges(r1);
   // Load order matters: the vector-memory counter drains in issue order.
-  // The first half's products wait for its slab tiles (and the entries
-  // issued before them); the second half's tiles go out before the dependent
-  // range lookups, so its products wait for the slab only and the lookups
-  // (random, often an L2 miss) overlap them.
+  // The range lookups go out as soon as the entries are in (issued first,
+  // they have mostly arrived by the staging barrier), after the first
+  // half's slab tiles, so the first half's products do not wait for them;
+  // the second half's products wait for its tiles, issued after the
+  // lookups, by which time the lookups (random, often an L2 miss) have
+  // mostly returned.
   if (DENSE) {
     mfma_half(0, false);
   } else {
@@ -331,15 +335,13 @@ __device__ __forceinline__ void score_body(const ScoreArgs &a, int vec4, const S
   }
   __builtin_amdgcn_sched_barrier(0);
   if (DENSE) load_half(st, 1);
-  fetch_ranges(r0);
-  fetch_ranges(r1);
   __builtin_amdgcn_sched_barrier(0);
   if (DENSE) mfma_half(1, false);
   __builtin_amdgcn_sched_barrier(0);
   // Further blocks of 32 heavy dims (corpora with many dims held by a large
   // share of the items): tile by tile, each block's values rounded to fixed
-  // point and added, so that every block keeps the error bound of one. Each wave reads a block's A tiles itself (L1 hits after the
-  // first wave).
+  // point and added, so that every block keeps the error bound of one. Each
+  // wave reads a block's A tiles itself (L1 hits after the first wave).
   auto load_block = [&](int b) {
 #pragma unroll
     for (int gi = 0; gi < kGroups; ++gi) {
