@@ -199,54 +199,63 @@ def main():
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(n_chunks)]
-    ev_prep = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+
+    def pair():
+        return (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
 
     def make_step(score_chunk, half=False, before=None):
-        """One pass of the path: prepare items and queries, then score every chunk."""
-        def step(record):
+        """One pass of the path: prepare items and queries, then score every chunk.
+        `evs` (timed steps only) holds the step's own events: (step, prepare, chunks)."""
+        def step(evs=None):
+            if evs is not None:
+                evs[0][0].record(stream)
             if before is not None:
                 before()
-            if record:
-                ev_prep[0].record(stream)
+            if evs is not None:
+                evs[1][0].record(stream)
             it = sps.prepare(items, chunk_size=C)
             if half:
                 it.enable_half()
             qq = sps.prepare_queries(queries, it)
-            if record:
-                ev_prep[1].record(stream)
+            if evs is not None:
+                evs[1][1].record(stream)
             for c in range(n_chunks):
-                if record:
-                    ev[c][0].record(stream)
+                if evs is not None:
+                    evs[2][c][0].record(stream)
                 score_chunk(qq, it, c)
-                if record:
-                    ev[c][1].record(stream)
+                if evs is not None:
+                    evs[2][c][1].record(stream)
+            if evs is not None:
+                evs[0][1].record(stream)
             return it, qq
         return step
 
     def run_timed(step):
-        """Warmup, then exactly args.steps timed steps: (seconds, per-chunk launch ms,
-        prepare ms), the last two averaged over the steps."""
+        """Warmup, then exactly args.steps timed steps, bracketed by a synchronize on
+        both sides and nothing else between them: (seconds, per-chunk launch ms,
+        prepare ms), the last two averaged over the steps. Every timed step records
+        events of its own, read only after the timed region, so that reading them
+        is not timed; the median step is taken from the steps' own events."""
         for _ in range(args.warmup):
-            step(False)
+            step()
         torch.cuda.synchronize()
+        evs = [(pair(), pair(), [pair() for _ in range(n_chunks)]) for _ in range(args.steps)]
+        keep = []
+        t0 = time.perf_counter()
+        for k in range(args.steps):
+            keep.append(step(evs[k]))
+        torch.cuda.synchronize()
+        t_total = time.perf_counter() - t0
+        keep.clear()
         kern = np.zeros(n_chunks)
         prep = 0.0
-        keep = []
         per_step = []
-        t0 = time.perf_counter()
-        for _ in range(args.steps):
-            ts = time.perf_counter()
-            keep.append(step(True))
-            torch.cuda.synchronize()  # events of this step are read before the next records them
-            per_step.append(time.perf_counter() - ts)
-            kern += np.array([a.elapsed_time(b) for a, b in ev])
-            prep += ev_prep[0].elapsed_time(ev_prep[1])
-            keep.clear()
-        torch.cuda.synchronize()
-        run_timed.median_ms = 1e3 * float(np.median(per_step))
-        return time.perf_counter() - t0, kern / args.steps, prep / args.steps
+        for e_step, e_prep, e_chunks in evs:
+            kern += np.array([a.elapsed_time(b) for a, b in e_chunks])
+            prep += e_prep[0].elapsed_time(e_prep[1])
+            per_step.append(e_step[0].elapsed_time(e_step[1]))
+        run_timed.median_ms = float(np.median(per_step))
+        return t_total, kern / args.steps, prep / args.steps
 
     t_total, kern_ms, prep_ms = run_timed(
         make_step(lambda qq, it, c: sps.cosine_chunk(qq, it, c, out, sums[c])))
@@ -315,7 +324,7 @@ def main():
         count_step = make_step(
             lambda qq, it, c: sps.cosine_chunk_threshold(qq, it, c, t_, no_hits, count, sums[c]),
             before=count.zero_)
-        count_step(False)
+        count_step()
         torch.cuda.synchronize()
         n_hits = int(count.item())
         hits = torch.empty(n_hits, 3, dtype=torch.int32, device=dev)
