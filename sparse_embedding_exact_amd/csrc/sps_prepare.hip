@@ -285,8 +285,15 @@ __global__ __launch_bounds__(kSortNT) void csc_sort_pass_kernel(
   const int32_t *kin = FIRST ? indices + b : src_key + b;
   if (t < 256) s_hist[t] = 0u;
   __syncthreads();
-  for (int64_t i = t; i < n; i += kSortNT)
-    atomicAdd(&s_hist[((uint32_t)kin[i] >> shift) & 255u], 1u);
+  // (four tiles' keys in flight at a time)
+  for (int64_t i = t; i < n; i += 4 * kSortNT) {
+    uint32_t kk[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) kk[u] = i + u * kSortNT < n ? (uint32_t)kin[i + u * kSortNT] : 0u;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (i + u * kSortNT < n) atomicAdd(&s_hist[(kk[u] >> shift) & 255u], 1u);
+  }
   __syncthreads();
   {
     const int32_t v = t < 256 ? (int32_t)s_hist[t] : 0;
@@ -296,13 +303,30 @@ __global__ __launch_bounds__(kSortNT) void csc_sort_pass_kernel(
   }
   const uint64_t lt = lane ? (~0ull >> (64 - lane)) : 0ull;
   uint32_t *cflat = &s_cnt[0][0];
+  // the next tile's key and value (or payload) are loaded during this tile
+  int32_t nkey = 0;
+  uint2 npay = make_uint2(0u, 0u);
+  float nval = 0.0f;
+  if (t < n) {
+    nkey = kin[t];
+    if (FIRST) nval = values[b + t];
+    else npay = src_pay[b + t];
+  }
   for (int64_t base = 0; base < n; base += kSortNT) {
     const int64_t i = base + t;
     const bool valid = i < n;
     int32_t key = 0;
     uint2 pay = make_uint2(0u, 0u);
+    const int32_t ckey = nkey;
+    const uint2 cpay = npay;
+    const float cval = nval;
+    if (i + kSortNT < n) {
+      nkey = kin[i + kSortNT];
+      if (FIRST) nval = values[b + i + kSortNT];
+      else npay = src_pay[b + i + kSortNT];
+    }
     if (valid) {
-      key = kin[i];
+      key = ckey;
       if (FIRST) {
         // the item of entry i: the last item starting at or before it
         int lo = 0, hi = nitems;
@@ -312,10 +336,10 @@ __global__ __launch_bounds__(kSortNT) void csc_sort_pass_kernel(
           else hi = mid;
         }
         const double nrm = norm64[i0 + lo];
-        const float w = nrm > 0.0 ? (float)((double)values[b + i] / nrm) : 0.0f;
+        const float w = nrm > 0.0 ? (float)((double)cval / nrm) : 0.0f;
         pay = make_uint2((uint32_t)lo, __float_as_uint(w));
       } else {
-        pay = src_pay[b + i];
+        pay = cpay;
       }
     }
     const uint32_t digit = ((uint32_t)key >> shift) & 255u;
@@ -351,11 +375,11 @@ __global__ __launch_bounds__(kSortNT) void csc_sort_pass_kernel(
 }
 
 // The slice's dim index (see sps_internal.h) from its sorted columns, in two
-// passes of one workgroup per slice over the sorted keys, tile by tile. An
-// entry ends a run (one dim's list) when the next key differs or the slice
-// ends; the run starts at the latest entry at or before it whose previous key
-// differs: a block-wide running maximum over the tile, carried from the
-// tiles before.
+// passes of one workgroup per slice over the sorted keys. An entry ends a run
+// (one dim's list) when the next key differs or the slice ends; the run
+// starts at the latest entry at or before it whose previous key differs: a
+// running maximum, within a lane's four keys and then across the wave (DPP),
+// carried from step to step of the wave's own share of the keys.
 //  COUNT   distinct dims -> info[s].w; with gdf, every list of at least hmin
 //          entries adds its length to gdf[d] (heavy-dim document frequency)
 //  INSERT  each list's (dim, start, length) into the slice's table
@@ -369,7 +393,6 @@ __global__ __launch_bounds__(kRunNT) void dim_runs_kernel(const int32_t *__restr
                                                           uint4 *__restrict__ tab,
                                                           int32_t *__restrict__ gdf, int32_t hmin) {
   constexpr int NW = kRunNT / 64;
-  __shared__ int32_t s_ws[2][NW];
   __shared__ int32_t s_cnt;
   const int64_t sl = blockIdx.x;
   const bool fault = flags[0] != 0;
@@ -380,60 +403,98 @@ __global__ __launch_bounds__(kRunNT) void dim_runs_kernel(const int32_t *__restr
   int4 inf = make_int4(0, 1, 0, 0);
   if (INSERT) inf = info[sl];
   if (!INSERT && t == 0) s_cnt = 0;
-  int32_t mine = 0;   // runs ending at this thread's entries
-  int32_t carry = 0;  // 1 + start of the run open at the tile's first entry
-  int parity = 0;
-  for (int64_t base = 0; base < n; base += kRunNT, parity ^= 1) {
-    const int64_t i = base + t;
-    const bool valid = i < n;
-    const int32_t k = valid ? ks[i] : 0;
-    const bool first = valid && (i == 0 || ks[i - 1] != k);
-    const bool last = valid && (i == n - 1 || ks[i + 1] != k);
-    // running maximum of 1 + (index of a run's first entry), 0 elsewhere
-    int32_t m = wave_incl_max_dpp(first ? (int32_t)i + 1 : 0);
-    if (lane == 63) s_ws[parity][wv] = m;
-    __syncthreads();
-    int32_t tile_max = 0;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const int32_t x = s_ws[parity][w];
-      if (w < wv) m = max(m, x);
-      tile_max = max(tile_max, x);
-    }
-    const int32_t st = max(m, carry) - 1;  // (alternate buffers: no second barrier)
-    carry = max(carry, tile_max);
-    if (!last) continue;
-    const int32_t len = (int32_t)i - st + 1;
-    if (!INSERT) {
-      ++mine;
-      if (gdf != nullptr && len >= hmin) atomicAdd(&gdf[k], len);
-      continue;
-    }
-    const uint32_t nb = (uint32_t)inf.y;
-    uint32_t bk = dim_bucket((uint32_t)k, nb);
-    unsigned long long *t64 = reinterpret_cast<unsigned long long *>(tab + inf.x);
-    constexpr unsigned long long kEmpty64 = ~0ull;
-    for (uint32_t tries = 0; tries < nb; ++tries) {
-      unsigned long long *slot = t64 + 2 * (int64_t)bk;
-      if (inf.z) {  // wide: (dim, start) then (dim, length)
-        const unsigned long long w0 = (uint32_t)k | ((unsigned long long)(uint32_t)st << 32);
-        if (atomicCAS(slot, kEmpty64, w0) == kEmpty64) {
-          slot[1] = (uint32_t)k | ((unsigned long long)(uint32_t)len << 32);
-          break;
-        }
-      } else {
-        // a list is at most one entry per item of the slice (canonical CSR)
-        const uint32_t lm1 = (uint32_t)(len < kSliceMax ? len : kSliceMax) - 1u;
-        const uint32_t v = (uint32_t)st | (lm1 << kStartBits);
-        const unsigned long long w = (uint32_t)k | ((unsigned long long)v << 32);
-        if (atomicCAS(slot, kEmpty64, w) == kEmpty64) break;
-        if (atomicCAS(slot + 1, kEmpty64, w) == kEmpty64) break;
+  if (!INSERT) __syncthreads();
+  // Each wave takes its own contiguous share of the sorted keys (whole steps
+  // of 256, four consecutive keys per lane), with no barrier between the
+  // waves: a run is reported by the wave holding its last entry, its start
+  // found from the run open at the share's first entry (searched backwards, a
+  // run being at most one entry per item).
+  constexpr int KPL = 4;  // keys per lane and step
+  const int64_t share = ((n + NW - 1) / NW + 64 * KPL - 1) / (64 * KPL) * (64 * KPL);
+  const int64_t lo = wv * share, hi = lo + share < n ? lo + share : n;
+  int32_t mine = 0;   // runs ending in this wave's share
+  int32_t carry = 0;  // 1 + start of the run open at the current step's first entry
+  if (lo < hi && lo > 0) {
+    const int32_t k0 = ks[lo];
+    int64_t st = lo;
+    for (int64_t j = lo - 1; j >= 0; j -= 64) {  // (uniform: ballots decide)
+      const int64_t idx = j - lane;
+      const bool diff = idx < 0 || ks[idx] != k0;
+      const uint64_t m = __ballot(diff);
+      if (m != 0ull) {
+        st = j - __builtin_ctzll(m) + 1;
+        break;
       }
-      bk = bk + 1 == nb ? 0u : bk + 1;
+      st = j - 63;
+    }
+    carry = (int32_t)st + 1;
+  }
+  for (int64_t base = lo; base < hi; base += 64 * KPL) {
+    const int64_t j0 = base + KPL * lane;
+    int32_t k[KPL];
+#pragma unroll
+    for (int u = 0; u < KPL; ++u) k[u] = j0 + u < n ? ks[j0 + u] : -1;  // (-1: no dim)
+    // the keys before and after the lane's four (the neighbouring lanes'; the
+    // step's ends from memory)
+    const int32_t kb = base > 0 ? ks[base - 1] : -1;
+    const int32_t ka = base + 64 * KPL < n ? ks[base + 64 * KPL] : -1;
+    int32_t prev = __builtin_amdgcn_update_dpp(0, k[KPL - 1], 0x138, 0xf, 0xf, false);  // wave_shr:1
+    int32_t next = __builtin_amdgcn_update_dpp(0, k[0], 0x130, 0xf, 0xf, false);        // wave_shl:1
+    if (lane == 0) prev = kb;
+    if (lane == 63) next = ka;
+    bool valid[KPL], last[KPL];
+    int32_t lm[KPL];  // running maximum of 1 + (a run's first entry) within the lane
+#pragma unroll
+    for (int u = 0; u < KPL; ++u) {
+      const int64_t j = j0 + u;
+      valid[u] = j < hi;
+      const int32_t kp = u == 0 ? prev : k[u - 1];
+      const int32_t kn = u == KPL - 1 ? next : k[u + 1];
+      const bool first = valid[u] && (j == 0 || kp != k[u]);
+      last[u] = valid[u] && (j == n - 1 || kn != k[u]);
+      const int32_t f = first ? (int32_t)j + 1 : 0;
+      lm[u] = u == 0 ? f : max(lm[u - 1], f);
+    }
+    const int32_t incl = wave_incl_max_dpp(lm[KPL - 1]);
+    const int32_t excl = __builtin_amdgcn_update_dpp(0, incl, 0x138, 0xf, 0xf, false);
+    const int32_t c = max(carry, lane == 0 ? 0 : excl);
+    carry = max(carry, __builtin_amdgcn_readlane(incl, 63));
+#pragma unroll
+    for (int u = 0; u < KPL; ++u) {
+      if (!last[u]) continue;
+      const int32_t st = max(lm[u], c) - 1;
+      const int32_t len = (int32_t)(j0 + u) - st + 1;
+      const int32_t kk = k[u];
+      if (!INSERT) {
+        ++mine;
+        if (gdf != nullptr && len >= hmin) atomicAdd(&gdf[kk], len);
+        continue;
+      }
+      const uint32_t nb = (uint32_t)inf.y;
+      uint32_t bk = dim_bucket((uint32_t)kk, nb);
+      unsigned long long *t64 = reinterpret_cast<unsigned long long *>(tab + inf.x);
+      constexpr unsigned long long kEmpty64 = ~0ull;
+      for (uint32_t tries = 0; tries < nb; ++tries) {
+        unsigned long long *slot = t64 + 2 * (int64_t)bk;
+        if (inf.z) {  // wide: (dim, start) then (dim, length)
+          const unsigned long long w0 = (uint32_t)kk | ((unsigned long long)(uint32_t)st << 32);
+          if (atomicCAS(slot, kEmpty64, w0) == kEmpty64) {
+            slot[1] = (uint32_t)kk | ((unsigned long long)(uint32_t)len << 32);
+            break;
+          }
+        } else {
+          // a list is at most one entry per item of the slice (canonical CSR)
+          const uint32_t lm1 = (uint32_t)(len < kSliceMax ? len : kSliceMax) - 1u;
+          const uint32_t v = (uint32_t)st | (lm1 << kStartBits);
+          const unsigned long long w = (uint32_t)kk | ((unsigned long long)v << 32);
+          if (atomicCAS(slot, kEmpty64, w) == kEmpty64) break;
+          if (atomicCAS(slot + 1, kEmpty64, w) == kEmpty64) break;
+        }
+        bk = bk + 1 == nb ? 0u : bk + 1;
+      }
     }
   }
   if (INSERT) return;
-  __syncthreads();  // s_cnt is cleared
   mine = wave_sum(mine);
   if (lane == 0 && mine != 0) atomicAdd(&s_cnt, mine);
   __syncthreads();
