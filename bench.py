@@ -240,13 +240,14 @@ def main():
             step()
         torch.cuda.synchronize()
         evs = [(pair(), pair(), [pair() for _ in range(n_chunks)]) for _ in range(args.steps)]
-        keep = []
         t0 = time.perf_counter()
         for k in range(args.steps):
-            keep.append(step(evs[k]))
+            # (a step's prepared structures are released as soon as its work is
+            # queued: their workspaces are stream-ordered torch memory, reused by
+            # the next step without new device allocations)
+            step(evs[k])
         torch.cuda.synchronize()
         t_total = time.perf_counter() - t0
-        keep.clear()
         kern = np.zeros(n_chunks)
         prep = 0.0
         per_step = []
