@@ -160,7 +160,7 @@ ItemsLayout items_layout(const sps::Geom &g, int64_t dim, int64_t nnz, bool dens
   L.skey0 = s.add(nnz, 4);
   L.skey1 = s.add(nnz, 4);
   L.spay = s.add(nnz, 8);
-  L.gdf = s.add(dense ? (uint64_t)dim : 0, 4);
+  L.gdf = s.add(dense ? (uint64_t)sps::kGdfStripes * (uint64_t)dim : 0, 4);
   L.hsel = s.add(dense ? sps::kHeavySelInts : 0, 4);
   L.scratch = s.off;
   L.overflow = p.overflow || s.overflow;

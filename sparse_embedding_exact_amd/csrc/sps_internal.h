@@ -224,10 +224,15 @@ struct ItemsDev {
   double *norm64;       // scratch, n_items
   int32_t *skey[2];     // scratch, nnz each: columns during the radix sort (sorted: skey[0])
   uint2 *spay;          // scratch, nnz: (item, value) during the radix sort
-  int32_t *gdf;         // scratch, dim (dense only)
+  int32_t *gdf;         // scratch, kGdfStripes * dim (dense only)
   int32_t *hsel;        // scratch, kHeavySelInts (dense only): heavy-dim candidates
 };
 constexpr int kHeavySelInts = 33 + 2 * 2048;
+// The heavy-dim document frequencies are counted in this many copies of the
+// dim-sized array (slice s adds to copy s % kGdfStripes), then summed: the
+// most frequent dims have a long list in nearly every slice, and one counter
+// per dim would take all of those atomic adds in turn.
+constexpr int kGdfStripes = 16;
 hipError_t launch_prepare_items(const ItemsDev &d, hipStream_t s);
 // col_ptr[0..dim] of slice `slice` expanded from its dim index; *status |= 1
 // (nullable) where a list's length disagrees with the next list's start

@@ -17,6 +17,7 @@
 // structural fault (the dim index then holds no lists).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #include "sps_device.h"
 #include "sps_internal.h"
@@ -374,131 +375,242 @@ __global__ __launch_bounds__(kSortNT) void csc_sort_pass_kernel(
   }
 }
 
-// The slice's dim index (see sps_internal.h) from its sorted columns, in two
-// passes of one workgroup per slice over the sorted keys. An entry ends a run
-// (one dim's list) when the next key differs or the slice ends; the run
-// starts at the latest entry at or before it whose previous key differs: a
-// running maximum, within a lane's four keys and then across the wave (DPP),
-// carried from step to step of the wave's own share of the keys.
+// The slice's dim index (see sps_internal.h) from its sorted columns, one
+// workgroup per slice over the sorted keys. An entry ends a run (one dim's
+// list) when the next key differs or the slice ends; the run starts at the
+// latest entry at or before it whose previous key differs: a running
+// maximum, within a lane's four keys and then across the wave (DPP), carried
+// from step to step of the wave's own share of the keys.
 //  COUNT   distinct dims -> info[s].w; with gdf, every list of at least hmin
-//          entries adds its length to gdf[d] (heavy-dim document frequency)
-//  INSERT  each list's (dim, start, length) into the slice's table
+//          entries adds its length to gdf[(s % kGdfStripes) * dim + d]
+//          (heavy-dim document frequency, summed over the copies later)
+//  BUILD   the slice's table, kBuildBuckets buckets at a time in LDS: each
+//          sweep over the runs inserts those whose home bucket lies in the
+//          range (linear probing in LDS, no global atomics), then the range
+//          is written out whole, empty slots included (so the table needs no
+//          clearing). A run whose probe would leave the range is deferred and
+//          inserted after the last range, by atomic compare-and-swap in the
+//          written table from its home bucket: every slot it passes is full
+//          by then, so it lands where a plain linear-probing insert would
+//          have been allowed to put it, and a lookup from its home finds it.
 // A structural fault leaves every slice with no lists.
 constexpr int kRunNT = 1024;
-template <bool INSERT>
+constexpr int kBuildBuckets = 8192;  // 128 KiB of 16-byte buckets in LDS per range
+constexpr int kDeferCap = 512;       // deferred runs kept in LDS per slice
+
+// The build's deferred-run capacity: kDeferCap, or less when SPS_DIM_DEFER_CAP
+// asks (a test hook: 0 sends every deferred run through the fallback sweep).
+static int32_t dim_defer_cap() {
+  int32_t cap = kDeferCap;
+  if (const char *ev = getenv("SPS_DIM_DEFER_CAP")) {
+    const long v = atol(ev);
+    if (v >= 0 && v < cap) cap = (int32_t)v;
+  }
+  return cap;
+}
+enum { kRunsCount = 0, kRunsBuild = 1 };
+template <int MODE>
 __global__ __launch_bounds__(kRunNT) void dim_runs_kernel(const int32_t *__restrict__ flags,
                                                           const int32_t *__restrict__ slice_base,
                                                           const int32_t *__restrict__ keys,
                                                           int4 *__restrict__ info,
                                                           uint4 *__restrict__ tab,
-                                                          int32_t *__restrict__ gdf, int32_t hmin) {
+                                                          int32_t *__restrict__ gdf, int32_t hmin,
+                                                          int64_t dim, int32_t defer_cap) {
+  constexpr bool BUILD = MODE == kRunsBuild;
   constexpr int NW = kRunNT / 64;
+  constexpr unsigned long long kEmpty64 = ~0ull;
+  static_assert(kDimEmpty == 0xFFFFFFFFu, "an empty slot is all ones");
   __shared__ int32_t s_cnt;
+  __shared__ unsigned long long s_tab[BUILD ? 2 * kBuildBuckets : 1];
+  __shared__ uint4 s_def[BUILD ? kDeferCap : 1];  // (first word, second word) of deferred runs
+  __shared__ int32_t s_ndef;
   const int64_t sl = blockIdx.x;
   const bool fault = flags[0] != 0;
   const int64_t b = fault ? 0 : slice_base[sl];
   const int64_t n = fault ? 0 : slice_base[sl + 1] - b;
   const int32_t *ks = keys + b;
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  int32_t *const gdf_s = gdf == nullptr ? nullptr : gdf + (sl % kGdfStripes) * dim;
   int4 inf = make_int4(0, 1, 0, 0);
-  if (INSERT) inf = info[sl];
-  if (!INSERT && t == 0) s_cnt = 0;
-  if (!INSERT) __syncthreads();
+  if (BUILD) inf = info[sl];
+  if (t == 0) s_cnt = s_ndef = 0;
+  __syncthreads();
   // Each wave takes its own contiguous share of the sorted keys (whole steps
   // of 256, four consecutive keys per lane), with no barrier between the
   // waves: a run is reported by the wave holding its last entry, its start
   // found from the run open at the share's first entry (searched backwards, a
-  // run being at most one entry per item).
+  // run being at most one entry per item). visit(dim, start, length) is called
+  // once per run.
   constexpr int KPL = 4;  // keys per lane and step
   const int64_t share = ((n + NW - 1) / NW + 64 * KPL - 1) / (64 * KPL) * (64 * KPL);
   const int64_t lo = wv * share, hi = lo + share < n ? lo + share : n;
-  int32_t mine = 0;   // runs ending in this wave's share
-  int32_t carry = 0;  // 1 + start of the run open at the current step's first entry
-  if (lo < hi && lo > 0) {
-    const int32_t k0 = ks[lo];
-    int64_t st = lo;
-    for (int64_t j = lo - 1; j >= 0; j -= 64) {  // (uniform: ballots decide)
-      const int64_t idx = j - lane;
-      const bool diff = idx < 0 || ks[idx] != k0;
-      const uint64_t m = __ballot(diff);
-      if (m != 0ull) {
-        st = j - __builtin_ctzll(m) + 1;
-        break;
+  auto sweep = [&](auto &&visit) {
+    int32_t carry = 0;  // 1 + start of the run open at the current step's first entry
+    if (lo < hi && lo > 0) {
+      const int32_t k0 = ks[lo];
+      int64_t st = lo;
+      for (int64_t j = lo - 1; j >= 0; j -= 64) {  // (uniform: ballots decide)
+        const int64_t idx = j - lane;
+        const bool diff = idx < 0 || ks[idx] != k0;
+        const uint64_t m = __ballot(diff);
+        if (m != 0ull) {
+          st = j - __builtin_ctzll(m) + 1;
+          break;
+        }
+        st = j - 63;
       }
-      st = j - 63;
+      carry = (int32_t)st + 1;
     }
-    carry = (int32_t)st + 1;
+    for (int64_t base = lo; base < hi; base += 64 * KPL) {
+      const int64_t j0 = base + KPL * lane;
+      int32_t k[KPL];
+#pragma unroll
+      for (int u = 0; u < KPL; ++u) k[u] = j0 + u < n ? ks[j0 + u] : -1;  // (-1: no dim)
+      // the keys before and after the lane's four (the neighbouring lanes'; the
+      // step's ends from memory)
+      const int32_t kb = base > 0 ? ks[base - 1] : -1;
+      const int32_t ka = base + 64 * KPL < n ? ks[base + 64 * KPL] : -1;
+      int32_t prev = __builtin_amdgcn_update_dpp(0, k[KPL - 1], 0x138, 0xf, 0xf, false);  // wave_shr:1
+      int32_t next = __builtin_amdgcn_update_dpp(0, k[0], 0x130, 0xf, 0xf, false);  // wave_shl:1
+      if (lane == 0) prev = kb;
+      if (lane == 63) next = ka;
+      bool last[KPL];
+      int32_t lm[KPL];  // running maximum of 1 + (a run's first entry) within the lane
+#pragma unroll
+      for (int u = 0; u < KPL; ++u) {
+        const int64_t j = j0 + u;
+        const bool valid = j < hi;
+        const int32_t kp = u == 0 ? prev : k[u - 1];
+        const int32_t kn = u == KPL - 1 ? next : k[u + 1];
+        const bool first = valid && (j == 0 || kp != k[u]);
+        last[u] = valid && (j == n - 1 || kn != k[u]);
+        const int32_t f = first ? (int32_t)j + 1 : 0;
+        lm[u] = u == 0 ? f : max(lm[u - 1], f);
+      }
+      const int32_t incl = wave_incl_max_dpp(lm[KPL - 1]);
+      const int32_t excl = __builtin_amdgcn_update_dpp(0, incl, 0x138, 0xf, 0xf, false);
+      const int32_t c = max(carry, lane == 0 ? 0 : excl);
+      carry = max(carry, __builtin_amdgcn_readlane(incl, 63));
+#pragma unroll
+      for (int u = 0; u < KPL; ++u) {
+        if (!last[u]) continue;
+        const int32_t st = max(lm[u], c) - 1;
+        visit(k[u], st, (int32_t)(j0 + u) - st + 1);
+      }
+    }
+  };
+  if (!BUILD) {
+    int32_t mine = 0;  // runs ending in this wave's share
+    sweep([&](int32_t kk, int32_t st, int32_t len) {
+      ++mine;
+      if (gdf_s != nullptr && len >= hmin) atomicAdd(&gdf_s[kk], len);
+    });
+    mine = wave_sum(mine);
+    if (lane == 0 && mine != 0) atomicAdd(&s_cnt, mine);
+    __syncthreads();
+    if (t == 0) info[sl] = make_int4(0, 0, 0, s_cnt);
+    return;
   }
-  for (int64_t base = lo; base < hi; base += 64 * KPL) {
-    const int64_t j0 = base + KPL * lane;
-    int32_t k[KPL];
-#pragma unroll
-    for (int u = 0; u < KPL; ++u) k[u] = j0 + u < n ? ks[j0 + u] : -1;  // (-1: no dim)
-    // the keys before and after the lane's four (the neighbouring lanes'; the
-    // step's ends from memory)
-    const int32_t kb = base > 0 ? ks[base - 1] : -1;
-    const int32_t ka = base + 64 * KPL < n ? ks[base + 64 * KPL] : -1;
-    int32_t prev = __builtin_amdgcn_update_dpp(0, k[KPL - 1], 0x138, 0xf, 0xf, false);  // wave_shr:1
-    int32_t next = __builtin_amdgcn_update_dpp(0, k[0], 0x130, 0xf, 0xf, false);        // wave_shl:1
-    if (lane == 0) prev = kb;
-    if (lane == 63) next = ka;
-    bool valid[KPL], last[KPL];
-    int32_t lm[KPL];  // running maximum of 1 + (a run's first entry) within the lane
-#pragma unroll
-    for (int u = 0; u < KPL; ++u) {
-      const int64_t j = j0 + u;
-      valid[u] = j < hi;
-      const int32_t kp = u == 0 ? prev : k[u - 1];
-      const int32_t kn = u == KPL - 1 ? next : k[u + 1];
-      const bool first = valid[u] && (j == 0 || kp != k[u]);
-      last[u] = valid[u] && (j == n - 1 || kn != k[u]);
-      const int32_t f = first ? (int32_t)j + 1 : 0;
-      lm[u] = u == 0 ? f : max(lm[u - 1], f);
+  // BUILD. A slot pair per bucket: narrow tables hold two runs per bucket,
+  // (dim | (start | (length - 1) << kStartBits) << 32) each; wide tables one,
+  // (dim | start << 32) then (dim | length << 32).
+  const uint32_t nb = (uint32_t)inf.y;
+  const bool wide = inf.z != 0;
+  uint4 *const gtab = tab + inf.x;
+  auto words = [&](int32_t kk, int32_t st, int32_t len, unsigned long long &w0,
+                   unsigned long long &w1) {
+    if (wide) {
+      w0 = (uint32_t)kk | ((unsigned long long)(uint32_t)st << 32);
+      w1 = (uint32_t)kk | ((unsigned long long)(uint32_t)len << 32);
+    } else {
+      // a list is at most one entry per item of the slice (canonical CSR)
+      const uint32_t lm1 = (uint32_t)(len < kSliceMax ? len : kSliceMax) - 1u;
+      w0 = w1 = (uint32_t)kk | ((unsigned long long)((uint32_t)st | (lm1 << kStartBits)) << 32);
     }
-    const int32_t incl = wave_incl_max_dpp(lm[KPL - 1]);
-    const int32_t excl = __builtin_amdgcn_update_dpp(0, incl, 0x138, 0xf, 0xf, false);
-    const int32_t c = max(carry, lane == 0 ? 0 : excl);
-    carry = max(carry, __builtin_amdgcn_readlane(incl, 63));
-#pragma unroll
-    for (int u = 0; u < KPL; ++u) {
-      if (!last[u]) continue;
-      const int32_t st = max(lm[u], c) - 1;
-      const int32_t len = (int32_t)(j0 + u) - st + 1;
-      const int32_t kk = k[u];
-      if (!INSERT) {
-        ++mine;
-        if (gdf != nullptr && len >= hmin) atomicAdd(&gdf[kk], len);
-        continue;
+  };
+  // into the global table from the run's home bucket on: the first free
+  // slot, unless a slot on the way already holds the dim (only atomics touch
+  // the table here, so no cached copy of it is read)
+  auto insert_global = [&](uint32_t bk, unsigned long long w0, unsigned long long w1) {
+    unsigned long long *t64 = reinterpret_cast<unsigned long long *>(gtab);
+    const uint32_t kk = (uint32_t)w0;
+    for (uint32_t tries = 0; tries < nb; ++tries) {
+      unsigned long long *slot = t64 + 2 * (int64_t)bk;
+      unsigned long long old = atomicCAS(slot, kEmpty64, w0);
+      if (old == kEmpty64) {
+        if (wide) slot[1] = w1;
+        return;
       }
-      const uint32_t nb = (uint32_t)inf.y;
-      uint32_t bk = dim_bucket((uint32_t)kk, nb);
-      unsigned long long *t64 = reinterpret_cast<unsigned long long *>(tab + inf.x);
-      constexpr unsigned long long kEmpty64 = ~0ull;
-      for (uint32_t tries = 0; tries < nb; ++tries) {
-        unsigned long long *slot = t64 + 2 * (int64_t)bk;
-        if (inf.z) {  // wide: (dim, start) then (dim, length)
-          const unsigned long long w0 = (uint32_t)kk | ((unsigned long long)(uint32_t)st << 32);
+      if ((uint32_t)old == kk) return;
+      if (!wide) {
+        old = atomicCAS(slot + 1, kEmpty64, w0);
+        if (old == kEmpty64 || (uint32_t)old == kk) return;
+      }
+      bk = bk + 1 == nb ? 0u : bk + 1;
+    }
+  };
+  for (uint32_t p0 = 0; p0 < nb; p0 += kBuildBuckets) {
+    const uint32_t p1 = nb - p0 < (uint32_t)kBuildBuckets ? nb : p0 + kBuildBuckets;
+    for (uint32_t i = t; i < 2 * (p1 - p0); i += kRunNT) s_tab[i] = kEmpty64;
+    __syncthreads();
+    sweep([&](int32_t kk, int32_t st, int32_t len) {
+      const uint32_t home = dim_bucket((uint32_t)kk, nb);
+      if (home < p0 || home >= p1) return;
+      unsigned long long w0, w1;
+      words(kk, st, len, w0, w1);
+      for (uint32_t bk = home; bk < p1; ++bk) {
+        unsigned long long *slot = s_tab + 2 * (bk - p0);
+        if (wide) {
           if (atomicCAS(slot, kEmpty64, w0) == kEmpty64) {
-            slot[1] = (uint32_t)kk | ((unsigned long long)(uint32_t)len << 32);
-            break;
+            slot[1] = w1;
+            return;
           }
         } else {
-          // a list is at most one entry per item of the slice (canonical CSR)
-          const uint32_t lm1 = (uint32_t)(len < kSliceMax ? len : kSliceMax) - 1u;
-          const uint32_t v = (uint32_t)st | (lm1 << kStartBits);
-          const unsigned long long w = (uint32_t)kk | ((unsigned long long)v << 32);
-          if (atomicCAS(slot, kEmpty64, w) == kEmpty64) break;
-          if (atomicCAS(slot + 1, kEmpty64, w) == kEmpty64) break;
+          if (atomicCAS(slot, kEmpty64, w0) == kEmpty64) return;
+          if (atomicCAS(slot + 1, kEmpty64, w0) == kEmpty64) return;
         }
-        bk = bk + 1 == nb ? 0u : bk + 1;
       }
-    }
+      // the probe would leave the range: defer
+      const int i = atomicAdd(&s_ndef, 1);
+      if (i < defer_cap)
+        s_def[i] = make_uint4((uint32_t)w0, (uint32_t)(w0 >> 32), (uint32_t)w1,
+                              (uint32_t)(w1 >> 32));
+    });
+    __syncthreads();
+    const uint4 *st4 = reinterpret_cast<const uint4 *>(s_tab);
+    for (uint32_t i = t; i < p1 - p0; i += kRunNT) gtab[p0 + i] = st4[i];
+    __syncthreads();  // (the range is read before the next one clears it)
   }
-  if (INSERT) return;
-  mine = wave_sum(mine);
-  if (lane == 0 && mine != 0) atomicAdd(&s_cnt, mine);
+  // the deferred runs, into the written table (its stores are complete: the
+  // barrier above waited for them)
+  const int nd = s_ndef;  // (uniform: read after the last barrier)
+  for (int i = t; i < (nd < defer_cap ? nd : defer_cap); i += kRunNT) {
+    const uint4 d = s_def[i];
+    const unsigned long long w0 = d.x | ((unsigned long long)d.y << 32);
+    const unsigned long long w1 = d.z | ((unsigned long long)d.w << 32);
+    insert_global(dim_bucket(d.x, nb), w0, w1);
+  }
+  if (nd <= defer_cap) return;
+  // More deferred runs than s_def holds (a table far from its usual fill):
+  // every run not yet in the table goes in by the same global insert.
   __syncthreads();
-  if (t == 0) info[sl] = make_int4(0, 0, 0, s_cnt);
+  sweep([&](int32_t kk, int32_t st, int32_t len) {
+    unsigned long long w0, w1;
+    words(kk, st, len, w0, w1);
+    insert_global(dim_bucket((uint32_t)kk, nb), w0, w1);
+  });
+}
+
+// gdf[d] += gdf[s * dim + d] for the other copies s
+__global__ void gdf_fold_kernel(int64_t dim, int32_t *__restrict__ gdf) {
+  for (int64_t d = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; d < dim;
+       d += (int64_t)gridDim.x * blockDim.x) {
+    int32_t v = gdf[d];
+#pragma unroll
+    for (int s = 1; s < kGdfStripes; ++s) v += gdf[s * dim + d];
+    gdf[d] = v;
+  }
 }
 
 // Bucket ranges of the slices' tables (one workgroup): nb = max(1, 2 distinct),
@@ -525,15 +637,6 @@ __global__ __launch_bounds__(1024) void dim_layout_kernel(int64_t ns,
     carry += tot;
   }
   if (threadIdx.x == 0) info[ns] = make_int4(carry, 0, 0, 0);
-}
-
-// every word of the first info[ns].x buckets set to all ones (empty)
-__global__ void dim_clear_kernel(const int4 *__restrict__ total, uint4 *__restrict__ tab) {
-  const int64_t n = total->x;
-  const uint4 e = make_uint4(kDimEmpty, kDimEmpty, kDimEmpty, kDimEmpty);
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
-       i += (int64_t)gridDim.x * blockDim.x)
-    tab[i] = e;
 }
 
 // col_ptr of one slice from its index (for verification and tools): dims
@@ -780,7 +883,7 @@ hipError_t launch_prepare_items(const ItemsDev &d, hipStream_t s) {
   if (e != hipSuccess) return e;
   if (g.n_items == 0) return hipSuccess;
   if (d.dense) {
-    e = launch_fill_i32(d.gdf, d.dim, 0, s);
+    e = launch_fill_i32(d.gdf, kGdfStripes * d.dim, 0, s);
     if (e != hipSuccess) return e;
   }
   // radix passes: 8-bit digits of the largest column, at least one (the
@@ -803,17 +906,17 @@ hipError_t launch_prepare_items(const ItemsDev &d, hipStream_t s) {
                          kd, pd, 8 * p);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  // the dim index: count the lists, lay out the tables, clear them, insert
+  // the dim index: count the lists, lay out the tables, build them
   const int32_t hmin = g.S / (2 * kHeavyFracInv) > 2 ? g.S / (2 * kHeavyFracInv) : 2;
-  hipLaunchKernelGGL(dim_runs_kernel<false>, dim3((unsigned)ns), dim3(kRunNT), 0, s, d.flags,
-                     d.slice_base, d.skey[0], d.dinfo, d.dtab, d.dense ? d.gdf : nullptr, hmin);
+  hipLaunchKernelGGL(dim_runs_kernel<kRunsCount>, dim3((unsigned)ns), dim3(kRunNT), 0, s, d.flags,
+                     d.slice_base, d.skey[0], d.dinfo, d.dtab, d.dense ? d.gdf : nullptr, hmin,
+                     d.dim, 0);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(dim_layout_kernel, dim3(1), dim3(1024), 0, s, ns, d.slice_base, d.dinfo);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(dim_clear_kernel, dim3(2048), dim3(256), 0, s, d.dinfo + ns, d.dtab);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(dim_runs_kernel<true>, dim3((unsigned)ns), dim3(kRunNT), 0, s, d.flags,
-                     d.slice_base, d.skey[0], d.dinfo, d.dtab, nullptr, 0);
+  hipLaunchKernelGGL(dim_runs_kernel<kRunsBuild>, dim3((unsigned)ns), dim3(kRunNT), 0, s, d.flags,
+                     d.slice_base, d.skey[0], d.dinfo, d.dtab, nullptr, 0, d.dim,
+                     dim_defer_cap());
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (!d.dense) return hipSuccess;
   const int64_t tg64 = (g.n_items + kHeavyFracInv - 1) / kHeavyFracInv;
@@ -822,6 +925,8 @@ hipError_t launch_prepare_items(const ItemsDev &d, hipStream_t s) {
   if (e != hipSuccess) return e;
   int64_t hblocks = (d.dim + 255) / 256;
   if (hblocks > 1024) hblocks = 1024;
+  hipLaunchKernelGGL(gdf_fold_kernel, dim3((unsigned)hblocks), dim3(256), 0, s, d.dim, d.gdf);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(heavy_level_kernel, dim3((unsigned)hblocks), dim3(256), 0, s, d.gdf, d.dim,
                      tglob, d.flags, d.hsel);
   if ((e = hipGetLastError()) != hipSuccess) return e;

@@ -134,6 +134,19 @@ def test_structures_dense_and_edge(env, orc):
     _check_structures(env, orc, items, 8192, "edge 17000 items (empty rows, signed)")
 
 
+@pytest.mark.parametrize("cap", ["0", "1"])
+def test_structures_dim_index_fallback(env, orc, cap, monkeypatch):
+    """The dim index built with room for fewer deferred runs than the slices
+    defer (SPS_DIM_DEFER_CAP; runs whose probe leaves an LDS range of the
+    table are deferred): the rest go in through the fallback sweep, and the
+    index must come out the same."""
+    monkeypatch.setenv("SPS_DIM_DEFER_CAP", cap)
+    _, items, _ = synth.make_workload("mid", n_item=30001)
+    _check_structures(env, orc, items, 8192, "mid 30001 items, deferred-run cap %s" % cap)
+    _, items, _ = synth.make_workload("edge", n_item=17000)
+    _check_structures(env, orc, items, 8192, "edge 17000 items, deferred-run cap %s" % cap)
+
+
 @pytest.mark.parametrize("name", ["pages", "dense", "edge"])
 def test_structures_full_size_sample(env, orc, name):
     """Bit-exact inverted lists on a seeded sample of the full-size corpora's
