@@ -28,16 +28,29 @@ namespace sps {
 // small utilities
 // ---------------------------------------------------------------------------
 
+// p[0..n) = v: 16-byte stores over the aligned middle, the (at most three)
+// ints before it and after it by the first workgroup
 __global__ void fill_i32_kernel(int32_t *__restrict__ p, int64_t n, int32_t v) {
-  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t lead = (int64_t)((16u - (uint32_t)(reinterpret_cast<uintptr_t>(p) & 15u)) & 15u) / 4;
+  const int64_t h = lead < n ? lead : n;
+  const int64_t n4 = (n - h) / 4;
+  int4 *const p4 = reinterpret_cast<int4 *>(p + h);
+  const int4 v4 = make_int4(v, v, v, v);
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (; i < n; i += stride) p[i] = v;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) p4[i] = v4;
+  if (blockIdx.x == 0 && threadIdx.x < 4) {
+    const int64_t k = threadIdx.x;
+    if (k < h) p[k] = v;
+    if (h + 4 * n4 + k < n) p[h + 4 * n4 + k] = v;
+  }
 }
 
 hipError_t launch_fill_i32(int32_t *p, int64_t n, int32_t v, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  int64_t blocks = (n + 255) / 256;
-  if (blocks > 65536) blocks = 65536;
+  // (a bounded grid: a launch of many small workgroups is paced by their dispatch)
+  int64_t blocks = (n / 4 + 255) / 256;
+  if (blocks < 1) blocks = 1;
+  if (blocks > 4096) blocks = 4096;
   hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, n, v);
   return hipGetLastError();
 }
@@ -77,9 +90,13 @@ __device__ __forceinline__ void report(int32_t *flags, int64_t row, int bit, int
   atomicMin(reinterpret_cast<unsigned long long *>(flags + 2), key);
 }
 
-// Rows are checked as in a plain loop over each row; a workgroup whose 256
-// row pointers are all in order and in range stages the rows' indices (and
-// values, for the full check) through LDS in windows, with coalesced loads.
+// Rows are checked as in a plain loop over each row. A workgroup whose 256
+// row pointers are all in order and in range reads its rows' entries, one
+// contiguous range, with coalesced loads: for the index-range check alone,
+// entry by entry (an index out of range is charged to its row, found by a
+// binary search of the row pointers; a row's later bad indices add nothing
+// to what its first one reported), for the full check through LDS windows,
+// each thread then walking its own row in order.
 constexpr int kCheckWin = 4096;
 
 __global__ __launch_bounds__(256) void csr_check_kernel(int64_t n_rows, int64_t n_cols,
@@ -125,6 +142,29 @@ __global__ __launch_bounds__(256) void csr_check_kernel(int64_t n_rows, int64_t 
   if (__syncthreads_and(ok)) {
     const int64_t r1 = r0 + 256 < n_rows ? r0 + 256 : n_rows;
     const int64_t vb = r0 < n_rows ? indptr[r0] : 0, ve = r0 < n_rows ? indptr[r1] : 0;
+    if (!full) {
+      // (eight loads in flight per thread)
+      for (int64_t k0 = vb + threadIdx.x; k0 < ve; k0 += 8 * 256) {
+        int32_t dd[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) dd[u] = k0 + u * 256 < ve ? indices[k0 + u * 256] : 0;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int64_t k = k0 + u * 256;
+          if (k < ve && (dd[u] < 0 || (int64_t)dd[u] >= n_cols)) {
+            // the row holding entry k: the last row of the group starting at or before it
+            int64_t lo = r0, hi = r1;
+            while (hi - lo > 1) {
+              const int64_t mid = (lo + hi) >> 1;
+              if ((int64_t)indptr[mid] <= k) lo = mid;
+              else hi = mid;
+            }
+            report(flags, lo, 4, 3);
+          }
+        }
+      }
+      return;
+    }
     for (int64_t w0 = vb; w0 < ve; w0 += kCheckWin) {
       const int64_t w1 = w0 + kCheckWin < ve ? w0 + kCheckWin : ve;
       __syncthreads();  // the previous window has been read
@@ -837,32 +877,52 @@ __global__ __launch_bounds__(1024) void heavy_rank_kernel(int32_t cap, float gai
   if (t == 0) heavy[kHeavyMax] = count;
 }
 
-// slab of slice s: item j's split-fp16 heavy values in its tile (pre-zeroed)
-__global__ __launch_bounds__(256) void slab_scatter_kernel(
-    int32_t cap, int32_t pitch, int64_t bstride, const int32_t *__restrict__ flags,
+// slab of slice c (one workgroup per slice), block by block of kHeavyBlock
+// heavy dims in use: the block's tiles are assembled in LDS (zeroed, then
+// each of its dims' lists written in as split-fp16 values; wave w takes the
+// block's dims w, w + 16, ...) and written out whole. Blocks past the ones in
+// use are never read.
+constexpr int kSlabNT = 1024;
+__global__ __launch_bounds__(kSlabNT) void slab_scatter_kernel(
+    int32_t pitch, int64_t bstride, const int32_t *__restrict__ flags,
     const int32_t *__restrict__ heavy,
     const int4 *__restrict__ dinfo, const uint4 *__restrict__ dtab,
     const int32_t *__restrict__ slice_base, const uint2 *__restrict__ post,
     uint16_t *__restrict__ slab) {
-  const int64_t c = blockIdx.x / cap;
-  const int h = blockIdx.x % cap;
-  if (flags[0] != 0 || h >= heavy[kHeavyMax]) return;
-  const int32_t d = heavy[h];
+  constexpr int NW = kSlabNT / 64;
+  constexpr int kBlockHalves = kSliceMax * kHeavyRec;  // one block of a whole slice
+  __shared__ uint4 s_blk[kBlockHalves * 2 / 16];
+  uint16_t *const sh = reinterpret_cast<uint16_t *>(s_blk);
+  const int64_t c = blockIdx.x;
+  if (flags[0] != 0) return;
+  const int count = heavy[kHeavyMax];
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const int64_t base = slice_base[c];
   const int32_t snnz = slice_base[c + 1] - slice_base[c];
-  int32_t b = 0, len = 0;
-  if (!dim_lookup(dtab, dinfo[c], (uint32_t)d, b, len)) return;
-  const int32_t e = (int32_t)clamp64((int64_t)b + len, 0, snnz);
-  uint16_t *sl = slab + (h / kHeavyBlock) * bstride + c * (int64_t)pitch * kHeavyRec;
-  for (int32_t k = b + threadIdx.x; k < e; k += 256) {
-    const uint2 pe = post[base + k];
-    if (pe.x < (uint32_t)pitch) {
-      uint16_t hi, lo;
-      split_fp16(__uint_as_float(pe.y), hi, lo);
-      uint16_t *tile = sl + (int64_t)(pe.x >> 4) * kTileHalves;
-      tile[heavy_tile_index(pe.x, h, 0)] = hi;
-      tile[heavy_tile_index(pe.x, h, 1)] = lo;
+  const int words = pitch * kHeavyRec * 2 / 16;  // 16-byte words of the slice's block
+  for (int hb = 0; hb < heavy_blocks(count); ++hb) {
+    for (int i = t; i < words; i += kSlabNT) s_blk[i] = make_uint4(0u, 0u, 0u, 0u);
+    __syncthreads();
+    const int hend = count < (hb + 1) * kHeavyBlock ? count : (hb + 1) * kHeavyBlock;
+    for (int h = hb * kHeavyBlock + wv; h < hend; h += NW) {
+      int32_t b = 0, len = 0;
+      if (!dim_lookup(dtab, dinfo[c], (uint32_t)heavy[h], b, len)) continue;
+      const int32_t e = (int32_t)clamp64((int64_t)b + len, 0, snnz);
+      for (int32_t k = b + lane; k < e; k += 64) {
+        const uint2 pe = post[base + k];
+        if (pe.x < (uint32_t)pitch) {
+          uint16_t hi, lo;
+          split_fp16(__uint_as_float(pe.y), hi, lo);
+          uint16_t *tile = sh + (pe.x >> 4) * kTileHalves;
+          tile[heavy_tile_index(pe.x, h, 0)] = hi;
+          tile[heavy_tile_index(pe.x, h, 1)] = lo;
+        }
+      }
     }
+    __syncthreads();
+    uint4 *dst = reinterpret_cast<uint4 *>(slab + hb * bstride + c * (int64_t)pitch * kHeavyRec);
+    for (int i = t; i < words; i += kSlabNT) dst[i] = s_blk[i];
+    __syncthreads();  // (read out before the next block clears it)
   }
 }
 
@@ -938,12 +998,9 @@ hipError_t launch_prepare_items(const ItemsDev &d, hipStream_t s) {
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (d.heavy_cap <= 0) return hipSuccess;
   const int32_t pitch = slab_pitch(g.S);
-  e = launch_fill_i32(reinterpret_cast<int32_t *>(d.slab),
-                      heavy_blocks(d.heavy_cap) * d.slab_bstride / 2, 0, s);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(slab_scatter_kernel, dim3((unsigned)(ns * d.heavy_cap)), dim3(256), 0, s,
-                     d.heavy_cap, pitch, d.slab_bstride, d.flags, d.heavy, d.dinfo, d.dtab,
-                     d.slice_base, d.post, d.slab);
+  hipLaunchKernelGGL(slab_scatter_kernel, dim3((unsigned)ns), dim3(kSlabNT), 0, s, pitch,
+                     d.slab_bstride, d.flags, d.heavy, d.dinfo, d.dtab, d.slice_base, d.post,
+                     d.slab);
   return hipGetLastError();
 }
 
