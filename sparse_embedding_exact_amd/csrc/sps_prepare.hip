@@ -908,14 +908,21 @@ __global__ __launch_bounds__(kSlabNT) void slab_scatter_kernel(
       int32_t b = 0, len = 0;
       if (!dim_lookup(dtab, dinfo[c], (uint32_t)heavy[h], b, len)) continue;
       const int32_t e = (int32_t)clamp64((int64_t)b + len, 0, snnz);
-      for (int32_t k = b + lane; k < e; k += 64) {
-        const uint2 pe = post[base + k];
-        if (pe.x < (uint32_t)pitch) {
-          uint16_t hi, lo;
-          split_fp16(__uint_as_float(pe.y), hi, lo);
-          uint16_t *tile = sh + (pe.x >> 4) * kTileHalves;
-          tile[heavy_tile_index(pe.x, h, 0)] = hi;
-          tile[heavy_tile_index(pe.x, h, 1)] = lo;
+      // (four postings in flight per lane)
+      for (int32_t k0 = b + lane; k0 < e; k0 += 4 * 64) {
+        uint2 pe[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          pe[u] = k0 + 64 * u < e ? post[base + k0 + 64 * u] : make_uint2(0xFFFFFFFFu, 0u);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          if (pe[u].x < (uint32_t)pitch) {
+            uint16_t hi, lo;
+            split_fp16(__uint_as_float(pe[u].y), hi, lo);
+            uint16_t *tile = sh + (pe[u].x >> 4) * kTileHalves;
+            tile[heavy_tile_index(pe[u].x, h, 0)] = hi;
+            tile[heavy_tile_index(pe[u].x, h, 1)] = lo;
+          }
         }
       }
     }
