@@ -66,6 +66,11 @@ def parse():
                     help="measured HBM bytes per score launch (rocprofv3 FETCH_SIZE / "
                          "WRITE_SIZE summary); used only while the score kernel's sources "
                          "still hash to the value recorded there")
+    ap.add_argument("--event-every", type=int, default=16, metavar="E",
+                    help="timed steps bracket every E-th score launch with events (step k "
+                         "the chunks c = k mod E), for the average launch duration; a "
+                         "per-launch event pair costs about 6 us of a step, so 1 (every "
+                         "launch) adds about 1.5 ms to the pages step")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (5 times) and "
                          "exit: the reference for scaling FETCH_SIZE / WRITE_SIZE counters")
@@ -205,7 +210,8 @@ def main():
 
     def make_step(score_chunk, half=False, before=None):
         """One pass of the path: prepare items and queries, then score every chunk.
-        `evs` (timed steps only) holds the step's own events: (step, prepare, chunks)."""
+        `evs` (timed steps only) holds the step's own events: (step, prepare, score
+        loop, {chunk: pair} for the sampled chunks)."""
         def step(evs=None):
             if evs is not None:
                 evs[0][0].record(stream)
@@ -219,27 +225,55 @@ def main():
             qq = sps.prepare_queries(queries, it)
             if evs is not None:
                 evs[1][1].record(stream)
+                evs[2][0].record(stream)
             for c in range(n_chunks):
-                if evs is not None:
-                    evs[2][c][0].record(stream)
+                e = evs[3].get(c) if evs is not None else None
+                if e is not None:
+                    e[0].record(stream)
                 score_chunk(qq, it, c)
-                if evs is not None:
-                    evs[2][c][1].record(stream)
+                if e is not None:
+                    e[1].record(stream)
             if evs is not None:
+                evs[2][1].record(stream)
                 evs[0][1].record(stream)
             return it, qq
         return step
 
+    def sampled_chunks(k):
+        """The chunks whose launches timed step k brackets with events."""
+        e = max(1, args.event_every)
+        r = (k % e) % n_chunks
+        return [c for c in range(n_chunks) if c % e == r]
+
+    class Timed:
+        """A timed run: wall seconds over the steps, the sampled launches' (chunk,
+        ms) pairs, the mean prepare and score-loop ms per step, the median step ms."""
+        def __init__(self, total, samples, prep, loop, median):
+            self.total, self.samples, self.prep, self.loop, self.median = (
+                total, samples, prep, loop, median)
+
+        def launch_ms(self):
+            return np.array([ms for _, ms in self.samples])
+
+        def avg_launch_ms(self):
+            return float(self.launch_ms().mean())
+
+        def achieved_gbps(self, nbytes):
+            """Algorithmic bytes of the sampled launches over their summed time."""
+            b = float(sum(nbytes[c] for c, _ in self.samples))
+            return b / (float(self.launch_ms().sum()) * 1e-3) / 1e9
+
     def run_timed(step):
         """Warmup, then exactly args.steps timed steps, bracketed by a synchronize on
-        both sides and nothing else between them: (seconds, per-chunk launch ms,
-        prepare ms), the last two averaged over the steps. Every timed step records
-        events of its own, read only after the timed region, so that reading them
-        is not timed; the median step is taken from the steps' own events."""
+        both sides and nothing else between them. Every timed step records events
+        of its own (the step, the prepare, the score loop, and the sampled chunks'
+        launches), read only after the timed region, so that reading them is not
+        timed; the median step is taken from the steps' own events."""
         for _ in range(args.warmup):
             step()
         torch.cuda.synchronize()
-        evs = [(pair(), pair(), [pair() for _ in range(n_chunks)]) for _ in range(args.steps)]
+        evs = [(pair(), pair(), pair(), {c: pair() for c in sampled_chunks(k)})
+               for k in range(args.steps)]
         t0 = time.perf_counter()
         for k in range(args.steps):
             # (a step's prepared structures are released as soon as its work is
@@ -248,29 +282,28 @@ def main():
             step(evs[k])
         torch.cuda.synchronize()
         t_total = time.perf_counter() - t0
-        kern = np.zeros(n_chunks)
-        prep = 0.0
-        per_step = []
-        for e_step, e_prep, e_chunks in evs:
-            kern += np.array([a.elapsed_time(b) for a, b in e_chunks])
+        samples, prep, loop, per_step = [], 0.0, 0.0, []
+        for e_step, e_prep, e_loop, e_chunks in evs:
+            samples += [(c, a.elapsed_time(b)) for c, (a, b) in sorted(e_chunks.items())]
             prep += e_prep[0].elapsed_time(e_prep[1])
+            loop += e_loop[0].elapsed_time(e_loop[1])
             per_step.append(e_step[0].elapsed_time(e_step[1]))
-        run_timed.median_ms = float(np.median(per_step))
-        return t_total, kern / args.steps, prep / args.steps
+        return Timed(t_total, samples, prep / args.steps, loop / args.steps,
+                     float(np.median(per_step)))
 
-    t_total, kern_ms, prep_ms = run_timed(
-        make_step(lambda qq, it, c: sps.cosine_chunk(qq, it, c, out, sums[c])))
+    main = run_timed(make_step(lambda qq, it, c: sps.cosine_chunk(qq, it, c, out, sums[c])))
+    t_total, prep_ms = main.total, main.prep
     ms_per_step = 1e3 * t_total / args.steps
-    median_step_ms = run_timed.median_ms
+    median_step_ms = main.median
     scores = float(n_q) * float(n_i)
     value = scores * args.steps / t_total
 
     # algorithmic bytes of one score launch: fp32 scores written, the chunk's
     # posting entries read once (8-byte (item id, value) records), fp64 row sums
     alg_bytes = 4.0 * n_q * chunk_len + 8.0 * chunk_nnz + 8.0 * n_q
-    avg_launch_ms = float(kern_ms.mean())
-    achieved = float(alg_bytes.mean()) / (avg_launch_ms * 1e-3) / 1e9
-    loop_ms = float(kern_ms.sum())
+    avg_launch_ms = main.avg_launch_ms()
+    achieved = main.achieved_gbps(alg_bytes)
+    loop_ms = main.loop
     traffic = measured_traffic(args.traffic, w.name)
 
     # checksum sanity on the last step: row sums finite
@@ -289,13 +322,13 @@ def main():
     log("step %.2f ms: prepare %.2f ms, %d score launches %.2f ms (avg %.3f ms)" %
         (ms_per_step, prep_ms, n_chunks, loop_ms, avg_launch_ms))
 
-    def variant(total, kern, prep, nbytes, **extra):
-        avg = float(kern.mean())
-        ach = float(nbytes.mean()) / (avg * 1e-3) / 1e9
-        d = {"value": scores * args.steps / total, "unit": "scores/s",
-             "ms_per_step": 1e3 * total / args.steps}
+    def variant(tm, nbytes, **extra):
+        avg = tm.avg_launch_ms()
+        ach = tm.achieved_gbps(nbytes)
+        d = {"value": scores * args.steps / tm.total, "unit": "scores/s",
+             "ms_per_step": 1e3 * tm.total / args.steps}
         d.update(extra)
-        d["breakdown_ms"] = {"prepare": prep, "score_loop": float(kern.sum()),
+        d["breakdown_ms"] = {"prepare": tm.prep, "score_loop": tm.loop,
                              "score_launch_avg": avg}
         d["roofline"] = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBPS,
                          "unit": "GB/s", "frac": ach / HBM_PEAK_GBPS}
@@ -306,10 +339,9 @@ def main():
     half = None
     if not args.no_half:
         out16 = torch.empty(n_q, min(C, n_i), dtype=torch.float16, device=dev)
-        h_total, h_kern, h_prep = run_timed(make_step(
+        h_tm = run_timed(make_step(
             lambda qq, it, c: sps.cosine_chunk_half(qq, it, c, out16, sums[c]), half=True))
-        half = variant(h_total, h_kern, h_prep,
-                       2.0 * n_q * chunk_len + 4.0 * chunk_nnz + 8.0 * n_q,
+        half = variant(h_tm, 2.0 * n_q * chunk_len + 4.0 * chunk_nnz + 8.0 * n_q,
                        dtype="f16", max_abs_error_bound=1e-3)
         log("fp16 variant: step %.2f ms, avg launch %.3f ms" %
             (half["ms_per_step"], half["breakdown_ms"]["score_launch_avg"]))
@@ -329,12 +361,11 @@ def main():
         torch.cuda.synchronize()
         n_hits = int(count.item())
         hits = torch.empty(n_hits, 3, dtype=torch.int32, device=dev)
-        t_total_, t_kern, t_prep = run_timed(make_step(
+        t_tm = run_timed(make_step(
             lambda qq, it, c: sps.cosine_chunk_threshold(qq, it, c, t_, hits, count, sums[c]),
             before=count.zero_))
         assert int(count.item()) == n_hits
-        thr = variant(t_total_, t_kern, t_prep,
-                      8.0 * chunk_nnz + 8.0 * n_q + 12.0 * n_hits / n_chunks,
+        thr = variant(t_tm, 8.0 * chunk_nnz + 8.0 * n_q + 12.0 * n_hits / n_chunks,
                       dtype="f32", threshold=t_, hits=n_hits)
         log("threshold %.2f variant: %d hits, step %.2f ms, avg launch %.3f ms" %
             (t_, n_hits, thr["ms_per_step"], thr["breakdown_ms"]["score_launch_avg"]))
@@ -549,7 +580,8 @@ def main():
         "cpu_baseline": cpu,
         "breakdown_ms": {"prepare": prep_ms, "score_loop": loop_ms,
                          "score_launch_avg": avg_launch_ms,
-                         "score_launch_median": float(np.median(kern_ms)),
+                         "score_launch_median": float(np.median(main.launch_ms())),
+                         "launches_timed": len(main.samples),
                          "step_median": median_step_ms},
         "step_hbm_gbps_algorithmic": float(alg_bytes.sum()) / (ms_per_step * 1e-3) / 1e9,
         "write_ceiling_gbps": write_ceiling,
