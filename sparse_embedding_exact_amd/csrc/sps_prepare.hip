@@ -456,7 +456,9 @@ __global__ __launch_bounds__(kRunNT) void dim_runs_kernel(const int32_t *__restr
                                                           int4 *__restrict__ info,
                                                           uint4 *__restrict__ tab,
                                                           int32_t *__restrict__ gdf, int32_t hmin,
-                                                          int64_t dim, int32_t defer_cap) {
+                                                          int64_t dim, int32_t defer_cap,
+                                                          int32_t *__restrict__ ldim,
+                                                          uint2 *__restrict__ lval) {
   constexpr bool BUILD = MODE == kRunsBuild;
   constexpr int NW = kRunNT / 64;
   constexpr unsigned long long kEmpty64 = ~0ull;
@@ -464,7 +466,7 @@ __global__ __launch_bounds__(kRunNT) void dim_runs_kernel(const int32_t *__restr
   __shared__ int32_t s_cnt;
   __shared__ unsigned long long s_tab[BUILD ? 2 * kBuildBuckets : 1];
   __shared__ uint4 s_def[BUILD ? kDeferCap : 1];  // (first word, second word) of deferred runs
-  __shared__ int32_t s_ndef;
+  __shared__ int32_t s_ndef, s_nlist;
   const int64_t sl = blockIdx.x;
   const bool fault = flags[0] != 0;
   const int64_t b = fault ? 0 : slice_base[sl];
@@ -590,13 +592,28 @@ __global__ __launch_bounds__(kRunNT) void dim_runs_kernel(const int32_t *__restr
       bk = bk + 1 == nb ? 0u : bk + 1;
     }
   };
+  // The runs whose home bucket lies past the current range go onto a list (the
+  // slice's own span of the free sort buffers, at most one run per entry),
+  // which the next range reads instead of sweeping the keys again; it
+  // rewrites the list in place with the runs still ahead (never past the
+  // entries it has read).
+  int32_t *const ld = ldim + b;
+  uint2 *const lv = lval + b;
+  int32_t nlist = 0;  // runs on the list (uniform: read after a barrier)
   for (uint32_t p0 = 0; p0 < nb; p0 += kBuildBuckets) {
     const uint32_t p1 = nb - p0 < (uint32_t)kBuildBuckets ? nb : p0 + kBuildBuckets;
     for (uint32_t i = t; i < 2 * (p1 - p0); i += kRunNT) s_tab[i] = kEmpty64;
+    if (t == 0) s_nlist = 0;
     __syncthreads();
-    sweep([&](int32_t kk, int32_t st, int32_t len) {
+    // a run whose home is in [p0, p1) into the range, else onto the list
+    auto place = [&](int32_t kk, int32_t st, int32_t len) {
       const uint32_t home = dim_bucket((uint32_t)kk, nb);
-      if (home < p0 || home >= p1) return;
+      if (home >= p1) {
+        const int i = atomicAdd(&s_nlist, 1);
+        ld[i] = kk;
+        lv[i] = make_uint2((uint32_t)st, (uint32_t)len);
+        return;
+      }
       unsigned long long w0, w1;
       words(kk, st, len, w0, w1);
       for (uint32_t bk = home; bk < p1; ++bk) {
@@ -616,8 +633,24 @@ __global__ __launch_bounds__(kRunNT) void dim_runs_kernel(const int32_t *__restr
       if (i < defer_cap)
         s_def[i] = make_uint4((uint32_t)w0, (uint32_t)(w0 >> 32), (uint32_t)w1,
                               (uint32_t)(w1 >> 32));
-    });
+    };
+    if (p0 == 0) {
+      sweep(place);
+    } else {
+      for (int32_t cb = 0; cb < nlist; cb += kRunNT) {
+        const int32_t i = cb + t;
+        int32_t kk = 0;
+        uint2 v = make_uint2(0u, 0u);
+        if (i < nlist) {
+          kk = ld[i];
+          v = lv[i];
+        }
+        __syncthreads();  // (this block of the list is read before any of it is rewritten)
+        if (i < nlist) place(kk, (int32_t)v.x, (int32_t)v.y);
+      }
+    }
     __syncthreads();
+    nlist = s_nlist;
     const uint4 *st4 = reinterpret_cast<const uint4 *>(s_tab);
     for (uint32_t i = t; i < p1 - p0; i += kRunNT) gtab[p0 + i] = st4[i];
     __syncthreads();  // (the range is read before the next one clears it)
@@ -977,13 +1010,13 @@ hipError_t launch_prepare_items(const ItemsDev &d, hipStream_t s) {
   const int32_t hmin = g.S / (2 * kHeavyFracInv) > 2 ? g.S / (2 * kHeavyFracInv) : 2;
   hipLaunchKernelGGL(dim_runs_kernel<kRunsCount>, dim3((unsigned)ns), dim3(kRunNT), 0, s, d.flags,
                      d.slice_base, d.skey[0], d.dinfo, d.dtab, d.dense ? d.gdf : nullptr, hmin,
-                     d.dim, 0);
+                     d.dim, 0, nullptr, nullptr);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(dim_layout_kernel, dim3(1), dim3(1024), 0, s, ns, d.slice_base, d.dinfo);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(dim_runs_kernel<kRunsBuild>, dim3((unsigned)ns), dim3(kRunNT), 0, s, d.flags,
                      d.slice_base, d.skey[0], d.dinfo, d.dtab, nullptr, 0, d.dim,
-                     dim_defer_cap());
+                     dim_defer_cap(), d.skey[1], d.spay);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (!d.dense) return hipSuccess;
   const int64_t tg64 = (g.n_items + kHeavyFracInv - 1) / kHeavyFracInv;
