@@ -368,7 +368,10 @@ __device__ __forceinline__ void score_body(const ScoreArgs &a, int vec4, const S
       mfma_tiles(T, 1, true, T & 1);
     }
   }
-  __syncthreads();  // accumulators initialised before any sparse update
+  // accumulators initialised before any sparse update: the first batch's scan
+  // has a barrier (after every wave's part of the initial values above) and the
+  // walk follows it; a first group with no light entries takes one here
+  if (ge[0] == ge[1]) __syncthreads();
 
   const uint2 *__restrict__ ppost = a.post + cb0;
   const uint32_t *__restrict__ ppost4 = HALF ? a.post4 + cb0 : nullptr;
@@ -380,9 +383,11 @@ __device__ __forceinline__ void score_body(const ScoreArgs &a, int vec4, const S
   int scan_par = 0;
   for (int gi = 0; gi < ng; ++gi) {
     const int64_t q0 = (grp0 + gi) * kRows;
-    if (gi > 0) {
-      // the previous group's epilogue has read the accumulators
-      __syncthreads();
+    // the group's initial values into the accumulators: right after its first
+    // batch's scan, whose barrier follows every wave's part of the previous
+    // group's epilogue (a group with no light entries has no scan: barriers of
+    // its own)
+    auto init_acc = [&]() {
       if (DENSE) {
         if (wdense) {
 #pragma unroll
@@ -394,6 +399,10 @@ __device__ __forceinline__ void score_body(const ScoreArgs &a, int vec4, const S
         int4 *acc4 = reinterpret_cast<int4 *>(acc);
         for (int k = t; k < kRows * Lp / 4; k += NT) acc4[k] = make_int4(0, 0, 0, 0);
       }
+    };
+    if (gi > 0 && ge[gi] == ge[gi + 1]) {
+      __syncthreads();
+      init_acc();
       __syncthreads();
     }
 
@@ -420,6 +429,11 @@ __device__ __forceinline__ void score_body(const ScoreArgs &a, int vec4, const S
       // a fast wave's next scan could overwrite totals a slow wave still reads.
       const int32_t pend = block_incl_scan_1b<NT>(nseg[0] + nseg[1], ws[scan_par], &total);
       scan_par ^= 1;
+      if (gi > 0 && eb == ge[gi]) {
+        init_acc();
+        // (with no segments no round barrier follows: one before the epilogue)
+        if (total == 0) __syncthreads();
+      }
       const int32_t sp[2] = {pend - nseg[0] - nseg[1], pend - nseg[1]};
       for (int32_t r0 = 0; r0 < total; r0 += kSegMax) {
         // the segments of this round that belong to this thread's lists
