@@ -55,24 +55,65 @@ hipError_t launch_fill_i32(int32_t *p, int64_t n, int32_t v, hipStream_t s) {
   return hipGetLastError();
 }
 
-// single-workgroup inclusive scan in place over a[0..n)
-template <int NT>
-__global__ __launch_bounds__(NT) void scan_inplace_kernel(int32_t *__restrict__ a, int64_t n) {
-  __shared__ int32_t ws[NT / 64];
+// Inclusive scan in place over a[0..n), in blocks of kScanBlock values (1024
+// threads, eight consecutive values each): every block scanned on its own;
+// then one workgroup makes each block's last value final (the running sum of
+// the blocks' totals); then every block after the first adds the previous
+// block's last value to its others. No scratch: the block totals travel in
+// the array itself.
+constexpr int kScanNT = 1024, kScanPer = 8, kScanBlock = kScanNT * kScanPer;
+
+__global__ __launch_bounds__(kScanNT) void scan_blocks_kernel(int32_t *__restrict__ a, int64_t n) {
+  __shared__ int32_t ws[kScanNT / 64];
+  const int64_t j0 = (int64_t)blockIdx.x * kScanBlock + (int64_t)threadIdx.x * kScanPer;
+  int32_t v[kScanPer];
+#pragma unroll
+  for (int e = 0; e < kScanPer; ++e) v[e] = j0 + e < n ? a[j0 + e] : 0;
+#pragma unroll
+  for (int e = 1; e < kScanPer; ++e) v[e] += v[e - 1];
+  int32_t tot;
+  const int32_t off = block_incl_scan_1b<kScanNT>(v[kScanPer - 1], ws, &tot) - v[kScanPer - 1];
+#pragma unroll
+  for (int e = 0; e < kScanPer; ++e)
+    if (j0 + e < n) a[j0 + e] = off + v[e];
+}
+
+// a[last of block b] += the totals of blocks 0 .. b-1 (one workgroup)
+__global__ __launch_bounds__(kScanNT) void scan_tops_kernel(int32_t *__restrict__ a, int64_t n) {
+  __shared__ int32_t ws[2][kScanNT / 64];
+  const int64_t nb = (n + kScanBlock - 1) / kScanBlock;
   int32_t carry = 0;
-  for (int64_t base = 0; base < n; base += NT) {
-    const int64_t j = base + threadIdx.x;
-    const int32_t v = j < n ? a[j] : 0;
+  int par = 0;
+  for (int64_t b0 = 0; b0 < nb; b0 += kScanNT) {
+    const int64_t b = b0 + threadIdx.x;
+    const int64_t last = b < nb ? ((b + 1) * kScanBlock < n ? (b + 1) * kScanBlock : n) - 1 : 0;
+    const int32_t v = b < nb ? a[last] : 0;
     int32_t tot;
-    const int32_t incl = block_incl_scan<NT>(v, ws, &tot);
-    if (j < n) a[j] = carry + incl;
+    const int32_t incl = block_incl_scan_1b<kScanNT>(v, ws[par], &tot);
+    par ^= 1;  // (alternate buffers: one barrier per step suffices)
+    if (b < nb) a[last] = carry + incl;
     carry += tot;
   }
 }
 
+// block b >= 1: every value but its last += the previous block's last value
+__global__ __launch_bounds__(256) void scan_add_kernel(int32_t *__restrict__ a, int64_t n) {
+  const int64_t b = blockIdx.x + 1;
+  const int64_t first = b * kScanBlock;
+  const int64_t last = ((b + 1) * kScanBlock < n ? (b + 1) * kScanBlock : n) - 1;
+  const int32_t off = a[first - 1];
+  for (int64_t j = first + threadIdx.x; j < last; j += 256) a[j] += off;
+}
+
 hipError_t launch_scan_inplace(int32_t *a, int64_t n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(scan_inplace_kernel<1024>, dim3(1), dim3(1024), 0, s, a, n);
+  const int64_t nb = (n + kScanBlock - 1) / kScanBlock;
+  hipLaunchKernelGGL(scan_blocks_kernel, dim3((unsigned)nb), dim3(kScanNT), 0, s, a, n);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || nb == 1) return e;
+  hipLaunchKernelGGL(scan_tops_kernel, dim3(1), dim3(kScanNT), 0, s, a, n);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(scan_add_kernel, dim3((unsigned)(nb - 1)), dim3(256), 0, s, a, n);
   return hipGetLastError();
 }
 
@@ -1199,9 +1240,7 @@ hipError_t launch_prepare_queries(const QueriesDev &d, hipStream_t s) {
                      d.indptr, d.indices, d.values, d.norm64, d.flags, heavy, d.qh_gstride,
                      d.lptr, d.lrec, d.qh);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(scan_inplace_kernel<1024>, dim3(1), dim3(1024), 0, s, d.lptr,
-                     d.n_rows + 1);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = launch_scan_inplace(d.lptr, d.n_rows + 1, s)) != hipSuccess) return e;
   hipLaunchKernelGGL(light_split_kernel<true>, dim3(blocks), dim3(256), 0, s, d.n_rows,
                      d.indptr, d.indices, d.values, d.norm64, d.flags, heavy, d.qh_gstride,
                      d.lptr, d.lrec, d.qh);
