@@ -1126,9 +1126,14 @@ __global__ __launch_bounds__(256) void light_split_kernel(
     const float *__restrict__ values, const double *__restrict__ norm64,
     const int32_t *__restrict__ flags, const int32_t *__restrict__ heavy, int32_t qh_gstride,
     int32_t *__restrict__ lptr, uint3 *__restrict__ lrec, uint16_t *__restrict__ qh) {
+  // the heavy list in LDS: each entry's search over it is then a few LDS reads
+  // rather than dependent global loads
+  __shared__ int32_t s_heavy[kHeavyMax];
+  const int m = heavy != nullptr ? heavy[kHeavyMax] : 0;
+  for (int i = threadIdx.x; i < m; i += blockDim.x) s_heavy[i] = heavy[i];
+  __syncthreads();
   const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (q >= n_rows) return;
-  const int m = heavy != nullptr ? heavy[kHeavyMax] : 0;
   int64_t b = 0, e = 0;
   if (flags[0] == 0) {
     b = indptr[q];
@@ -1140,7 +1145,7 @@ __global__ __launch_bounds__(256) void light_split_kernel(
   int32_t count = 0;
   for (int64_t k = b; k < e; ++k) {
     const int32_t d = indices[k];
-    const int hs = m > 0 ? heavy_slot(heavy, m, d) : -1;
+    const int hs = m > 0 ? heavy_slot(s_heavy, m, d) : -1;
     if (FILL) {
       const float v = (n > 0.0) ? (float)((double)values[k] / n) : 0.0f;
       if (hs >= 0) {
