@@ -465,6 +465,34 @@ def test_group_first_batch_misses_slice(env, orc):
     assert np.abs(got[15]).max() > 0.01  # the second batch did contribute
 
 
+def test_wide_slice_index(env, orc):
+    """A slice of more than 2^22 entries (1,024 items of 4,100 entries each) takes the
+    dim index's wide format: one list per bucket, its start and its length in separate
+    words. The index is built over two LDS ranges (8,192 dims, 16,384 buckets), and the
+    inverted lists and scores must match the oracle."""
+    from synth import HostCSR
+    rng = np.random.default_rng(77)
+    n_items, dim, per_row = 1024, 8192, 4100
+    assert n_items * per_row > (1 << 22)
+    indices = np.concatenate([np.sort(rng.choice(dim, per_row, replace=False))
+                              for _ in range(n_items)]).astype(np.int32)
+    indptr = (np.arange(n_items + 1, dtype=np.int64) * per_row).astype(np.int32)
+    values = rng.lognormal(0, 1, indices.size).astype(np.float32)
+    items = HostCSR(indptr, indices, values, n_items, dim)
+    _check_structures(env, orc, items, 1024, "wide slice (4.2M entries)")
+    qrows = []
+    for r in range(20):
+        d = np.sort(rng.choice(dim, 40 + 13 * r, replace=False))
+        qrows.append(list(zip(d.tolist(), rng.lognormal(0, 1, d.size).astype(np.float32).tolist())))
+    import pins
+    q = pins.csr_from_rows(qrows, dim)
+    ref = orc.scores(q, items)
+    got = np.concatenate([g for _, _, g, _ in gpu_chunks(env, q, items, 1024)], axis=1)
+    err = float(np.abs(got - ref).max())
+    report("20x1024: one slice of 4.2M entries (wide dim index)", err, got.size)
+    assert err <= TOL
+
+
 def test_edge_rows_and_ld(env, orc):
     """Empty rows on both sides, explicit zeros, a dim no item has, a chunk
     length that is not a multiple of 4, ld > chunk_len (the tail untouched)."""
