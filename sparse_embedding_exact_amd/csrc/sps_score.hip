@@ -70,9 +70,11 @@ static_assert(kDenseToFix == 1.0f, "dense sums are already in fixed-point units"
 
 // x rounded to the nearest integer, ties upward: floor(x + 0.5) in one
 // instruction (|x| <= 2^30 here, so no saturation).
+// (Not volatile: a pure register operation, which the scheduler may move
+// like any other; a volatile one orders every memory access around it.)
 __device__ __forceinline__ int round_fix(float x) {
   int r;
-  asm volatile("v_cvt_rpi_i32_f32 %0, %1" : "=v"(r) : "v"(x));
+  asm("v_cvt_rpi_i32_f32 %0, %1" : "=v"(r) : "v"(x));
   return r;
 }
 
@@ -105,8 +107,8 @@ static_assert(kRows == 16 && kHeavyBlock == 32, "one 16x16x32 MFMA tile covers t
 // Sparse part: posting lists are cut into segments of kSeg entries, one per
 // 16 lanes, described in an LDS table.
 constexpr int kSeg = 16;
-constexpr int kSegMax = 896;         // segments per round
-constexpr int kSegPad = 16 * NW * 2;  // one walk step past the end (16 segments, 2 per wave)
+constexpr int kSegMax = 1024;        // segments per round (the LDS left beside two 64 KiB accumulators)
+constexpr int kSegPad = 16 * NW * 2;  // at least one walk step past the end (SPI * NW * U segments)
 static_assert(kRows * kSliceMax * 4 < (1 << 27), "row byte offset fits the segment record");
 
 // MODE kOutExact: fp32 scores. kOutHalf: the reduced-precision variant (item
@@ -132,7 +134,10 @@ template <bool DENSE, int MODE>
 __device__ __forceinline__ void score_body(const ScoreArgs &a, int vec4, const ScoreLds &L,
                                            int nblk) {
   constexpr bool HALF = MODE == kOutHalf;
-  constexpr int U = 2;                      // segment groups per wave per walk step
+  // segment groups per wave per walk step: three where the dense part runs
+  // (its corpora have long lists), two otherwise (the edge corpus: no heavy
+  // dims, short lists)
+  constexpr int U = HALF || !DENSE ? 2 : 3;
   constexpr int PPL = HALF ? 4 : 2;         // postings per lane (one 16-byte load)
   constexpr int LPS = kSeg / PPL;           // lanes per segment
   constexpr int SPI = 64 / LPS;             // segments per wave per load
