@@ -128,6 +128,7 @@ struct ScoreLds {
   int32_t (*ws)[NW];
   int32_t *s_wtot;
   unsigned long long *s_hbase;
+  int *sink;  // one slot per lane for the walk's masked-off adds
 };
 
 template <bool DENSE, int MODE>
@@ -483,12 +484,8 @@ __device__ __forceinline__ void score_body(const ScoreArgs &a, int vec4, const S
 #pragma unroll
           for (int u = 0; u < U; ++u)
             pe[u] = HALF ? ld_quad4(ppost4, pos[u] * 4u) : ld_pair(ppost, pos[u] * 8u);
-          // all U loads are in flight before the first is waited on (keeps the
-          // compiler from sinking a load into the masked update below it)
+          // all U loads are in flight before the first is waited on
           __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-          for (int u = 0; u < U; ++u)
-            asm volatile("" ::"v"(pe[u].x), "v"(pe[u].y), "v"(pe[u].z), "v"(pe[u].w));
 #pragma unroll
           for (int u = 0; u < U; ++u) {
             char *const rbase = reinterpret_cast<char *>(acc) + aoff[u];
@@ -500,19 +497,25 @@ __device__ __forceinline__ void score_body(const ScoreArgs &a, int vec4, const S
                 const uint32_t it = x & 0xFFFFu;
                 const float w = (float)__builtin_bit_cast(_Float16, (uint16_t)(x >> 16)) *
                                 (1.0f / kHeavyScale);
-                if (nn[u] > k && it < (uint32_t)slen)
-                  atomicAdd(reinterpret_cast<int *>(rbase + 4 * it), round_fix(qv[u] * w));
+                int *const p = nn[u] > k && it < (uint32_t)slen
+                                   ? reinterpret_cast<int *>(rbase + 4 * it)
+                                   : L.sink + lane;
+                atomicAdd(p, round_fix(qv[u] * w));
               }
             } else {
               // (no bound check on the item: every posting the prepare writes,
               // the zero padding included, holds a slice-local id below the
-              // slice size S <= Lp, so the address stays in acc[row][0, Lp))
-              if (nn[u] > 0)
-                atomicAdd(reinterpret_cast<int *>(rbase + 4 * pe[u].x),
-                          round_fix(qv[u] * __uint_as_float(pe[u].y)));
-              if (nn[u] > 1)
-                atomicAdd(reinterpret_cast<int *>(rbase + 4 * pe[u].z),
-                          round_fix(qv[u] * __uint_as_float(pe[u].w)));
+              // slice size S <= Lp, so the address stays in acc[row][0, Lp)).
+              // No branches either: a lane whose posting lies past its
+              // segment's end adds to a slot of its own outside the
+              // accumulators (distinct per lane, so no two lanes' dummy adds
+              // meet at one address), which nothing reads.
+              int *const p0 =
+                  nn[u] > 0 ? reinterpret_cast<int *>(rbase + 4 * pe[u].x) : L.sink + lane;
+              int *const p1 =
+                  nn[u] > 1 ? reinterpret_cast<int *>(rbase + 4 * pe[u].z) : L.sink + lane;
+              atomicAdd(p0, round_fix(qv[u] * __uint_as_float(pe[u].y)));
+              atomicAdd(p1, round_fix(qv[u] * __uint_as_float(pe[u].w)));
             }
           }
         }
@@ -706,7 +709,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void sc
   __shared__ int32_t ws[2][NW];
   __shared__ int32_t s_wtot[NW];
   __shared__ unsigned long long s_hbase;
-  const ScoreLds L{acc, s_spos, s_sqv, s_smeta, ws, s_wtot, &s_hbase};
+  __shared__ int s_sink[64];
+  const ScoreLds L{acc, s_spos, s_sqv, s_smeta, ws, s_wtot, &s_hbase, s_sink};
   // heavy-dim blocks in use (the slab and the query tiles hold a.heavy_blocks);
   // a corpus with no heavy dims takes the path without the dense part. The
   // choice is uniform across the workgroup.
@@ -728,7 +732,7 @@ __global__ void fold_row_sums_kernel(int64_t n_q, int32_t n_sub, const double *_
 }
 
 size_t score_lds_bytes(int32_t S) {
-  return (size_t)kRows * acc_pitch(S) * sizeof(int) + (kSegMax + kSegPad) * 12 + 2 * NW * 4 + 8;
+  return (size_t)kRows * acc_pitch(S) * sizeof(int) + (kSegMax + kSegPad) * 12 + 2 * NW * 4 + 8 + 64 * 4;
 }
 
 template <bool DENSE, int MODE>
